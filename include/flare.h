@@ -1,0 +1,167 @@
+/*
+ * flare.h -- C ABI of the MI355X (gfx950) split-KV softmax library (libflare.so).
+ *
+ * The library computes exact softmax attention of M latent query rows over N
+ * token keys/values that are split into R disjoint partitions, returns each
+ * partition's normalised output and log-normaliser, merges those states with
+ * the associative log-sum-exp rule, decodes every token against the latents,
+ * and differentiates the encoder with the global statistics.  Sources:
+ *
+ *  [FLARE++] "FLARE++: Low-rank attention with dynamic attention routing",
+ *            appendix on context parallelism (eq. 18, the local-shard states,
+ *            eq. 23, the max-stabilised merge, the FLARE and FLARE++ forward
+ *            paragraphs, the backward paragraph).
+ *  [RING]    "Ring vs. Tree Attention" (the online-softmax merge, the balanced
+ *            tree schedule, the failure mode of overlapping subsets).
+ *
+ * Conventions shared by every call
+ *  - Tensor pointers are DEVICE pointers to dense row-major arrays owned by the
+ *    caller; the library never allocates, frees or keeps them.  Offsets are a
+ *    HOST array.
+ *  - Layouts: Q is [H,M,D] replicated over the batch (q_batch_stride = 0) or
+ *    [B,H,M,D] (q_batch_stride = H*M*D elements); K, V, Xq, Y, dK, dV are
+ *    [B,H,N,D]; Z, dZ, dQ, O_part[r] are [B,H,M,D]; L, L_part[r] are [B,H,M];
+ *    O_part is [R,B,H,M,D] and L_part is [R,B,H,M].
+ *  - dtype selects the element type of Q, K, V, Xq, Klat, dZ, Y, dK, dV
+ *    (FLARE_F32 = float, FLARE_BF16 = bfloat16).  O_part, L_part, Z, L and dQ
+ *    are always float.  Arithmetic: products of bfloat16 operands accumulate
+ *    in float (bf16 matrix cores), softmax statistics are float, and the
+ *    softmax weights are rounded to bfloat16 before they multiply V.
+ *  - scale is the score multiplier s (the pages use s = D^-1/2); scores are
+ *    s * q.k.  Log-normalisers are natural logarithms of sums of exp(score).
+ *  - mask (nullable) is [B,N] uint8, nonzero = valid key.  Masked keys never
+ *    influence any output, whatever values (even NaN/Inf) they hold [FLARE++:
+ *    padding is excluded by local masks].
+ *  - stream is a hipStream_t (NULL = the null stream).  Every call is
+ *    asynchronous on that stream and never synchronises the device.
+ *  - Every argument is validated before anything is launched: a non-OK status
+ *    means nothing was written.  flare_last_error() then describes the problem
+ *    (thread-local).  FLARE_EHIP reports a failed launch.
+ *  - The library holds no state between calls: the statistics saved by one
+ *    encoder invocation are the caller's to keep [FLARE++ backward paragraph].
+ *  - Supported shapes: D % 4 == 0 and 4 <= D <= 256, M >= 1; matrix-core paths
+ *    for bfloat16 with D in {64,128} and M a multiple of 32 up to 256, a vector
+ *    path for M = 1, and a general vector path for everything else.
+ */
+#ifndef FLARE_H
+#define FLARE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flare_status {
+  FLARE_OK = 0,
+  FLARE_EINVAL = -1,        /* bad argument: null pointer, negative size, bad offsets */
+  FLARE_EUNSUPPORTED = -2,  /* valid but unsupported shape/dtype combination */
+  FLARE_EHIP = -3,          /* a HIP launch failed */
+  FLARE_EWORKSPACE = -4     /* workspace missing or smaller than the size query says */
+} flare_status;
+
+typedef enum flare_dtype { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
+
+/* hipStream_t, passed as an opaque pointer so this header needs no HIP headers. */
+typedef void* flare_stream_t;
+
+/* Bytes of device workspace flare_encode needs for these arguments (0 if none).
+ * Returns 0 as well when the arguments are invalid; flare_encode reports those. */
+size_t flare_encode_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D,
+                                   int R, const int64_t* offsets);
+
+/*
+ * flare_encode -- the local-shard encoder of [FLARE++] (the equations between
+ * eq. 18 and eq. 23), for all R partitions of every (batch, head) at once.
+ *
+ * Partition r holds tokens [offsets[r], offsets[r+1]); offsets has R+1 int64
+ * entries with 0 = offsets[0] <= offsets[1] <= ... <= offsets[R] = N (empty
+ * partitions allowed; overlapping or unsorted offsets are rejected with
+ * FLARE_EINVAL since double counting would go unnoticed [RING, failure mode]).
+ * For every (r, b, h, m) with S[n] = scale * Q[b,h,m,:].K[b,h,n,:] over the
+ * valid tokens n of partition r:
+ *     L_part[r,b,h,m]   = log sum_n exp(S[n])
+ *     O_part[r,b,h,m,:] = sum_n exp(S[n] - L_part) V[b,h,n,:]
+ * and a row with no valid token in the partition gets L = -inf, O = 0 (never
+ * NaN).  workspace (device, nullable when the size query returns 0) must hold
+ * flare_encode_workspace_size() bytes; it holds partial states between two
+ * internal kernels and carries nothing between calls.
+ */
+flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D,
+                          const void* Q, int64_t q_batch_stride, const void* K, const void* V,
+                          int R, const int64_t* offsets, const uint8_t* mask, float scale,
+                          float* O_part, float* L_part,
+                          void* workspace, size_t workspace_bytes, flare_stream_t stream);
+
+/*
+ * lse_merge -- the exact cross-partition merge of [FLARE++] (eqs. 21-23 and
+ * the max-stabilised merge paragraph), evaluated as the balanced binary tree
+ * of [RING]: leaves are (m, l, acc) = (L_r, 1, O_r) (or (-inf, 0, 0) for an
+ * empty state); round k merges state i with state i + 2^k for i = 0 mod
+ * 2^(k+1), a state without a partner passing through; each merge takes
+ * m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m), acc likewise.  Outputs
+ * Z = acc / l and L = m + log l per row; a row empty in every partition gets
+ * Z = 0, L = -inf.
+ *
+ * O_part: [R, rows, D] float, L_part: [R, rows] float (rows = B*H*M).
+ * Z: [rows, D] float, L: [rows] float.  Z_bf16 (nullable): [rows, D]
+ * bfloat16 copy of Z, rounded to nearest even (used as the next encoder's
+ * queries in FLARE++).  R >= 1.
+ */
+flare_status lse_merge(int R, int64_t rows, int D, const float* O_part, const float* L_part,
+                       float* Z, float* L, void* Z_bf16, flare_stream_t stream);
+
+/*
+ * flare_decode -- the local decode of [FLARE++] (FLARE and FLARE++ forward
+ * paragraphs): every token attends over the M replicated latents,
+ *     Y[b,h,n,:] = sum_m softmax_m(scale * Xq[b,h,n,:].Klat[b,h,m,:]) Z[b,h,m,:]
+ * Xq: [B,H,N,D] token-side queries (FLARE uses the token's key row K),
+ * Klat: latent keys (FLARE: the latent queries Q; FLARE++: the dynamic
+ * queries Q(X)), [H,M,D] with klat_batch_stride = 0 or [B,H,M,D] with
+ * klat_batch_stride = H*M*D; Z: [B,H,M,D] float (the merged encoder output);
+ * token_mask (nullable) [B,N] uint8, zero marks padding whose Y row is set
+ * to 0.  Y: [B,H,N,D] in dtype.  No cross-partition work is involved.
+ */
+flare_status flare_decode(flare_dtype dtype, int B, int H, int N, int M, int D,
+                          const void* Xq, const void* Klat, int64_t klat_batch_stride,
+                          const float* Z, const uint8_t* token_mask, float scale, void* Y,
+                          flare_stream_t stream);
+
+/* Bytes of device workspace flare_encode_bwd needs (0 if none). */
+size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D,
+                                       int R, const int64_t* offsets);
+
+/*
+ * flare_encode_bwd -- the encoder backward of [FLARE++] (backward paragraph):
+ * gradients of sum(dZ * Z) with the GLOBAL forward statistics Z and L (as
+ * returned by lse_merge for this encoder invocation), for every partition:
+ *     P[m,n]  = exp(S[m,n] - L[m])          (S as in flare_encode; 0 if masked)
+ *     c[m]    = sum_d dZ[m,d] Z[m,d]        (between-partition row term)
+ *     dS[m,n] = P[m,n] (dZ[m,:].V[n,:] - c[m])
+ *     dV[n,:] = sum_m P[m,n] dZ[m,:]        dK[n,:] = scale sum_m dS[m,n] Q[m,:]
+ *     dQ[m,:] = scale sum_n dS[m,n] K[n,:]  summed over all partitions
+ * dQ: [B,H,M,D] float, one slice per batch even when Q is replicated (the sum
+ * over the batch is the caller's).  dK, dV: [B,H,N,D] in dtype; rows of masked
+ * tokens are written as 0.  Rows with L = -inf get zero gradients.
+ * Offsets are validated as in flare_encode; workspace must hold
+ * flare_encode_bwd_workspace_size() bytes.
+ */
+flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D,
+                              const void* Q, int64_t q_batch_stride, const void* K, const void* V,
+                              int R, const int64_t* offsets, const uint8_t* mask, float scale,
+                              const float* Z, const float* L, const void* dZ,
+                              float* dQ, void* dK, void* dV,
+                              void* workspace, size_t workspace_bytes, flare_stream_t stream);
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+const char* flare_last_error(void);
+
+/* Library version string. */
+const char* flare_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLARE_H */

@@ -1,0 +1,370 @@
+// C ABI of libflare: argument validation, work decomposition and launches.
+// Declarations and their contract are in include/flare.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/flare.h"
+#include "kernels.h"
+
+using namespace flare;
+
+namespace {
+
+thread_local std::string g_err;
+
+flare_status fail(flare_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+flare_status hip_fail(hipError_t e, const char* what) {
+  return fail(FLARE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(flare_dtype dt) { return dt == FLARE_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- validation
+flare_status check_common(flare_dtype dt, int B, int H, int N, int M, int D) {
+  if (dt != FLARE_F32 && dt != FLARE_BF16) return fail(FLARE_EINVAL, "unknown dtype %d", (int)dt);
+  if (B < 0 || H < 0 || N < 0 || M < 0 || D < 0)
+    return fail(FLARE_EINVAL, "negative size (B=%d H=%d N=%d M=%d D=%d)", B, H, N, M, D);
+  if (D % 4 != 0 || D < 4 || D > 256)
+    return fail(FLARE_EUNSUPPORTED, "head dimension D=%d unsupported (need D %% 4 == 0, 4 <= D <= 256)", D);
+  return FLARE_OK;
+}
+
+flare_status check_offsets(int N, int R, const int64_t* off) {
+  if (R < 1) return fail(FLARE_EINVAL, "R=%d partitions; need R >= 1", R);
+  if (!off) return fail(FLARE_EINVAL, "offsets is NULL");
+  if (off[0] != 0) return fail(FLARE_EINVAL, "offsets[0]=%lld, must be 0", (long long)off[0]);
+  for (int r = 0; r < R; ++r)
+    if (off[r + 1] < off[r])
+      return fail(FLARE_EINVAL, "offsets not sorted: offsets[%d]=%lld > offsets[%d]=%lld (partitions must be disjoint)",
+                  r, (long long)off[r], r + 1, (long long)off[r + 1]);
+  if (off[R] != N) return fail(FLARE_EINVAL, "offsets[R]=%lld must equal N=%d", (long long)off[R], N);
+  return FLARE_OK;
+}
+
+// ------------------------------------------------------------ work planning
+enum class EncKind { Mfma, Q1, Generic };
+
+EncKind encode_kind(flare_dtype dt, int M, int D) {
+  if (dt == FLARE_BF16 && encode_mfma_supported(M, D)) return EncKind::Mfma;
+  if (dt == FLARE_BF16 && encode_q1_supported(M, D)) return EncKind::Q1;
+  return EncKind::Generic;
+}
+
+struct Chunk {
+  int32_t lo, hi;
+  int part;
+};
+
+struct EncodePlan {
+  EncKind kind;
+  std::vector<Chunk> chunks;
+  std::vector<int> first_chunk;   // per partition, index into chunks; size R+1
+  std::vector<int16_t> slot;      // per chunk
+  int nslots = 0;
+  size_t ws_bytes = 0;
+};
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Chunk length for a partition of n tokens.
+int chunk_len_for(EncKind kind, int B, int H, int R, int M, int64_t max_part) {
+  if (max_part <= 0) return 1;
+  switch (kind) {
+    case EncKind::Mfma: {
+      // Enough workgroups to keep every CU busy with a few resident groups,
+      // but long enough chunks that the partial states stay a few percent of
+      // the K/V bytes (state bytes / K,V bytes = 2M / chunk_len).
+      const int64_t base = (int64_t)B * H * R;
+      int split = env_int("FLARE_ENCODE_SPLIT", 0);
+      if (split <= 0) split = (int)std::max<int64_t>(1, (512 + base - 1) / base);
+      int len = round_up((int)((max_part + split - 1) / split), 64);
+      const int min_len = std::max(1024, 32 * M);
+      if (split > 1 && len < min_len) len = min_len;
+      return std::max(len, 64);
+    }
+    case EncKind::Q1:
+      return 4096;
+    default:
+      return 2048;
+  }
+}
+
+EncodePlan plan_encode(flare_dtype dt, int B, int H, int N, int M, int D, int R, const int64_t* off) {
+  EncodePlan p;
+  p.kind = encode_kind(dt, M, D);
+  int64_t max_part = 0;
+  for (int r = 0; r < R; ++r) max_part = std::max<int64_t>(max_part, off[r + 1] - off[r]);
+  const int len = chunk_len_for(p.kind, B, H, R, M, max_part);
+  p.first_chunk.resize(R + 1);
+  for (int r = 0; r < R; ++r) {
+    p.first_chunk[r] = (int)p.chunks.size();
+    const int64_t lo = off[r], hi = off[r + 1];
+    const int64_t n = hi - lo;
+    if (n <= 0) continue;
+    const int64_t k = (n + len - 1) / len;
+    // equal pieces rounded up to whole 64-token tiles
+    const int64_t piece = ((n + k - 1) / k + 63) / 64 * 64;
+    for (int64_t t = lo; t < hi; t += piece) p.chunks.push_back({(int32_t)t, (int32_t)std::min<int64_t>(hi, t + piece), r});
+  }
+  p.first_chunk[R] = (int)p.chunks.size();
+  p.slot.resize(p.chunks.size());
+  for (int r = 0; r < R; ++r) {
+    const int a = p.first_chunk[r], b = p.first_chunk[r + 1];
+    if (b - a == 1) {
+      p.slot[a] = (int16_t)(-(r + 1));
+    } else {
+      for (int i = a; i < b; ++i) p.slot[i] = (int16_t)(p.nslots++);
+    }
+  }
+  const size_t per = (size_t)B * H * M;
+  p.ws_bytes = p.nslots ? (size_t)p.nslots * per * (D + 1) * sizeof(float) + 256 : 0;
+  return p;
+}
+
+bool plan_fits(const EncodePlan& p, int R) {
+  // slots and partition indices must fit the 16-bit table entries
+  return p.nslots < 32767 && R < 32767;
+}
+
+}  // namespace
+
+// =============================================================== C ABI
+extern "C" {
+
+const char* flare_last_error(void) { return g_err.c_str(); }
+
+const char* flare_version(void) { return "libflare 0.1 (gfx950)"; }
+
+size_t flare_encode_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D, int R,
+                                   const int64_t* offsets) {
+  const std::string saved = g_err;
+  if (check_common(dtype, B, H, N, M, D) != FLARE_OK || check_offsets(N, R, offsets) != FLARE_OK) {
+    g_err = saved;
+    return 0;
+  }
+  return plan_encode(dtype, B, H, N, M, D, R, offsets).ws_bytes;
+}
+
+flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
+                          int64_t q_batch_stride, const void* K, const void* V, int R,
+                          const int64_t* offsets, const uint8_t* mask, float scale, float* O_part,
+                          float* L_part, void* workspace, size_t workspace_bytes, flare_stream_t stream) {
+  flare_status st = check_common(dtype, B, H, N, M, D);
+  if (st != FLARE_OK) return st;
+  st = check_offsets(N, R, offsets);
+  if (st != FLARE_OK) return st;
+  if (!std::isfinite(scale)) return fail(FLARE_EINVAL, "scale must be finite");
+  if (q_batch_stride < 0) return fail(FLARE_EINVAL, "q_batch_stride must be >= 0");
+  if ((int64_t)B * H * M == 0) return FLARE_OK;
+  if (!O_part || !L_part) return fail(FLARE_EINVAL, "O_part and L_part must not be NULL");
+  if (!Q) return fail(FLARE_EINVAL, "Q must not be NULL");
+  if (N > 0 && (!K || !V)) return fail(FLARE_EINVAL, "K and V must not be NULL");
+  const EncodePlan plan = plan_encode(dtype, B, H, N, M, D, R, offsets);
+  if (!plan_fits(plan, R)) return fail(FLARE_EUNSUPPORTED, "too many partitions or chunks (R=%d)", R);
+  if (plan.kind != EncKind::Generic) {
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || (q_batch_stride * esize(dtype)) % 16 != 0)
+      return fail(FLARE_EINVAL, "Q, K, V and the Q batch stride must be 16-byte aligned");
+  }
+  if (!aligned16(O_part)) return fail(FLARE_EINVAL, "O_part must be 16-byte aligned");
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(FLARE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(FLARE_EINVAL, "workspace must be 16-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  EncodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.mask = mask;
+  a.O_part = O_part;
+  a.L_part = L_part;
+  const size_t per = (size_t)B * H * M;
+  if (plan.nslots) {
+    a.ws_O = static_cast<float*>(workspace);
+    const size_t o_bytes = ((size_t)plan.nslots * per * D * sizeof(float) + 255) / 256 * 256;
+    a.ws_L = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  }
+  a.q_bstride = q_batch_stride;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.M = M;
+  a.D = D;
+  a.R = R;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  // encoder launches over groups of at most kMaxChunks consecutive chunks
+  const int nc = (int)plan.chunks.size();
+  for (int c0 = 0; c0 < nc; c0 += kMaxChunks) {
+    const int n = std::min(kMaxChunks, nc - c0);
+    a.tab.nchunks = n;
+    for (int i = 0; i < n; ++i) {
+      a.tab.bnd[i] = plan.chunks[c0 + i].lo;
+      a.tab.slot[i] = plan.slot[c0 + i];
+    }
+    a.tab.bnd[n] = plan.chunks[c0 + n - 1].hi;
+    hipError_t e;
+    switch (plan.kind) {
+      case EncKind::Mfma: e = launch_encode_mfma(a, s); break;
+      case EncKind::Q1: e = launch_encode_q1(a, s); break;
+      default: e = launch_encode_generic(a, dtype == FLARE_BF16, s); break;
+    }
+    if (e != hipSuccess) return hip_fail(e, "encode launch");
+  }
+
+  // fold split partitions and write the empty state of empty partitions
+  FoldArgs f;
+  memset(&f, 0, sizeof(f));
+  f.in_O = a.ws_O;
+  f.in_L = a.ws_L;
+  f.out_O = O_part;
+  f.out_L = L_part;
+  f.rows = (int64_t)per;
+  f.D = D;
+  int ng = 0;
+  int cursor = 0;   // slots are numbered in partition order, so groups are consecutive
+  auto flush = [&]() -> hipError_t {
+    if (ng == 0) return hipSuccess;
+    f.tab.ngroups = ng;
+    hipError_t e = launch_fold(f, s);
+    ng = 0;
+    return e;
+  };
+  for (int r = 0; r < R; ++r) {
+    const int n = plan.first_chunk[r + 1] - plan.first_chunk[r];
+    if (n == 1) continue;   // written directly by the encoder
+    if (ng == 0) f.tab.in_begin[0] = cursor;
+    f.tab.out_index[ng] = r;
+    cursor += n;            // n == 0: an empty group writes (0, -inf)
+    f.tab.in_begin[ng + 1] = cursor;
+    if (++ng == kMaxGroups) {
+      hipError_t e = flush();
+      if (e != hipSuccess) return hip_fail(e, "fold launch");
+    }
+  }
+  hipError_t e = flush();
+  if (e != hipSuccess) return hip_fail(e, "fold launch");
+  return FLARE_OK;
+}
+
+flare_status lse_merge(int R, int64_t rows, int D, const float* O_part, const float* L_part, float* Z,
+                       float* L, void* Z_bf16, flare_stream_t stream) {
+  if (R < 1) return fail(FLARE_EINVAL, "R=%d; need R >= 1", R);
+  if (rows < 0) return fail(FLARE_EINVAL, "rows must be >= 0");
+  if (D % 4 != 0 || D < 4 || D > 256) return fail(FLARE_EUNSUPPORTED, "D=%d unsupported", D);
+  if (R > 65535) return fail(FLARE_EUNSUPPORTED, "R=%d exceeds 65535 states", R);
+  if (rows == 0) return FLARE_OK;
+  if (!O_part || !L_part || !Z || !L) return fail(FLARE_EINVAL, "NULL pointer argument");
+  if (!aligned16(O_part) || !aligned16(Z)) return fail(FLARE_EINVAL, "O_part and Z must be 16-byte aligned");
+  if (Z_bf16 && (reinterpret_cast<uintptr_t>(Z_bf16) & 7u)) return fail(FLARE_EINVAL, "Z_bf16 must be 8-byte aligned");
+  FoldArgs f;
+  memset(&f, 0, sizeof(f));
+  f.in_O = O_part;
+  f.in_L = L_part;
+  f.out_O = Z;
+  f.out_L = L;
+  f.out_bf16 = static_cast<uint16_t*>(Z_bf16);
+  f.rows = rows;
+  f.D = D;
+  f.tab.ngroups = 1;
+  f.tab.in_begin[0] = 0;
+  f.tab.in_begin[1] = R;
+  f.tab.out_index[0] = 0;
+  hipError_t e = launch_fold(f, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return FLARE_OK;
+}
+
+flare_status flare_decode(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Xq,
+                          const void* Klat, int64_t klat_batch_stride, const float* Z,
+                          const uint8_t* token_mask, float scale, void* Y, flare_stream_t stream) {
+  flare_status st = check_common(dtype, B, H, N, M, D);
+  if (st != FLARE_OK) return st;
+  if (M > 256) return fail(FLARE_EUNSUPPORTED, "decode supports M <= 256 (M=%d)", M);
+  if (!std::isfinite(scale)) return fail(FLARE_EINVAL, "scale must be finite");
+  if (klat_batch_stride < 0) return fail(FLARE_EINVAL, "klat_batch_stride must be >= 0");
+  if ((int64_t)B * H * N == 0) return FLARE_OK;
+  if (M == 0) return fail(FLARE_EINVAL, "decode needs M >= 1 latents");
+  if (!Xq || !Klat || !Z || !Y) return fail(FLARE_EINVAL, "NULL pointer argument");
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Xq = Xq;
+  a.Klat = Klat;
+  a.Z = Z;
+  a.token_mask = token_mask;
+  a.Y = Y;
+  a.klat_bstride = klat_batch_stride;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.M = M;
+  a.D = D;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == FLARE_BF16 && decode_mfma_supported(M, D)) {
+    if (!aligned16(Xq) || !aligned16(Klat) || !aligned16(Y) || (klat_batch_stride * 2) % 16 != 0)
+      return fail(FLARE_EINVAL, "Xq, Klat, Y and the Klat batch stride must be 16-byte aligned");
+    // about a thousand workgroups, each at least one 128-token round
+    const int64_t per_slice = std::max<int64_t>(1, 1024 / std::max<int64_t>(1, (int64_t)B * H));
+    int tpb = (int)std::min<int64_t>(2048, (N + per_slice - 1) / per_slice);
+    tpb = std::max(128, round_up(tpb, 128));
+    a.tokens_per_block = tpb;
+    e = launch_decode_mfma(a, s);
+  } else {
+    e = launch_decode_generic(a, dtype == FLARE_BF16, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return FLARE_OK;
+}
+
+size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D, int R,
+                                       const int64_t* offsets) {
+  (void)dtype; (void)B; (void)H; (void)N; (void)M; (void)D; (void)R; (void)offsets;
+  return 0;
+}
+
+flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
+                              int64_t q_batch_stride, const void* K, const void* V, int R,
+                              const int64_t* offsets, const uint8_t* mask, float scale, const float* Z,
+                              const float* L, const void* dZ, float* dQ, void* dK, void* dV, void* workspace,
+                              size_t workspace_bytes, flare_stream_t stream) {
+  (void)Q; (void)q_batch_stride; (void)K; (void)V; (void)mask; (void)scale; (void)Z; (void)L; (void)dZ;
+  (void)dQ; (void)dK; (void)dV; (void)workspace; (void)workspace_bytes; (void)stream;
+  flare_status st = check_common(dtype, B, H, N, M, D);
+  if (st != FLARE_OK) return st;
+  st = check_offsets(N, R, offsets);
+  if (st != FLARE_OK) return st;
+  return fail(FLARE_EUNSUPPORTED, "encoder backward not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Launch-side interface between the C ABI (capi.hip) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flare {
+
+// A launch covers up to kMaxChunks token chunks; chunk c of the launch spans
+// tokens [bnd[c], bnd[c+1]) of every (batch, head) slice, and lies inside one
+// partition.  slot[c] >= 0 sends its state to workspace slot slot[c]; a
+// negative slot -(r+1) means the chunk is all of partition r and writes
+// O_part[r] / L_part[r] directly.
+constexpr int kMaxChunks = 256;
+
+struct ChunkTable {
+  int nchunks;
+  int32_t bnd[kMaxChunks + 1];
+  int16_t slot[kMaxChunks];
+};
+
+struct EncodeArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const uint8_t* mask;
+  float* O_part;   // [R,B,H,M,D]
+  float* L_part;   // [R,B,H,M]
+  float* ws_O;     // [slots,B,H,M,D]
+  float* ws_L;     // [slots,B,H,M]
+  int64_t q_bstride;
+  int B, H, N, M, D, R;
+  float scale;        // s
+  float scale_log2;   // s * log2(e)
+  ChunkTable tab;
+};
+
+// Group g folds input states [in_begin[g], in_begin[g+1]) of `in` into output
+// state out_index[g]; an empty group writes the empty state (0, -inf).
+constexpr int kMaxGroups = 256;
+struct FoldTable {
+  int ngroups;
+  int32_t in_begin[kMaxGroups + 1];
+  int32_t out_index[kMaxGroups];
+};
+
+struct FoldArgs {
+  const float* in_O;   // [S, rows, D]
+  const float* in_L;   // [S, rows]
+  float* out_O;        // [G, rows, D]
+  float* out_L;        // [G, rows]
+  uint16_t* out_bf16;  // nullable [G, rows, D]
+  int64_t rows;
+  int D;
+  FoldTable tab;
+};
+
+struct DecodeArgs {
+  const void* Xq;
+  const void* Klat;
+  const float* Z;
+  const uint8_t* token_mask;
+  void* Y;
+  int64_t klat_bstride;
+  int B, H, N, M, D;
+  float scale_log2;
+  int tokens_per_block;   // tokens handled by one workgroup
+};
+
+// Encoder kernels. Return hipSuccess or the launch error.
+bool encode_mfma_supported(int M, int D);
+hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s);
+bool encode_q1_supported(int M, int D);
+hipError_t launch_encode_q1(const EncodeArgs& a, hipStream_t s);
+hipError_t launch_encode_generic(const EncodeArgs& a, bool bf16, hipStream_t s);
+
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
+
+bool decode_mfma_supported(int M, int D);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace flare

@@ -1,0 +1,113 @@
+// Cross-partition merge of (O_r, L_r) states ("FLARE++: Low-rank attention
+// with dynamic attention routing", appendix on context parallelism, eqs.
+// 21-23 and the max-stabilised merge paragraph), evaluated as the balanced
+// binary tree of "Ring vs. Tree Attention" (two topologies section and the
+// semigroup proposition): leaves (m, l, acc) = (L_r, 1, O_r), empty leaves
+// (-inf, 0, 0); round k merges state i with state i + 2^k for i = 0 mod 2^(k+1)
+// and a state without a partner passes through; one merge takes
+// m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m), acc = acc1 e^(m1-m) + acc2 e^(m2-m).
+//
+// A thread owns one (row, 4 columns) and visits the leaves in order keeping
+// one partial state per tree level (a binary counter): after leaf i the
+// levels whose bit is set in i are merged into it.  Because i is the same for
+// every thread the branches are uniform and the level slots stay in
+// registers.  Leftover levels are merged from the lowest upwards, which is
+// exactly the round schedule above with its pass-through survivors.
+#include "common.h"
+#include "kernels.h"
+
+namespace flare {
+
+namespace {
+constexpr int kLevels = 16;   // up to 65536 states per group
+
+struct St {
+  float m, l;
+  f32x4_t acc;
+};
+
+__device__ __forceinline__ St merge_st(const St& x, const St& y) {
+  St r;
+  r.m = fmaxf(x.m, y.m);
+  if (r.m == kNegInf) {
+    r.l = 0.f;
+    r.acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    return r;
+  }
+  const float fx = __expf(x.m - r.m);   // exactly 0 for an empty side
+  const float fy = __expf(y.m - r.m);
+  r.l = x.l * fx + y.l * fy;
+  r.acc = x.acc * fx + y.acc * fy;
+  return r;
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void fold_kernel(const FoldArgs a) {
+  const int g = blockIdx.y;
+  const int D4 = a.D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.rows * D4) return;
+  const int64_t row = idx / D4;
+  const int c4 = (int)(idx % D4);
+  const int s0 = a.tab.in_begin[g], s1 = a.tab.in_begin[g + 1];
+  const int64_t sstride = a.rows * a.D;
+
+  St lv[kLevels];
+  St cur;
+  cur.m = kNegInf;
+  cur.l = 0.f;
+  cur.acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int n = s1 - s0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t s = s0 + i;
+    St leaf;
+    leaf.m = a.in_L[s * a.rows + row];
+    leaf.l = (leaf.m == kNegInf) ? 0.f : 1.f;
+    leaf.acc = (leaf.m == kNegInf) ? f32x4_t{0.f, 0.f, 0.f, 0.f}
+                                   : *reinterpret_cast<const f32x4_t*>(a.in_O + s * sstride + row * a.D + 4 * c4);
+    // carry: merge the completed left subtrees of equal size into the new
+    // leaf; the first level whose bit is clear in i takes the result
+    bool carry = true;
+#pragma unroll
+    for (int k = 0; k < kLevels; ++k) {
+      if (carry) {
+        if ((i >> k) & 1) {
+          leaf = merge_st(lv[k], leaf);
+        } else {
+          lv[k] = leaf;
+          carry = false;
+        }
+      }
+    }
+  }
+  // collect the levels still occupied (bits of n), lowest first
+  bool have = false;
+#pragma unroll
+  for (int k = 0; k < kLevels; ++k) {
+    if ((n >> k) & 1) {
+      cur = have ? merge_st(lv[k], cur) : lv[k];
+      have = true;
+    }
+  }
+  const int oi = a.tab.out_index[g];
+  const bool empty = !(cur.l > 0.f);
+  const float inv = empty ? 0.f : 1.f / cur.l;
+  f32x4_t z = cur.acc * inv;
+  if (empty) z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  *reinterpret_cast<f32x4_t*>(a.out_O + (int64_t)oi * sstride + row * a.D + 4 * c4) = z;
+  if (c4 == 0) a.out_L[(int64_t)oi * a.rows + row] = empty ? kNegInf : cur.m + __logf(cur.l);
+  if (a.out_bf16) {
+    u32x2_t w = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+    *reinterpret_cast<u32x2_t*>(a.out_bf16 + (int64_t)oi * sstride + row * a.D + 4 * c4) = w;
+  }
+}
+
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s) {
+  const int64_t n = a.rows * (a.D / 4);
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks == 0 || a.tab.ngroups == 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)blocks, (unsigned)a.tab.ngroups), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace flare

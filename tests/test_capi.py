@@ -1,0 +1,108 @@
+"""Host-side checks of the C ABI (CPU only): the library loads, exports every
+declared entry point, and validates arguments before touching the GPU.
+
+The validation paths return before any HIP call, so they run without a GPU;
+device pointers passed here are placeholders that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "flare.h")
+LIB = os.path.join(ROOT, "split_kv_softmax_amd", "libflare.so")
+
+EINVAL, EUNSUP, EWS = -1, -2, -4
+FAKE = ctypes.c_void_p(0x7f0000000000)   # aligned placeholder, never dereferenced
+
+
+def declared_functions():
+    txt = open(HDR).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b((?:flare|lse)_\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libflare.so is not built (run python -m split_kv_softmax_amd.build)")
+    L = ctypes.CDLL(LIB)
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.flare_encode.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp, sz, vp]
+    L.flare_encode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64]
+    L.flare_encode_workspace_size.restype = sz
+    L.lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp, vp]
+    L.flare_decode.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp]
+    L.flare_encode_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp,
+                                   vp, vp, vp, vp, sz, vp]
+    L.flare_encode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64]
+    L.flare_encode_bwd_workspace_size.restype = sz
+    L.flare_last_error.restype = ctypes.c_char_p
+    L.flare_version.restype = ctypes.c_char_p
+    return L
+
+
+def offs(*v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"flare_encode", "lse_merge", "flare_decode", "flare_encode_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert b"gfx950" in lib.flare_version()
+
+
+def _enc(lib, o, N=1024, M=64, D=64, dt=1, ws=None, nbytes=0, Q=FAKE):
+    return lib.flare_encode(dt, 1, 1, N, M, D, Q, 0, FAKE, FAKE, len(o) - 1, o, None, 0.125, FAKE, FAKE, ws, nbytes,
+                            None)
+
+
+def test_offsets_are_validated(lib):
+    assert _enc(lib, offs(1, 500, 1024)) == EINVAL                  # must start at 0
+    assert b"offsets[0]" in lib.flare_last_error()
+    assert _enc(lib, offs(0, 600, 500, 1024)) == EINVAL             # overlapping / unsorted
+    assert b"disjoint" in lib.flare_last_error()
+    assert _enc(lib, offs(0, 500, 1000)) == EINVAL                  # does not end at N
+    assert lib.flare_encode(1, 1, 1, 1024, 64, 64, FAKE, 0, FAKE, FAKE, 0, offs(0), None, 0.1, FAKE, FAKE, None, 0,
+                            None) == EINVAL                           # R = 0
+
+
+def test_shapes_pointers_and_scale_are_validated(lib):
+    assert _enc(lib, offs(0, 1024), D=6) == EUNSUP
+    assert _enc(lib, offs(0, 1024), D=512) == EUNSUP
+    assert _enc(lib, offs(0, 1024), dt=7) == EINVAL
+    assert _enc(lib, offs(0, 1024), Q=None) == EINVAL
+    assert lib.flare_encode(1, 1, 1, 1024, 64, 64, FAKE, 0, FAKE, FAKE, 1, offs(0, 1024), None, float("nan"), FAKE,
+                            FAKE, None, 0, None) == EINVAL
+    mis = ctypes.c_void_p(0x7f0000000002)
+    assert lib.flare_encode(1, 1, 1, 1024, 64, 64, mis, 0, FAKE, FAKE, 1, offs(0, 1024), None, 0.1, FAKE, FAKE,
+                            None, 0, None) == EINVAL                  # misaligned for the matrix-core path
+    assert lib.lse_merge(0, 10, 64, FAKE, FAKE, FAKE, FAKE, None, None) == EINVAL
+    assert lib.lse_merge(4, 10, 6, FAKE, FAKE, FAKE, FAKE, None, None) == EUNSUP
+    assert lib.flare_decode(1, 1, 1, 100, 300, 64, FAKE, FAKE, 0, FAKE, None, 0.1, FAKE, None) == EUNSUP
+    assert lib.flare_decode(1, 1, 1, 100, 64, 64, None, FAKE, 0, FAKE, None, 0.1, FAKE, None) == EINVAL
+
+
+def test_workspace_contract(lib):
+    o = offs(0, 40000, 80000)
+    n = lib.flare_encode_workspace_size(1, 1, 2, 80000, 128, 64, 2, o)
+    assert n > 0                                       # long partitions are split into chunks
+    assert n == lib.flare_encode_workspace_size(1, 1, 2, 80000, 128, 64, 2, o)
+    assert lib.flare_encode(1, 1, 2, 80000, 128, 64, FAKE, 0, FAKE, FAKE, 2, o, None, 0.125, FAKE, FAKE, None, 0,
+                            None) == EWS
+    assert b"workspace" in lib.flare_last_error()
+    assert lib.flare_encode(1, 1, 2, 80000, 128, 64, FAKE, 0, FAKE, FAKE, 2, o, None, 0.125, FAKE, FAKE, FAKE, n - 1,
+                            None) == EWS
+    # a small problem needs none, and invalid arguments report 0
+    assert lib.flare_encode_workspace_size(1, 1, 1, 1024, 64, 64, 1, offs(0, 1024)) == 0
+    assert lib.flare_encode_workspace_size(1, 1, 1, 1024, 64, 64, 2, offs(0, 900, 800)) == 0
+
+
+def test_backward_validates_offsets(lib):
+    assert lib.flare_encode_bwd(1, 1, 1, 100, 64, 64, FAKE, 0, FAKE, FAKE, 2, offs(0, 70, 60), None, 0.1, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, FAKE, None, 0, None) == EINVAL

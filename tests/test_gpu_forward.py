@@ -1,0 +1,279 @@
+"""GPU parity of the forward path (encode, merge, decode, FLARE, FLARE++) against the CPU oracle.
+
+Every case draws seeded inputs (workloads), runs the HIP library through its
+C ABI, copies the very same input bits to the host for the float64 oracle and
+compares element by element.  Sizes span several 64-token tiles, ragged
+partition tails and empty partitions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import split_kv_softmax_amd as fl
+import workloads as W
+from oracle import flare_ref as ref
+from tests._util import F32_ATOL, compare, compare_bf16, compare_L, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _enc_case(M, D, N, R, B=2, H=2, dtype="bf16", masked=False, q_per_batch=False, stress=1.0, wid=500):
+    base = W.Workload(name=f"case_M{M}_D{D}_N{N}", wid=wid + M + D, kind="encode", dtype=dtype, B=B, H=H, N=N,
+                      M=M, D=D, offsets=W.ragged_offsets(N, R, wid + M + D), q_std=D ** -0.5,
+                      q_per_batch=q_per_batch, stress=stress)
+    # make sure at least one partition is empty
+    offs = list(base.offsets)
+    if R >= 3:
+        offs[2] = offs[1]
+    base = base.with_(offsets=offs)
+    x = base.make(DEV)
+    if masked:
+        g = np.random.default_rng(wid)
+        m = (g.random((B, N)) > 0.35).astype(np.uint8)
+        m[:, 0] = 1
+        # one partition fully masked for batch 0
+        if R >= 4:
+            m[0, offs[3]:offs[4]] = 0
+        x["mask"] = torch.from_numpy(m).to(DEV)
+    return base, x
+
+
+def _check_encode(w, x, fp32=False, report=None):
+    mask = x.get("mask")
+    O_part, L_part = fl.encode(x["Q"], x["K"], x["V"], w.offsets, mask, w.scale)
+    Z, L, _ = fl.lse_merge(O_part, L_part)
+    torch.cuda.synchronize()
+    out = ref.encode_ref(x["Q"], x["K"], x["V"], w.offsets, mask, w.scale)
+    if fp32:
+        compare(O_part, out["O_part"], "O_part", F32_ATOL, report=report)
+        compare(L_part, out["L_part"], "L_part", F32_ATOL, report=report)
+        compare(Z, out["Z"], "Z", F32_ATOL, report=report)
+        compare(L, out["L"], "L", F32_ATOL, report=report)
+    else:
+        compare_bf16(O_part, out["O_part"], "O_part", report)
+        compare_L(L_part, out["L_part"], "L_part", report=report)
+        compare_bf16(Z, out["Z"], "Z", report)
+        compare_L(L, out["L"], "L", report=report)
+    return O_part, L_part, Z, L, out
+
+
+def test_fp32_small_encoder_workload():
+    """The single-head fp32 encoder with partitions 300/200/424/100 (max-abs 1e-5)."""
+    w = W.FLARE_ENCODE_F32_SMALL
+    x = w.make(DEV)
+    _check_encode(w, x, fp32=True)
+
+
+@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64), (64, 128), (128, 128), (256, 128)])
+@pytest.mark.parametrize("masked", [False, True])
+def test_bf16_encoder_matrix_core(M, D, masked):
+    w, x = _enc_case(M, D, N=2500, R=5, masked=masked)
+    _check_encode(w, x)
+
+
+def test_bf16_encoder_stress_scores():
+    """Q scaled so score spread is ~4: exercises the running-max rescale."""
+    w, x = _enc_case(128, 64, N=3000, R=4, stress=4 * 8.0)
+    _check_encode(w, x)
+
+
+def test_bf16_encoder_split_partitions():
+    """Long partitions split into several chunks and folded by the library."""
+    w = W.shrink(W.FLAREPP, 40000, R=2, H=2)
+    x = {"Q": W.normal((2, 128, 64), 77, W.T_Q, 1 / 8, torch.bfloat16, DEV),
+         "K": W.normal((1, 2, 40000, 64), 77, W.T_K, 1.0, torch.bfloat16, DEV),
+         "V": W.normal((1, 2, 40000, 64), 77, W.T_V, 1.0, torch.bfloat16, DEV)}
+    w = w.with_(kind="encode")
+    nbytes = fl.encode_workspace_size(torch.bfloat16, 1, 2, 40000, 128, 64, w.offsets)
+    assert nbytes > 0, "expected the library to split these partitions"
+    _check_encode(w, x)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_single_query_split_kv(D):
+    w, x = _enc_case(1, D, N=5000, R=7, B=2, H=3, q_per_batch=True)
+    _check_encode(w, x)
+
+
+def test_generic_vector_path_bf16():
+    """A bf16 shape without a matrix-core variant (M=16) takes the vector path."""
+    w, x = _enc_case(16, 64, N=700, R=3, masked=True)
+    _check_encode(w, x)
+
+
+def test_fp32_generic_larger():
+    w, x = _enc_case(24, 32, N=1500, R=4, dtype="f32", masked=True)
+    _check_encode(w, x, fp32=True)
+
+
+# ------------------------------------------------------------------- decode
+@pytest.mark.parametrize("M,D", [(64, 64), (128, 64), (64, 128), (256, 128)])
+def test_decode_matrix_core(M, D):
+    B, H, N = 2, 2, 1000
+    Xq = W.normal((B, H, N, D), 600 + M, W.T_K, 1.0, torch.bfloat16, DEV)
+    Kl = W.normal((H, M, D), 600 + M, W.T_Q, 1.0, torch.bfloat16, DEV)
+    Z = W.normal((B, H, M, D), 600 + M, W.T_V, 1.0, torch.float32, DEV)
+    s = W.scale_for(D)
+    Y = fl.decode(Xq, Kl, Z, s)
+    torch.cuda.synchronize()
+    compare_bf16(Y, ref.decode_ref(Xq, Kl, Z, s), "Y")
+
+
+def test_decode_token_mask_and_fp32():
+    B, H, N, M, D = 2, 3, 333, 20, 32
+    Xq = W.normal((B, H, N, D), 610, W.T_K, 1.0, torch.float32, DEV)
+    Kl = W.normal((B, H, M, D), 610, W.T_Q, 1.0, torch.float32, DEV)
+    Z = W.normal((B, H, M, D), 610, W.T_V, 1.0, torch.float32, DEV)
+    tm = (torch.rand(B, N, generator=torch.Generator().manual_seed(3)) > 0.3).to(torch.uint8).to(DEV)
+    Y = fl.decode(Xq, Kl, Z, 0.2, token_mask=tm)
+    torch.cuda.synchronize()
+    compare(Y, ref.decode_ref(Xq, Kl, Z, 0.2, token_mask=tm), "Y", F32_ATOL)
+
+
+def test_decode_token_mask_bf16():
+    B, H, N, M, D = 1, 2, 500, 128, 64
+    Xq = W.normal((B, H, N, D), 611, W.T_K, 1.0, torch.bfloat16, DEV)
+    Xq[0, :, 7] = float("nan")          # a padded token's row may hold anything
+    Kl = W.normal((H, M, D), 611, W.T_Q, 1.0, torch.bfloat16, DEV)
+    Z = W.normal((B, H, M, D), 611, W.T_V, 1.0, torch.float32, DEV)
+    tm = torch.ones(B, N, dtype=torch.uint8, device=DEV)
+    tm[0, 7] = 0
+    tm[0, 100:140] = 0
+    Y = fl.decode(Xq, Kl, Z, 0.125, token_mask=tm)
+    torch.cuda.synchronize()
+    compare_bf16(Y, ref.decode_ref(Xq.nan_to_num(0.0), Kl, Z, 0.125, token_mask=tm), "Y")
+
+
+# ------------------------------------------------------------ FLARE / FLARE++
+def test_flare_block_small():
+    w = W.shrink(W.FLARE_BLOCK, 6000, R=8, B=2, H=2, ragged=True)
+    x = w.make(DEV)
+    out = fl.flare_forward(x["Q"], x["K"], x["V"], w.offsets, None, w.scale)
+    torch.cuda.synchronize()
+    e = ref.encode_ref(x["Q"], x["K"], x["V"], w.offsets, None, w.scale)
+    compare_bf16(out["Z"], e["Z"], "Z")
+    compare_L(out["L"], e["L"], "L")
+    compare_bf16(out["Y"], ref.decode_ref(x["K"], x["Q"], e["Z"], w.scale), "Y")
+
+
+def test_flarepp_small():
+    w = W.shrink(W.FLAREPP, 5000, R=4, H=2, ragged=True)
+    x = w.make(DEV)
+    out = fl.flarepp_forward(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale)
+    torch.cuda.synchronize()
+    r = ref.flarepp_ref(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale)
+    compare_bf16(out["QX"], r["QX"], "QX")
+    compare_bf16(out["Z"], r["Z"], "Z")
+    compare_L(out["L"], r["L"], "L")
+    compare_bf16(out["Y"], r["Y"], "Y")
+
+
+# ------------------------------------------------------- exactness properties
+def test_empty_and_fully_masked_partitions_are_exact():
+    w, x = _enc_case(64, 64, N=1200, R=5, masked=True)
+    O_part, L_part = fl.encode(x["Q"], x["K"], x["V"], w.offsets, x["mask"], w.scale)
+    torch.cuda.synchronize()
+    o = O_part.cpu()
+    l = L_part.cpu()
+    assert torch.isneginf(l[1]).all()                          # empty by offsets
+    assert (o[1] == 0).all() and not torch.signbit(o[1]).any()
+    assert torch.isneginf(l[3, 0]).all() and (o[3, 0] == 0).all()   # fully masked, batch 0
+    assert not torch.isnan(o).any()
+
+
+def test_nan_padding_never_leaks():
+    w, x = _enc_case(128, 64, N=1500, R=4, masked=True)
+    inv = (x["mask"] == 0)[:, None, :, None].expand_as(x["K"])
+    K2 = x["K"].masked_fill(inv, float("nan"))
+    V2 = x["V"].masked_fill(inv, float("inf"))
+    a = fl.encode(x["Q"], x["K"], x["V"], w.offsets, x["mask"], w.scale)
+    b = fl.encode(x["Q"], K2, V2, w.offsets, x["mask"], w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert not torch.isnan(b[0]).any()
+
+
+def test_runs_are_bitwise_deterministic():
+    w, x = _enc_case(128, 64, N=9000, R=3)
+    a = fl.flare_forward(x["Q"], x["K"], x["V"], w.offsets)
+    b = fl.flare_forward(x["Q"], x["K"], x["V"], w.offsets)
+    torch.cuda.synchronize()
+    for k in ("O_part", "L_part", "Z", "L", "Y"):
+        assert torch.equal(a[k], b[k]), k
+
+
+# ------------------------------------------------------------ spike tests
+def _spike_inputs(B, H, N, M, D, spikes, device=DEV):
+    """Q[m] = a e_{m mod D}; K[n*] = a e_j for each (n*, j) spike, 0 elsewhere;
+    V rows carry (n mod 256, n // 256 mod 256, h, b) as bf16-exact integers."""
+    a = 32.0 if D <= 64 else 64.0
+    Q = torch.zeros(H, M, D)
+    for m in range(M):
+        Q[:, m, m % D] = a
+    K = torch.zeros(B, H, N, D)
+    for n, j in spikes:
+        K[:, :, n, j] = a
+    n_idx = torch.arange(N, dtype=torch.float32)
+    V = torch.zeros(B, H, N, D)
+    V[..., 0] = (n_idx % 256)[None, None]
+    V[..., 1] = ((n_idx // 256) % 256)[None, None]
+    V[..., 2] = torch.arange(H, dtype=torch.float32)[None, :, None]
+    V[..., 3] = torch.arange(B, dtype=torch.float32)[:, None, None]
+    return (Q.to(torch.bfloat16).to(device), K.to(torch.bfloat16).to(device), V.to(torch.bfloat16).to(device))
+
+
+@pytest.mark.parametrize("M,D", [(64, 64), (128, 64), (256, 128), (1, 128)])
+def test_spike_index_handling_is_bit_exact(M, D):
+    B, H = 2, 3
+    offs = [0, 300, 500, 500, 924, 1024, 1500]
+    N = offs[-1]
+    # spikes at partition edges and tile tails, one direction each
+    positions = [0, 299, 300, 499, 500, 563, 923, 924, 1023, 1024, 1087, 1499]
+    dirs = list(range(len(positions)))
+    spikes = list(zip(positions, dirs))
+    Q, K, V = _spike_inputs(B, H, N, M, D, spikes)
+    if M == 1:
+        Q = Q[:, :1].unsqueeze(0).expand(B, H, 1, D).contiguous()
+        Q[:] = 0
+        Q[..., 5] = 32.0 if D <= 64 else 64.0         # row 0 looks for direction 5 -> token 923
+    s = W.scale_for(D)
+    O_part, L_part = fl.encode(Q, K, V, offs, None, s)
+    Z, L, _ = fl.lse_merge(O_part, L_part)
+    torch.cuda.synchronize()
+    Zc, Vc = Z.cpu(), V.float().cpu()
+    for m in range(M):
+        j = (m % D) if M > 1 else 5
+        if j >= len(positions):
+            continue
+        n_star = positions[j]
+        r_star = max(r for r in range(len(offs) - 1) if offs[r] <= n_star < offs[r + 1])
+        assert torch.equal(Zc[:, :, m], Vc[:, :, n_star]), (m, n_star)
+        assert torch.equal(O_part[r_star, :, :, m].cpu(), Vc[:, :, n_star]), (m, n_star, r_star)
+    # empty partition 2 is exactly (0, -inf)
+    assert torch.isneginf(L_part[2]).all() and (O_part[2] == 0).all()
+    if M > 1:
+        # decode: spike token n*_j attends only to latents with direction j
+        Y = fl.decode(K, Q, Z, s)
+        torch.cuda.synchronize()
+        Yc = Y.float().cpu()
+        for j, n_star in enumerate(positions):
+            if j >= min(M, D):
+                continue
+            assert torch.equal(Yc[:, :, n_star], Zc[:, :, j]), (j, n_star)
+
+
+def test_uniform_scores_give_mean_of_v_on_gpu():
+    """Q = 0: every valid score is 0, so Z is the mean of the valid V rows and L = ln(count)."""
+    w, x = _enc_case(64, 64, N=1000, R=4, masked=True)
+    Q = torch.zeros_like(x["Q"])
+    O_part, L_part = fl.encode(Q, x["K"], x["V"], w.offsets, x["mask"], w.scale)
+    Z, L, _ = fl.lse_merge(O_part, L_part)
+    torch.cuda.synchronize()
+    m = x["mask"].cpu().bool()
+    V = to64(x["V"])
+    for b in range(w.B):
+        cnt = int(m[b].sum())
+        np.testing.assert_allclose(to64(L[b]), np.log(cnt), rtol=0, atol=1e-5)
+        mean = V[b][:, m[b].numpy()].mean(axis=1)       # [H, D]
+        np.testing.assert_allclose(to64(Z[b]), np.broadcast_to(mean[:, None, :], Z[b].shape), rtol=0, atol=1e-5)
