@@ -1,0 +1,193 @@
+"""Throughput of the split-KV / FLARE softmax hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of synthetic input that
+already sits in HBM.  For the default workload (FLARE++, B=1, H=16, N=262144,
+M=128, D=64, R=16, bf16) that is: encoder 1 over (Q~, K~, V~) -> merge ->
+encoder 2 over (Q(X), K, V) -> merge -> decode of every token.  The line
+printed is one JSON object: tokens/s (B*N*H per step), the roofline of the
+dominant kernel (the encoder: achieved algorithmic HBM bytes per launch over
+its event-timed duration) and the CPU oracle timed on a bounded sample.
+
+Only one GPU is used; --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import split_kv_softmax_amd as fl  # noqa: E402
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
+
+
+def _ev():
+    return torch.cuda.Event(enable_timing=True)
+
+
+class FlareppStep:
+    """The FLARE++ forward chain with preallocated outputs."""
+
+    def __init__(self, w: W.Workload, x):
+        self.w, self.x = w, x
+        B, H, N, M, D, R = w.B, w.H, w.N, w.M, w.D, w.R
+        dev = x["K"].device
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.O1 = torch.empty((R, B, H, M, D), **f32)
+        self.L1 = torch.empty((R, B, H, M), **f32)
+        self.QX = torch.empty((B, H, M, D), **f32)
+        self.QXL = torch.empty((B, H, M), **f32)
+        self.QXb = torch.empty((B, H, M, D), dtype=torch.bfloat16, device=dev)
+        self.O2 = torch.empty_like(self.O1)
+        self.L2 = torch.empty_like(self.L1)
+        self.Z = torch.empty((B, H, M, D), **f32)
+        self.L = torch.empty((B, H, M), **f32)
+        self.Y = torch.empty_like(x["K"])
+        self.ev = [_ev() for _ in range(6)]
+        # per-phase (enc1, merge1, enc2, merge2, decode) milliseconds
+        self.phase_ms = [0.0] * 5
+        self.count = 0
+
+    def __call__(self, timed_phases: bool):
+        x, w, ev = self.x, self.w, self.ev
+        if timed_phases:
+            ev[0].record()
+        fl.encode(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.O1, self.L1)
+        if timed_phases:
+            ev[1].record()
+        fl.lse_merge(self.O1, self.L1, Z=self.QX, L=self.QXL, Z_bf16=self.QXb)
+        if timed_phases:
+            ev[2].record()
+        fl.encode(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, self.O2, self.L2)
+        if timed_phases:
+            ev[3].record()
+        fl.lse_merge(self.O2, self.L2, Z=self.Z, L=self.L)
+        if timed_phases:
+            ev[4].record()
+        fl.decode(x["K"], self.QXb, self.Z, w.scale, None, self.Y)
+        if timed_phases:
+            ev[5].record()
+
+    def collect(self):
+        torch.cuda.synchronize()
+        for i in range(5):
+            self.phase_ms[i] += self.ev[i].elapsed_time(self.ev[i + 1])
+        self.count += 1
+
+
+def cpu_baseline_flarepp(w: W.Workload, x, heads=1):
+    """Time the float64 oracle on `heads` heads of the same inputs (full N)."""
+    import numpy as np
+    from oracle import flare_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    sl = [(0, h) for h in range(heads)]
+    # copy the sampled slices to the host before the clock starts
+    xs = {k: (v[:heads] if v.dim() == 3 else v[:, :heads]).cpu() for k, v in x.items()}
+    t0 = time.perf_counter()
+    ref.flarepp_ref(xs["Qt"], xs["Kt"], xs["Vt"], xs["K"], xs["V"], w.offsets, w.scale, slices=sl)
+    dt = time.perf_counter() - t0
+    tokens = w.B * w.N * heads
+    _ = np
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"FLARE++ chain (2 encoders + decode) for {heads} of {w.H} heads, batch 0, full N={w.N}; "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.FLAREPP.name)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path is per-GPU and this build has no multi-GPU leg.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(2)
+    w = W.BY_NAME[args.workload]
+    if w.kind != "flarepp":
+        print("only the FLARE++ workload is wired into this bench", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    x = w.make("cuda")
+    step = FlareppStep(w, x)
+    for _ in range(args.warmup):
+        step(timed_phases=False)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    t_start, t_end = _ev(), _ev()
+    torch.cuda.synchronize()
+    t_start.record()
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timed_phases=False)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # per-kernel durations from events on the launch stream (separate pass)
+    for _ in range(args.steps):
+        step(timed_phases=True)
+        step.collect()
+    ph = [p / step.count for p in step.phase_ms]
+    enc_ms = 0.5 * (ph[0] + ph[2])
+    kv_bytes = 2 * w.B * w.H * w.N * w.D * 2          # K and V, bf16, read once per encoder launch
+    step_bytes = 6 * w.B * w.H * w.N * w.D * 2        # 2 encoders (K,V) + decode (read K, write Y)
+    achieved = kv_bytes / (enc_ms * 1e-3) / 1e9
+    tokens = w.B * w.N * w.H
+
+    line = {
+        "metric": "FLARE encode+decode tokens/sec (B*N*H) at N=256K; % of HBM/MFMA roofline",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs rounded to bf16)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "R": w.R,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "flare_encode (encode_mfma_kernel<64,4> + partition fold)",
+                     "kernel_ms": enc_ms},
+        "step_roofline": {"algorithmic_bytes": step_bytes,
+                          "achieved_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                          "frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "phases_ms": {"encode1": ph[0], "merge1": ph[1], "encode2": ph[2], "merge2": ph[3], "decode": ph[4]},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_flarepp(w, x, heads=args.cpu_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

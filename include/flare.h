@@ -66,10 +66,11 @@ typedef enum flare_dtype { FLARE_F32 = 0, FLARE_BF16 = 1 } flare_dtype;
 /* hipStream_t, passed as an opaque pointer so this header needs no HIP headers. */
 typedef void* flare_stream_t;
 
-/* Bytes of device workspace flare_encode needs for these arguments (0 if none).
- * Returns 0 as well when the arguments are invalid; flare_encode reports those. */
+/* Bytes of device workspace flare_encode needs for these arguments (0 if none);
+ * masked != 0 when flare_encode will be given a padding mask.  Returns 0 as
+ * well when the arguments are invalid; flare_encode reports those. */
 size_t flare_encode_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D,
-                                   int R, const int64_t* offsets);
+                                   int R, const int64_t* offsets, int masked);
 
 /*
  * flare_encode -- the local-shard encoder of [FLARE++] (the equations between

@@ -54,7 +54,7 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     p64 = ctypes.POINTER(ctypes.c_int64)
-    lib.flare_encode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64]
+    lib.flare_encode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64, i32]
     lib.flare_encode_workspace_size.restype = sz
     lib.flare_encode.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp,
                                  vp, sz, vp]
@@ -165,9 +165,10 @@ def _mask_check(mask: Optional[torch.Tensor], B: int, N: int, device, name="mask
     return mask.view(torch.uint8) if mask.dtype == torch.bool else mask
 
 
-def encode_workspace_size(dtype: torch.dtype, B, H, N, M, D, offsets) -> int:
+def encode_workspace_size(dtype: torch.dtype, B, H, N, M, D, offsets, masked: bool = False) -> int:
     code = BF16 if dtype == torch.bfloat16 else F32
-    return int(_load().flare_encode_workspace_size(code, B, H, N, M, D, len(offsets) - 1, _offsets(offsets)))
+    return int(_load().flare_encode_workspace_size(code, B, H, N, M, D, len(offsets) - 1, _offsets(offsets),
+                                                   int(masked)))
 
 
 def encode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, offsets: Sequence[int],
@@ -196,7 +197,7 @@ def encode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, offsets: Sequence[
     _dev(L_part, "L_part")
     offs = _offsets(offsets)
     code = _dtype_code(K)
-    nbytes = int(lib.flare_encode_workspace_size(code, B, H, N, M, D, R, offs))
+    nbytes = int(lib.flare_encode_workspace_size(code, B, H, N, M, D, R, offs, int(mask is not None)))
     ws = _workspace(nbytes, dev)
     with torch.cuda.device(dev):
         _check(lib.flare_encode(code, B, H, N, M, D, _ptr(Q), qbs, _ptr(K), _ptr(V), R, offs, _ptr(mask),

@@ -26,6 +26,9 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs: the softmax reads the scores and
+    # rescales the accumulators with plain VALU ops, no AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -79,6 +79,9 @@ struct EncodePlan {
   std::vector<int> first_chunk;   // per partition, index into chunks; size R+1
   std::vector<int16_t> slot;      // per chunk
   int nslots = 0;
+  size_t mw_bytes = 0;    // validity words of the padding mask (matrix-core path)
+  int64_t mw_stride = 0;  // words per batch row
+  size_t o_bytes = 0;     // partial outputs of split partitions
   size_t ws_bytes = 0;
 };
 
@@ -113,7 +116,9 @@ int chunk_len_for(EncKind kind, int B, int H, int R, int M, int64_t max_part) {
   }
 }
 
-EncodePlan plan_encode(flare_dtype dt, int B, int H, int N, int M, int D, int R, const int64_t* off) {
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+EncodePlan plan_encode(flare_dtype dt, int B, int H, int N, int M, int D, int R, const int64_t* off, bool masked) {
   EncodePlan p;
   p.kind = encode_kind(dt, M, D);
   int64_t max_part = 0;
@@ -141,7 +146,13 @@ EncodePlan plan_encode(flare_dtype dt, int B, int H, int N, int M, int D, int R,
     }
   }
   const size_t per = (size_t)B * H * M;
-  p.ws_bytes = p.nslots ? (size_t)p.nslots * per * (D + 1) * sizeof(float) + 256 : 0;
+  if (masked && p.kind == EncKind::Mfma) {
+    p.mw_stride = (N + 63) / 64 + 1;     // one spare word for tiles that straddle the end
+    p.mw_bytes = align256((size_t)B * p.mw_stride * sizeof(uint64_t));
+  }
+  if (p.nslots) p.o_bytes = align256((size_t)p.nslots * per * D * sizeof(float));
+  const size_t l_bytes = p.nslots ? align256((size_t)p.nslots * per * sizeof(float)) : 0;
+  p.ws_bytes = p.mw_bytes + p.o_bytes + l_bytes;
   return p;
 }
 
@@ -160,13 +171,13 @@ const char* flare_last_error(void) { return g_err.c_str(); }
 const char* flare_version(void) { return "libflare 0.1 (gfx950)"; }
 
 size_t flare_encode_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D, int R,
-                                   const int64_t* offsets) {
+                                   const int64_t* offsets, int masked) {
   const std::string saved = g_err;
   if (check_common(dtype, B, H, N, M, D) != FLARE_OK || check_offsets(N, R, offsets) != FLARE_OK) {
     g_err = saved;
     return 0;
   }
-  return plan_encode(dtype, B, H, N, M, D, R, offsets).ws_bytes;
+  return plan_encode(dtype, B, H, N, M, D, R, offsets, masked != 0).ws_bytes;
 }
 
 flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
@@ -183,7 +194,7 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, 
   if (!O_part || !L_part) return fail(FLARE_EINVAL, "O_part and L_part must not be NULL");
   if (!Q) return fail(FLARE_EINVAL, "Q must not be NULL");
   if (N > 0 && (!K || !V)) return fail(FLARE_EINVAL, "K and V must not be NULL");
-  const EncodePlan plan = plan_encode(dtype, B, H, N, M, D, R, offsets);
+  const EncodePlan plan = plan_encode(dtype, B, H, N, M, D, R, offsets, mask != nullptr);
   if (!plan_fits(plan, R)) return fail(FLARE_EUNSUPPORTED, "too many partitions or chunks (R=%d)", R);
   if (plan.kind != EncKind::Generic) {
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || (q_batch_stride * esize(dtype)) % 16 != 0)
@@ -207,10 +218,14 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, 
   a.O_part = O_part;
   a.L_part = L_part;
   const size_t per = (size_t)B * H * M;
+  char* ws = static_cast<char*>(workspace);
+  if (plan.mw_bytes) {
+    a.mask_words = reinterpret_cast<const uint64_t*>(ws);
+    a.mask_words_stride = plan.mw_stride;
+  }
   if (plan.nslots) {
-    a.ws_O = static_cast<float*>(workspace);
-    const size_t o_bytes = ((size_t)plan.nslots * per * D * sizeof(float) + 255) / 256 * 256;
-    a.ws_L = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    a.ws_O = reinterpret_cast<float*>(ws + plan.mw_bytes);
+    a.ws_L = reinterpret_cast<float*>(ws + plan.mw_bytes + plan.o_bytes);
   }
   a.q_bstride = q_batch_stride;
   a.B = B;
@@ -221,6 +236,12 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, 
   a.R = R;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+
+  if (plan.mw_bytes) {
+    hipError_t e = launch_mask_words(mask, B, N, reinterpret_cast<uint64_t*>(ws), plan.mw_stride, s);
+    if (e != hipSuccess) return hip_fail(e, "mask launch");
+  }
+  (void)per;
 
   // encoder launches over groups of at most kMaxChunks consecutive chunks
   const int nc = (int)plan.chunks.size();
@@ -334,10 +355,11 @@ flare_status flare_decode(flare_dtype dtype, int B, int H, int N, int M, int D, 
   if (dtype == FLARE_BF16 && decode_mfma_supported(M, D)) {
     if (!aligned16(Xq) || !aligned16(Klat) || !aligned16(Y) || (klat_batch_stride * 2) % 16 != 0)
       return fail(FLARE_EINVAL, "Xq, Klat, Y and the Klat batch stride must be 16-byte aligned");
-    // about a thousand workgroups, each at least one 128-token round
+    // about a thousand workgroups, each at least one round of its waves
+    const int round = 32 * decode_waves(D);
     const int64_t per_slice = std::max<int64_t>(1, 1024 / std::max<int64_t>(1, (int64_t)B * H));
     int tpb = (int)std::min<int64_t>(2048, (N + per_slice - 1) / per_slice);
-    tpb = std::max(128, round_up(tpb, 128));
+    tpb = std::min(2048, std::max(round, round_up(tpb, round)));
     a.tokens_per_block = tpb;
     e = launch_decode_mfma(a, s);
   } else {

@@ -69,4 +69,46 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
+// ---- LDS ring helpers shared by the streaming kernels
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+// Direct HBM -> LDS load: lane l's 16 bytes at g land at lds_wave_base + 16*l.
+// Written as inline asm on purpose: the compiler then does not treat the LDS
+// ring as written by outstanding vector-memory operations, so it neither
+// drains them before every LDS read nor at every barrier; the kernel counts
+// and waits for them itself (wait_vm) before a barrier publishes a stage.
+// M0 (which carries the LDS destination) is saved and restored around it.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"                       // one wait state between an SALU write of M0 and its use
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_wave_base), "v"(g)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding vector-memory operation, including the ring's
+// in-flight tiles).  LDS writes made with ds_* are completed first.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 }  // namespace flare

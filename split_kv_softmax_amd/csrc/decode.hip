@@ -9,28 +9,55 @@
 namespace flare {
 
 // ---------------------------------------------------------------------------
-// bf16 matrix-core decode.  A workgroup (4 waves) owns one (batch, head) and a
-// run of tokens; each wave handles 32 tokens at a time:
-//   T^T[m][n] = Klat Xq^T         (A = latent rows from LDS, B = token rows
-//                                  loaded straight into registers)
+// bf16 matrix-core decode.  A workgroup of NWV waves owns one (batch, head) and
+// a run of tokens; each wave handles 32 tokens at a time:
+//   T^T[m][n] = Klat Xq^T         (A = latent rows from LDS, B = token rows)
 //   softmax over m                 (a token's M scores sit in one lane pair)
 //   Y^T[d][n] = Z^T P^T            (A = Z^T in bf16 from LDS, B = P)
-// so the normalisation by the row sum is lane-local.  Klat and Z are staged in
-// LDS once per workgroup.
+// so the normalisation by the row sum is lane-local.  Klat, Z and the token
+// mask are staged in LDS once per workgroup.  Token rows travel HBM -> LDS by
+// direct loads into a per-wave ring of S blocks: waves never wait for each
+// other, and S-1 blocks of a wave are in flight while it computes one.
 // ---------------------------------------------------------------------------
-template <int D, int MB>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
+__device__ __forceinline__ int row_swz(int D, int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+
+template <int NI, int ST, int S>
+__device__ __forceinline__ void wait_block(int later_blocks, int later_stores) {
+  // vector-memory ops issued after block j's loads: later_blocks more blocks of
+  // NI loads and later_stores blocks of ST stores
+#define FL_W(B, T)                                  \
+  if (later_blocks == B && later_stores == T) {     \
+    wait_vm<(NI * B + ST * T) < 64 ? (NI * B + ST * T) : 63>(); \
+    return;                                         \
+  }
+  static_assert(S <= 3, "wait table covers S <= 3");
+  static_assert(NI * (S - 2 > 0 ? S - 2 : 0) + ST * (S - 1) < 64, "vmcnt range");
+  FL_W(0, 0) FL_W(0, 1) FL_W(0, 2) FL_W(1, 0) FL_W(1, 1) FL_W(1, 2)
+#undef FL_W
+  wait_vm<0>();
+}
+
+template <int D, int MB, int NWV, int S>
+__global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int M = 32 * MB;
   constexpr int KS = D / 16;   // k-steps of the score product
   constexpr int DB = D / 32;   // 32-row blocks of Y^T
   constexpr int MS = M / 16;   // k-steps of the value product
   constexpr int KLD = D + 8;
   constexpr int ZLD = M + 8;
+  constexpr int BLK = 32;                    // tokens per wave block
+  constexpr int ROWB = 2 * D;
+  constexpr int BB = BLK * ROWB;             // bytes per block
+  constexpr int NI = BB / 1024;              // direct loads per block
+  constexpr int ST = DB * 4;                 // 8-byte stores per block and lane
+  constexpr int MAXT = 2048;                 // tokens per workgroup (host keeps tokens_per_block <= MAXT)
   __shared__ __attribute__((aligned(16))) uint16_t Kl[M * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Zt[D * ZLD];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * S * BB];
+  __shared__ uint8_t tmask[MAXT];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int nblk = (a.N + a.tokens_per_block - 1) / a.tokens_per_block;
   int bid = blockIdx.x;
   const int tb = bid % nblk;
@@ -38,36 +65,64 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
   const int h = bid % a.H;
   const int b = bid / a.H;
   const int64_t bh = (int64_t)b * a.H + h;
+  const int n_lo = tb * a.tokens_per_block;
+  const int n_hi = min(a.N, n_lo + a.tokens_per_block);
 
-  {  // stage latent keys (row-major) and Z (transposed, rounded to bf16)
+  {  // stage latent keys (row-major), Z (transposed, rounded to bf16) and the token mask
     const uint16_t* kg = static_cast<const uint16_t*>(a.Klat) + (int64_t)b * a.klat_bstride + (int64_t)h * M * D;
-    for (int f = tid; f < M * D / 8; f += 256) {
+    for (int f = tid; f < M * D / 8; f += 64 * NWV) {
       const int row = f / (D / 8), chk = f % (D / 8);
       st16(&Kl[row * KLD + 8 * chk], ld16(kg + (int64_t)row * D + 8 * chk));
     }
     const float* zg = a.Z + bh * (int64_t)M * D;
-    for (int f = tid; f < M * D; f += 256) {
+    for (int f = tid; f < M * D; f += 64 * NWV) {
       const int m = f / D, d = f % D;
       Zt[d * ZLD + m] = to_bf16(zg[f]);
     }
+    const uint8_t* tm = a.token_mask ? a.token_mask + (int64_t)b * a.N : nullptr;
+    for (int i = tid; i < n_hi - n_lo; i += 64 * NWV) tmask[i] = tm ? tm[n_lo + i] : (uint8_t)1;
   }
-  __syncthreads();
+  __syncthreads();   // also completes the staging loads before the ring starts
 
   const uint16_t* Xg = static_cast<const uint16_t*>(a.Xq) + bh * (int64_t)a.N * D;
   uint16_t* Yg = static_cast<uint16_t*>(a.Y) + bh * (int64_t)a.N * D;
-  const uint8_t* tm = a.token_mask ? a.token_mask + (int64_t)b * a.N : nullptr;
   const float c2 = a.scale_log2;
-  const int n_lo = tb * a.tokens_per_block;
-  const int n_hi = min(a.N, n_lo + a.tokens_per_block);
+  uint8_t* myring = ring + wave * (S * BB);
+  const uint32_t myring_lds = lds_addr(myring);
 
-  for (int n0 = n_lo + 32 * wave; n0 < n_hi; n0 += 128) {
+  // blocks of this wave: tokens n_lo + 32*(wave + NWV*j)
+  const int span = n_hi - n_lo - BLK * wave;
+  const int nb = span > 0 ? (span + BLK * NWV - 1) / (BLK * NWV) : 0;
+  auto issue = [&](int j) {
+    const int n0 = n_lo + BLK * (wave + NWV * j);
+    const uint32_t st = myring_lds + (j % S) * BB;
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int byte = ii * 1024 + lane * 16;
+      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+      const int ch = pc ^ row_swz(D, r);
+      const int rr = n0 + r < n_hi ? r : 0;   // rows past the run re-read row 0 (results not stored)
+      dma16(Xg + (int64_t)(n0 + rr) * D + 8 * ch, st + ii * 1024);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (j < nb) issue(j);
+
+  const int swx = row_swz(D, l32);
+  for (int j = 0; j < nb; ++j) {
+    const int lb = min(S - 2, nb - 1 - j);          // blocks loaded after block j
+    const int ls = min(j, S - 1);                   // blocks stored after block j was loaded
+    wait_block<NI, ST, S>(lb > 0 ? lb : 0, ls);
+    if (j + S - 1 < nb) issue(j + S - 1);
+    const int n0 = n_lo + BLK * (wave + NWV * j);
     const int n = n0 + l32;
     const bool inb = n < n_hi;
+    const uint8_t* xs = myring + (j % S) * BB + l32 * ROWB;
     bf16x8_t xop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      xop[ks] = inb ? __builtin_bit_cast(bf16x8_t, ld16(Xg + (int64_t)n * D + 16 * ks + 8 * hh))
-                    : bf16x8_t{};
+      xop[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (((2 * ks + hh) ^ swx) * 16)));
     f32x16_t t[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -93,9 +148,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
       for (int g = 0; g < 2; ++g) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = fast_exp2(__builtin_fmaf(t[mb][8 * g + j], c2, nmc));
-          lsum += p[j];
+        for (int jj = 0; jj < 8; ++jj) {
+          p[jj] = fast_exp2(__builtin_fmaf(t[mb][8 * g + jj], c2, nmc));
+          lsum += p[jj];
         }
         u32x4_t w;
         w[0] = pack_bf16x2(p[0], p[1]);
@@ -115,20 +170,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeArgs a) {
         y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)),
                              pk[ks], y[db]);
     }
-    const bool keep = inb && (!tm || tm[n] != 0);
+    const bool keep = inb && tmask[inb ? n - n_lo : 0] != 0;
     const float inv = 1.f / lsum;
     if (inb) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          u32x2_t w;
-          if (keep) {
-            w[0] = pack_bf16x2(y[db][4 * q] * inv, y[db][4 * q + 1] * inv);
-            w[1] = pack_bf16x2(y[db][4 * q + 2] * inv, y[db][4 * q + 3] * inv);
-          } else {
-            w = u32x2_t{0u, 0u};
-          }
+          // select rather than branch: every block issues the same stores,
+          // which the ring's wait counts rely on
+          const uint32_t w0 = pack_bf16x2(y[db][4 * q] * inv, y[db][4 * q + 1] * inv);
+          const uint32_t w1 = pack_bf16x2(y[db][4 * q + 2] * inv, y[db][4 * q + 3] * inv);
+          const u32x2_t w = {keep ? w0 : 0u, keep ? w1 : 0u};
           *reinterpret_cast<u32x2_t*>(Yg + (int64_t)n * D + 32 * db + 8 * q + 4 * hh) = w;
         }
     }
@@ -142,15 +195,21 @@ bool decode_mfma_supported(int M, int D) {
   return false;
 }
 
+// waves per workgroup of the matrix-core decode (tokens_per_block is a multiple of 32 * this)
+int decode_waves(int D) { return D == 64 ? 8 : 4; }
+
 template <int D, int MB>
 static hipError_t launch_dec_t(const DecodeArgs& a, hipStream_t s) {
+  constexpr int NWV = D == 64 ? 8 : 4;
+  constexpr int S = (D == 64 && MB <= 4) ? 3 : 2;   // LDS: ring + staged latents within 160 KB
   const int64_t nblk = (a.N + a.tokens_per_block - 1) / a.tokens_per_block;
   const int64_t grid = nblk * a.H * a.B;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, MB>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<D, MB, NWV, S>), dim3((unsigned)grid), dim3(64 * NWV), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+  if (a.tokens_per_block > 2048 || a.tokens_per_block % (32 * decode_waves(a.D)) != 0) return hipErrorInvalidValue;
   if (a.D == 64) {
     switch (a.M) {
       case 32: return launch_dec_t<64, 1>(a, s);

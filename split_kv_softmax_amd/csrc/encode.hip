@@ -23,28 +23,60 @@ namespace flare {
 //   S^T[n][m] = K_tile Q_w^T      (A = K rows from LDS, B = Q from registers)
 //   online softmax over n          (the 32 scores of a row live in one lane
 //                                   pair, so the row max needs one exchange)
-//   O^T[d][m] += V_tile^T P^T      (A = V^T from LDS, B = P from registers)
+//   O^T[d][m] += V_tile^T P^T      (A = V^T via transposing LDS reads, B = P)
 // The result column of both products is the latent row, so the per-row
 // rescale and normalisation are lane-local.
+//
+// K and V tiles travel HBM -> LDS by direct (VGPR-free) loads into a ring of S
+// stages, so S-1 tiles are in flight while one is consumed; one barrier per
+// tile.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled by
+// row so that the operand reads of a wave spread over the LDS banks.
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a) {
-  constexpr int T = 64 * NW;
-  constexpr int TILE = 64;
-  constexpr int KS = D / 16;             // k-steps of the score product
-  constexpr int DB = D / 32;             // 32-row blocks of O^T
-  constexpr int KLD = D + 8;             // LDS row stride of K (elements)
-  constexpr int VLD = TILE + 8;          // LDS row stride of V^T (elements)
-  constexpr int KITEMS = TILE * D / 8;   // 16-byte pieces of a K tile
-  constexpr int VITEMS = (TILE / 2) * (D / 8);  // row pairs x 16-byte pieces of a V tile
-  constexpr int KI = (KITEMS + T - 1) / T;
-  constexpr int VI = (VITEMS + T - 1) / T;
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  const int s = swap23(r);
+  return D == 64 ? ((s >> 1) & 7) : (s & 15);
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[TILE * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VLD];
+template <int OPS, int S>
+__device__ __forceinline__ void wait_tiles(int later) {
+  // wait until at most `later` tiles' worth of this wave's loads are pending
+  if constexpr (S >= 4) {
+    if (later >= 2) { wait_vm<2 * OPS < 64 ? 2 * OPS : 63>(); return; }
+  }
+  if constexpr (S >= 3) {
+    if (later >= 1) { wait_vm<OPS < 64 ? OPS : 63>(); return; }
+  }
+  wait_vm<0>();
+}
+
+// Validity bits of the 64 tokens [t0, t0+64) of batch row `mw` (aligned words),
+// read through the constant address space so they become scalar loads.
+typedef __attribute__((address_space(4))) const uint64_t const_u64;
+__device__ __forceinline__ uint64_t mask_tile_bits(const_u64* mw, int t0) {
+  const int w = t0 >> 6, sh = t0 & 63;
+  const uint64_t lo = mw[w];
+  if (sh == 0) return lo;
+  return (lo >> sh) | (mw[w + 1] << (64 - sh));
+}
+
+template <int D, int NW, int S>
+__global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a) {
+  constexpr int TILE = 64;
+  constexpr int ROWB = 2 * D;              // bytes per row
+  constexpr int TB = TILE * ROWB;          // bytes of a K (or V) tile
+  constexpr int STAGE = 2 * TB;
+  constexpr int NI = TB / 1024;            // 1 KB direct loads per tile and tensor
+  constexpr int KS = D / 16;               // k-steps of the score product
+  constexpr int DB = D / 32;               // 32-row blocks of O^T
+  constexpr int OPS = 2 * NI / NW;         // loads this wave issues per tile
+  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  static_assert(OPS * (S - 2) < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int nch = a.tab.nchunks;
   int bid = blockIdx.x;
   const int c = bid % nch;
@@ -57,7 +89,7 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
   const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + bh * (int64_t)a.N * D;
   const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + (int64_t)b * a.q_bstride +
                        (int64_t)h * a.M * D;
-  const uint8_t* mk = a.mask ? a.mask + (int64_t)b * a.N : nullptr;
+  const_u64* mw = a.mask_words ? (const_u64*)(a.mask_words + (int64_t)b * a.mask_words_stride) : nullptr;
 
   // Q rows of this wave as the B operand: column j = latent row 32w + j.
   bf16x8_t qop[KS];
@@ -66,66 +98,33 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qop[ks] = __builtin_bit_cast(bf16x8_t, ld16(qrow + 16 * ks));
   }
+  // Complete the Q loads now: afterwards the only vector-memory operations
+  // in flight are the ring's, whose count the loop's waits rely on.
+  wait_vm<0>();
 
   const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
-
-  // validity of the 64 tokens of a tile as a wave-uniform bit mask
-  auto range_bits = [&](int t0) -> uint64_t {
+  auto tile_bits = [&](int u) -> uint64_t {
+    if (u >= ntiles) return 0ull;
+    const int t0 = t_begin + u * TILE;
     const int n = t_end - t0;
-    return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    uint64_t bits = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    if (mw) bits &= mask_tile_bits(mw, t0);
+    return bits;
   };
-  auto load_mask_byte = [&](int t0) -> int {
-    const int t = t0 + lane;
-    return (mk && t < t_end) ? (int)mk[t] : 1;
-  };
-  auto bits_from_byte = [&](int t0, int byte) -> uint64_t {
-    uint64_t rb = range_bits(t0);
-    if (!mk) return rb;
-    return rb & (uint64_t)__ballot(byte != 0);
-  };
-
-  u32x4_t kreg[KI];
-  u32x4_t vreg[VI][2];
-  auto issue_loads = [&](int t0, uint64_t bits) {
+  auto issue = [&](int u) {
+    const int t0 = t_begin + u * TILE;
+    const int nrows = t_end - t0;
+    const uint32_t kst = lds_addr(smem) + (u % S) * STAGE;
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int f = i * T + tid;
-      const int row = f / (D / 8), chk = f % (D / 8);
-      if (f < KITEMS && ((bits >> row) & 1ull))
-        kreg[i] = ld16(Kg + (int64_t)(t0 + row) * D + 8 * chk);
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int f = i * T + tid;
-      const int pr = f / (D / 8), chk = f % (D / 8);
-      if (f < VITEMS) {
-        if ((bits >> (2 * pr)) & 1ull) vreg[i][0] = ld16(Vg + (int64_t)(t0 + 2 * pr) * D + 8 * chk);
-        if ((bits >> (2 * pr + 1)) & 1ull) vreg[i][1] = ld16(Vg + (int64_t)(t0 + 2 * pr + 1) * D + 8 * chk);
-      }
-    }
-  };
-  auto store_lds = [&](uint64_t bits) {
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int f = i * T + tid;
-      const int row = f / (D / 8), chk = f % (D / 8);
-      if (f < KITEMS) st16(&Ks[row * KLD + 8 * chk], kreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int f = i * T + tid;
-      const int pr = f / (D / 8), chk = f % (D / 8);
-      if (f < VITEMS) {
-        // padding and out-of-chunk rows are zero so that P = 0 never meets NaN
-        const u32x4_t r0 = ((bits >> (2 * pr)) & 1ull) ? vreg[i][0] : u32x4_t{0, 0, 0, 0};
-        const u32x4_t r1 = ((bits >> (2 * pr + 1)) & 1ull) ? vreg[i][1] : u32x4_t{0, 0, 0, 0};
-        uint32_t* dst = reinterpret_cast<uint32_t*>(&Vt[(8 * chk) * VLD + 2 * pr]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dst[(2 * j) * (VLD / 2)] = __builtin_amdgcn_perm(r1[j], r0[j], 0x05040100u);
-          dst[(2 * j + 1) * (VLD / 2)] = __builtin_amdgcn_perm(r1[j], r0[j], 0x07060302u);
-        }
-      }
+    for (int j = 0; j < NI / NW; ++j) {
+      const int ii = wave + NW * j;
+      const int byte = ii * 1024 + lane * 16;
+      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+      const int ch = pc ^ kv_swz<D>(r);
+      const int rr = r < nrows ? r : 0;    // rows past the chunk re-read row 0 (in bounds, zeroed later)
+      const int64_t off = (int64_t)(t0 + rr) * D + 8 * ch;
+      dma16(Kg + off, kst + ii * 1024);
+      dma16(Vg + off, kst + TB + ii * 1024);
     }
   };
 
@@ -136,64 +135,84 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
   float l_run = 0.f;       // this lane half's share of the running sum
   const float c2 = a.scale_log2;
 
-  uint64_t bits_cur = 0;
-  int mbyte = 1;
-  if (ntiles > 0) {
-    bits_cur = bits_from_byte(t_begin, load_mask_byte(t_begin));
-    if (bits_cur) issue_loads(t_begin, bits_cur);
-    if (ntiles > 1) mbyte = load_mask_byte(t_begin + TILE);
+  // ring[k] = validity bits of tile t + k
+  uint64_t ring[S];
+#pragma unroll
+  for (int k = 0; k < S; ++k) ring[k] = 0ull;
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) {
+    ring[k] = tile_bits(k);
+    if (ring[k]) issue(k);
   }
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int t0 = t_begin + it * TILE;
-    __syncthreads();
-    if (bits_cur) store_lds(bits_cur);
-    __syncthreads();
-    uint64_t bits_next = 0;
-    if (it + 1 < ntiles) {
-      bits_next = bits_from_byte(t0 + TILE, mbyte);
-      if (bits_next) issue_loads(t0 + TILE, bits_next);
-      if (it + 2 < ntiles) mbyte = load_mask_byte(t0 + 2 * TILE);
-    }
-    if (bits_cur) {
+  // swizzle of the K rows this lane reads: row 32*b2 + swap23(l32) has
+  // swap23(row) = 32*b2 + l32, so it is the same for both blocks
+  const int swk = D == 64 ? ((l32 >> 1) & 7) : (l32 & 15);
+  for (int t = 0; t < ntiles; ++t) {
+    int later = 0;
+#pragma unroll
+    for (int k = 1; k < S - 1; ++k) later += ring[k] != 0ull;
+    wait_tiles<OPS, S>(later);
+    barrier_lds();
+    // every wave has finished tile t-1, so its stage may be refilled
+    ring[S - 1] = tile_bits(t + S - 1);
+    if (ring[S - 1]) issue(t + S - 1);
+    const uint64_t bits = ring[0];
+    if (bits) {
+      uint8_t* kst = smem + (t % S) * STAGE;
+      uint8_t* vst = kst + TB;
+      if (bits != ~0ull) {
+        // padding and rows past the chunk: zero their V rows so P = 0 never meets NaN
+        for (int f = tid; f < TILE * (ROWB / 16); f += 64 * NW) {
+          const int r = f / (ROWB / 16), pc = f % (ROWB / 16);
+          if (!((bits >> r) & 1ull)) st16(vst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
+        }
+        barrier_lds();
+      }
       // ---- scores S^T for the two 32-token blocks
-      f32x16_t s[2];
+      f32x16_t sc[2];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
-        s[b2] = f32x16_t{};
-        const uint16_t* krow = &Ks[(32 * b2 + swap23(l32)) * KLD + 8 * hh];
+        sc[b2] = f32x16_t{};
+        const uint8_t* krow = kst + (32 * b2 + swap23(l32)) * ROWB;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 16 * ks)),
-                               qop[ks], s[b2]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = (2 * ks + hh) ^ swk;
+          sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16)),
+                                qop[ks], sc[b2]);
+        }
       }
       // register r of lane half hh in block b2 holds token 32*b2 + 16*(r/8) + 8*hh + r%8
-      if (bits_cur != ~0ull) {
-        const uint64_t lb = bits_cur >> (8 * hh);
+      if (bits != ~0ull) {
+        const uint64_t lb = bits >> (8 * hh);
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int tk = 32 * b2 + 16 * (r >> 3) + (r & 7);
-            if (!((lb >> tk) & 1ull)) s[b2][r] = kNegInf;
+            if (!((lb >> tk) & 1ull)) sc[b2][r] = kNegInf;
           }
       }
-      float mx = s[0][0];
+      float mx = sc[0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float nmc = -m_use * c2;
-      if (__ballot(m_new != m_run)) {
-        const float alpha = fast_exp2(m_run * c2 + nmc);   // 0 when m_run = -inf
+      // Lazy reference: the subtracted maximum only moves when this tile's
+      // maximum exceeds it by more than 2^kLazy in the exponent; the constant
+      // cancels in O and L, and every weight stays below 2^kLazy.
+      constexpr float kLazy = 8.f;
+      const bool grow = m_run == kNegInf ? (mx != kNegInf) : ((mx - m_run) * c2 > kLazy);
+      if (__ballot(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = grow ? fast_exp2((m_run - m_new) * c2) : 1.f;   // 0 when m_run = -inf
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        m_run = m_new;
       }
-      m_run = m_new;
+      const float nmc = -((m_run == kNegInf) ? 0.f : m_run) * c2;
       bf16x8_t pk[4];
       float lsum = 0.f;
 #pragma unroll
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
           float p[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(__builtin_fmaf(s[b2][8 * g + j], c2, nmc));
+            p[j] = fast_exp2(__builtin_fmaf(sc[b2][8 * g + j], c2, nmc));
             lsum += p[j];
           }
           u32x4_t w;
@@ -214,17 +233,31 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
           pk[2 * b2 + g] = __builtin_bit_cast(bf16x8_t, w);
         }
       l_run += lsum;
-      // ---- O^T += V^T P^T ; k-step ks covers tokens 16ks .. 16ks+15
+      // ---- O^T += V^T P^T ; k-step ks covers tokens 16ks .. 16ks+15.
+      // Transposing reads: in each 16-lane group lane i points at token row
+      // (i/4) of a 4-token block and 4 head dims starting at 4*(i%4); it gets
+      // back the 4 tokens of head dim i of the group.
+      const int grp = lane >> 4, li = lane & 15;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* vrow = &Vt[(32 * db + l32) * VLD + 8 * hh];
+        const int d0 = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
+        const int chl = d0 >> 3, half = (d0 & 7) * 2;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vrow + 16 * ks)),
-                               pk[ks], o[db]);
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x2_t part[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int n = 16 * ks + 8 * (grp >> 1) + 4 * q + (li >> 2);
+            const uint8_t* src = vst + n * ROWB + ((chl ^ kv_swz<D>(n)) * 16) + half;
+            part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+          }
+          const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
+          o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pk[ks], o[db]);
+        }
       }
     }
-    bits_cur = bits_next;
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k) ring[k] = ring[k + 1];
   }
 
   // ---- normalise and store this chunk's state
@@ -254,42 +287,61 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
 }
 
 bool encode_mfma_supported(int M, int D) {
-  return (D == 64 || D == 128) && M % 32 == 0 && M >= 32 && M <= 256;
+  return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128 || M == 256);
 }
 
-template <int D, int NW>
+template <int D, int NW, int S>
 static hipError_t launch_mfma_t(const EncodeArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
-  hipLaunchKernelGGL((encode_mfma_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((encode_mfma_kernel<D, NW, S>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
-  const int NW = a.M / 32;
+  // LDS ring: D=64 stages are 16 KB, D=128 stages 32 KB
   if (a.D == 64) {
-    switch (NW) {
-      case 1: return launch_mfma_t<64, 1>(a, s);
-      case 2: return launch_mfma_t<64, 2>(a, s);
-      case 3: return launch_mfma_t<64, 3>(a, s);
-      case 4: return launch_mfma_t<64, 4>(a, s);
-      case 5: return launch_mfma_t<64, 5>(a, s);
-      case 6: return launch_mfma_t<64, 6>(a, s);
-      case 7: return launch_mfma_t<64, 7>(a, s);
-      case 8: return launch_mfma_t<64, 8>(a, s);
+    switch (a.M) {
+      case 32: return launch_mfma_t<64, 1, 4>(a, s);
+      case 64: return launch_mfma_t<64, 2, 4>(a, s);
+      case 128: return launch_mfma_t<64, 4, 4>(a, s);
+      case 256: return launch_mfma_t<64, 8, 4>(a, s);
     }
   } else if (a.D == 128) {
-    switch (NW) {
-      case 1: return launch_mfma_t<128, 1>(a, s);
-      case 2: return launch_mfma_t<128, 2>(a, s);
-      case 3: return launch_mfma_t<128, 3>(a, s);
-      case 4: return launch_mfma_t<128, 4>(a, s);
-      case 5: return launch_mfma_t<128, 5>(a, s);
-      case 6: return launch_mfma_t<128, 6>(a, s);
-      case 7: return launch_mfma_t<128, 7>(a, s);
-      case 8: return launch_mfma_t<128, 8>(a, s);
+    switch (a.M) {
+      case 32: return launch_mfma_t<128, 1, 3>(a, s);
+      case 64: return launch_mfma_t<128, 2, 3>(a, s);
+      case 128: return launch_mfma_t<128, 4, 4>(a, s);
+      case 256: return launch_mfma_t<128, 8, 4>(a, s);
     }
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Padding mask -> one 64-bit validity word per 64 tokens (bit i of word w of
+// batch b is mask[b][64w + i] != 0; tokens past N read as invalid), so that the
+// matrix-core encoder tests a whole tile with two scalar loads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mask_words_kernel(const uint8_t* __restrict__ mask, int B, int N,
+                                                          uint64_t* __restrict__ words, int64_t stride) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)B * stride) return;
+  const int b = (int)(idx / stride);
+  const int w = (int)(idx % stride);
+  const uint8_t* mr = mask + (int64_t)b * N;
+  uint64_t bits = 0;
+  for (int i = 0; i < 64; ++i) {
+    const int t = 64 * w + i;
+    if (t < N && mr[t] != 0) bits |= 1ull << i;
+  }
+  words[idx] = bits;
+}
+
+hipError_t launch_mask_words(const uint8_t* mask, int B, int N, uint64_t* words, int64_t stride, hipStream_t s) {
+  const int64_t n = (int64_t)B * stride;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mask_words_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, mask, B, N, words, stride);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -24,6 +24,8 @@ struct EncodeArgs {
   const void* K;
   const void* V;
   const uint8_t* mask;
+  const uint64_t* mask_words;   // [B, mask_words_stride] validity words (matrix-core path)
+  int64_t mask_words_stride;
   float* O_part;   // [R,B,H,M,D]
   float* L_part;   // [R,B,H,M]
   float* ws_O;     // [slots,B,H,M,D]
@@ -73,10 +75,12 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s);
 bool encode_q1_supported(int M, int D);
 hipError_t launch_encode_q1(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_encode_generic(const EncodeArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_mask_words(const uint8_t* mask, int B, int N, uint64_t* words, int64_t stride, hipStream_t s);
 
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 
 bool decode_mfma_supported(int M, int D);
+int decode_waves(int D);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s);
 

@@ -32,7 +32,7 @@ def lib():
     p64 = ctypes.POINTER(ctypes.c_int64)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     L.flare_encode.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp, sz, vp]
-    L.flare_encode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64]
+    L.flare_encode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64, i32]
     L.flare_encode_workspace_size.restype = sz
     L.lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp, vp]
     L.flare_decode.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp]
@@ -90,17 +90,18 @@ def test_shapes_pointers_and_scale_are_validated(lib):
 
 def test_workspace_contract(lib):
     o = offs(0, 40000, 80000)
-    n = lib.flare_encode_workspace_size(1, 1, 2, 80000, 128, 64, 2, o)
+    n = lib.flare_encode_workspace_size(1, 1, 2, 80000, 128, 64, 2, o, 0)
     assert n > 0                                       # long partitions are split into chunks
-    assert n == lib.flare_encode_workspace_size(1, 1, 2, 80000, 128, 64, 2, o)
+    assert n == lib.flare_encode_workspace_size(1, 1, 2, 80000, 128, 64, 2, o, 0)
+    assert lib.flare_encode_workspace_size(1, 1, 2, 80000, 128, 64, 2, o, 1) > n     # room for mask words
     assert lib.flare_encode(1, 1, 2, 80000, 128, 64, FAKE, 0, FAKE, FAKE, 2, o, None, 0.125, FAKE, FAKE, None, 0,
                             None) == EWS
     assert b"workspace" in lib.flare_last_error()
     assert lib.flare_encode(1, 1, 2, 80000, 128, 64, FAKE, 0, FAKE, FAKE, 2, o, None, 0.125, FAKE, FAKE, FAKE, n - 1,
                             None) == EWS
     # a small problem needs none, and invalid arguments report 0
-    assert lib.flare_encode_workspace_size(1, 1, 1, 1024, 64, 64, 1, offs(0, 1024)) == 0
-    assert lib.flare_encode_workspace_size(1, 1, 1, 1024, 64, 64, 2, offs(0, 900, 800)) == 0
+    assert lib.flare_encode_workspace_size(1, 1, 1, 1024, 64, 64, 1, offs(0, 1024), 0) == 0
+    assert lib.flare_encode_workspace_size(1, 1, 1, 1024, 64, 64, 2, offs(0, 900, 800), 0) == 0
 
 
 def test_backward_validates_offsets(lib):
