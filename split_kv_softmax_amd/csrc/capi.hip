@@ -98,12 +98,13 @@ int chunk_len_for(EncKind kind, int B, int H, int R, int M, int64_t max_part) {
   if (max_part <= 0) return 1;
   switch (kind) {
     case EncKind::Mfma: {
-      // Enough workgroups to keep every CU busy with a few resident groups,
+      // Enough workgroups for one full round of resident groups (three per
+      // CU on 256 CUs at head dim 64, where a 3-stage ring is 48 KB of LDS),
       // but long enough chunks that the partial states stay a few percent of
       // the K/V bytes (state bytes / K,V bytes = 2M / chunk_len).
       const int64_t base = (int64_t)B * H * R;
       int split = env_int("FLARE_ENCODE_SPLIT", 0);
-      if (split <= 0) split = (int)std::max<int64_t>(1, (512 + base - 1) / base);
+      if (split <= 0) split = (int)std::max<int64_t>(1, (768 + base - 1) / base);
       int len = round_up((int)((max_part + split - 1) / split), 64);
       const int min_len = std::max(1024, 32 * M);
       if (split > 1 && len < min_len) len = min_len;
@@ -355,11 +356,13 @@ flare_status flare_decode(flare_dtype dtype, int B, int H, int N, int M, int D, 
   if (dtype == FLARE_BF16 && decode_mfma_supported(M, D)) {
     if (!aligned16(Xq) || !aligned16(Klat) || !aligned16(Y) || (klat_batch_stride * 2) % 16 != 0)
       return fail(FLARE_EINVAL, "Xq, Klat, Y and the Klat batch stride must be 16-byte aligned");
-    // about a thousand workgroups, each at least one round of its waves
+    // One workgroup fills a CU (its LDS holds the staged latents and the
+    // waves' rings); aim for about two rounds of workgroups over the chip so
+    // the staging is amortised over thousands of tokens.
     const int round = 32 * decode_waves(D);
-    const int64_t per_slice = std::max<int64_t>(1, 1024 / std::max<int64_t>(1, (int64_t)B * H));
-    int tpb = (int)std::min<int64_t>(2048, (N + per_slice - 1) / per_slice);
-    tpb = std::min(2048, std::max(round, round_up(tpb, round)));
+    const int64_t per_slice = std::max<int64_t>(1, 512 / std::max<int64_t>(1, (int64_t)B * H));
+    int tpb = (int)std::min<int64_t>(8192, (N + per_slice - 1) / per_slice);
+    tpb = std::min(8192, std::max(round, round_up(tpb, round)));
     a.tokens_per_block = tpb;
     e = launch_decode_mfma(a, s);
   } else {

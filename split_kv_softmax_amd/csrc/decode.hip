@@ -49,8 +49,8 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
   constexpr int ROWB = 2 * D;
   constexpr int BB = BLK * ROWB;             // bytes per block
   constexpr int NI = BB / 1024;              // direct loads per block
-  constexpr int ST = DB * 4;                 // 8-byte stores per block and lane
-  constexpr int MAXT = 2048;                 // tokens per workgroup (host keeps tokens_per_block <= MAXT)
+  constexpr int ST = NI;                     // 1 KB row stores per block (as many as its loads)
+  constexpr int MAXT = 8192;                 // tokens per workgroup (host keeps tokens_per_block <= MAXT)
   __shared__ __attribute__((aligned(16))) uint16_t Kl[M * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Zt[D * ZLD];
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * S * BB];
@@ -68,19 +68,41 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
   const int n_lo = tb * a.tokens_per_block;
   const int n_hi = min(a.N, n_lo + a.tokens_per_block);
 
-  {  // stage latent keys (row-major), Z (transposed, rounded to bf16) and the token mask
+  {  // stage latent keys (row-major), Z (transposed, rounded to bf16) and the token mask;
+     // every load of a thread is issued before its first LDS store
+    constexpr int T = 64 * NWV;
+    constexpr int KI = (M * D / 8 + T - 1) / T;   // 16-byte pieces of Klat per thread
+    constexpr int ZI = (M * D / 4 + T - 1) / T;   // float4 pieces of Z per thread
     const uint16_t* kg = static_cast<const uint16_t*>(a.Klat) + (int64_t)b * a.klat_bstride + (int64_t)h * M * D;
-    for (int f = tid; f < M * D / 8; f += 64 * NWV) {
-      const int row = f / (D / 8), chk = f % (D / 8);
-      st16(&Kl[row * KLD + 8 * chk], ld16(kg + (int64_t)row * D + 8 * chk));
-    }
     const float* zg = a.Z + bh * (int64_t)M * D;
-    for (int f = tid; f < M * D; f += 64 * NWV) {
-      const int m = f / D, d = f % D;
-      Zt[d * ZLD + m] = to_bf16(zg[f]);
+    u32x4_t kv[KI];
+    f32x4_t zv[ZI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int f = tid + T * i;
+      if (f < M * D / 8) kv[i] = ld16(kg + 8 * (int64_t)f);
+    }
+#pragma unroll
+    for (int i = 0; i < ZI; ++i) {
+      const int f = tid + T * i;
+      if (f < M * D / 4) zv[i] = *reinterpret_cast<const f32x4_t*>(zg + 4 * (int64_t)f);
     }
     const uint8_t* tm = a.token_mask ? a.token_mask + (int64_t)b * a.N : nullptr;
-    for (int i = tid; i < n_hi - n_lo; i += 64 * NWV) tmask[i] = tm ? tm[n_lo + i] : (uint8_t)1;
+    for (int i = tid; i < n_hi - n_lo; i += T) tmask[i] = tm ? tm[n_lo + i] : (uint8_t)1;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int f = tid + T * i;
+      if (f < M * D / 8) st16(&Kl[(f / (D / 8)) * KLD + 8 * (f % (D / 8))], kv[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < ZI; ++i) {
+      const int f = tid + T * i;
+      if (f < M * D / 4) {
+        const int m = (4 * f) / D, d = (4 * f) % D;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Zt[(d + e) * ZLD + m] = to_bf16(zv[i][e]);
+      }
+    }
   }
   __syncthreads();   // also completes the staging loads before the ring starts
 
@@ -170,20 +192,32 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
         y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)),
                              pk[ks], y[db]);
     }
+    // Y block out through its own (consumed) ring stage: each lane writes its
+    // token's head dims as 8-byte pieces, then whole 128-byte rows leave with
+    // 16-byte stores.  Buffer stores drop the rows past the run, so every block
+    // issues the same ST stores (the ring's wait counts rely on that).
     const bool keep = inb && tmask[inb ? n - n_lo : 0] != 0;
     const float inv = 1.f / lsum;
-    if (inb) {
+    uint8_t* stg = myring + (j % S) * BB;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // select rather than branch: every block issues the same stores,
-          // which the ring's wait counts rely on
-          const uint32_t w0 = pack_bf16x2(y[db][4 * q] * inv, y[db][4 * q + 1] * inv);
-          const uint32_t w1 = pack_bf16x2(y[db][4 * q + 2] * inv, y[db][4 * q + 3] * inv);
-          const u32x2_t w = {keep ? w0 : 0u, keep ? w1 : 0u};
-          *reinterpret_cast<u32x2_t*>(Yg + (int64_t)n * D + 32 * db + 8 * q + 4 * hh) = w;
-        }
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w0 = pack_bf16x2(y[db][4 * q] * inv, y[db][4 * q + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(y[db][4 * q + 2] * inv, y[db][4 * q + 3] * inv);
+        const u32x2_t w = {keep ? w0 : 0u, keep ? w1 : 0u};
+        const int pc = (4 * db + q) ^ swx;
+        *reinterpret_cast<u32x2_t*>(stg + l32 * ROWB + pc * 16 + 8 * hh) = w;
+      }
+    const int valid_rows = min(BLK, n_hi - n0);
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(Yg + (int64_t)n0 * D, 0, valid_rows * ROWB, 0x00020000);
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int byte = ii * 1024 + lane * 16;
+      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + byte);
+      __builtin_amdgcn_raw_buffer_store_b128(v, yr, r * ROWB + ((pc ^ row_swz(D, r)) * 16), 0, 0);
     }
   }
 }
@@ -209,7 +243,7 @@ static hipError_t launch_dec_t(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
-  if (a.tokens_per_block > 2048 || a.tokens_per_block % (32 * decode_waves(a.D)) != 0) return hipErrorInvalidValue;
+  if (a.tokens_per_block > 8192 || a.tokens_per_block % (32 * decode_waves(a.D)) != 0) return hipErrorInvalidValue;
   if (a.D == 64) {
     switch (a.M) {
       case 32: return launch_dec_t<64, 1>(a, s);

@@ -11,6 +11,8 @@
 // exp(s (m - m')) (the online-softmax merge of "Ring vs. Tree Attention").
 // Exponentials are taken as exp2 of scores pre-multiplied by s log2(e); the
 // returned log-normaliser is natural: L = s m + ln l.
+#include <stdlib.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -297,14 +299,23 @@ static hipError_t launch_mfma_t(const EncodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+int encode_mfma_stages(int M, int D) {
+  // LDS ring: D=64 stages are 16 KB, D=128 stages 32 KB.  Three 16-KB stages
+  // let three workgroups share a CU when registers allow it.
+  const char* e = getenv("FLARE_ENCODE_STAGES");
+  if (D == 64 && e && (atoi(e) == 3 || atoi(e) == 4)) return atoi(e);
+  if (D == 64) return 3;
+  return (M >= 128) ? 4 : 3;
+}
+
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
-  // LDS ring: D=64 stages are 16 KB, D=128 stages 32 KB
   if (a.D == 64) {
+    const bool s3 = encode_mfma_stages(a.M, a.D) == 3;
     switch (a.M) {
-      case 32: return launch_mfma_t<64, 1, 4>(a, s);
-      case 64: return launch_mfma_t<64, 2, 4>(a, s);
-      case 128: return launch_mfma_t<64, 4, 4>(a, s);
-      case 256: return launch_mfma_t<64, 8, 4>(a, s);
+      case 32: return s3 ? launch_mfma_t<64, 1, 3>(a, s) : launch_mfma_t<64, 1, 4>(a, s);
+      case 64: return s3 ? launch_mfma_t<64, 2, 3>(a, s) : launch_mfma_t<64, 2, 4>(a, s);
+      case 128: return s3 ? launch_mfma_t<64, 4, 3>(a, s) : launch_mfma_t<64, 4, 4>(a, s);
+      case 256: return s3 ? launch_mfma_t<64, 8, 3>(a, s) : launch_mfma_t<64, 8, 4>(a, s);
     }
   } else if (a.D == 128) {
     switch (a.M) {

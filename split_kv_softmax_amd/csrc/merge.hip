@@ -13,6 +13,8 @@
 // every thread the branches are uniform and the level slots stay in
 // registers.  Leftover levels are merged from the lowest upwards, which is
 // exactly the round schedule above with its pass-through survivors.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -20,6 +22,7 @@ namespace flare {
 
 namespace {
 constexpr int kLevels = 16;   // up to 65536 states per group
+constexpr int kBatch = 8;     // leaves loaded together (all in flight at once)
 
 struct St {
   float m, l;
@@ -29,11 +32,7 @@ struct St {
 __device__ __forceinline__ St merge_st(const St& x, const St& y) {
   St r;
   r.m = fmaxf(x.m, y.m);
-  if (r.m == kNegInf) {
-    r.l = 0.f;
-    r.acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    return r;
-  }
+  if (r.m == kNegInf) return St{kNegInf, 0.f, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   const float fx = __expf(x.m - r.m);   // exactly 0 for an empty side
   const float fy = __expf(y.m - r.m);
   r.l = x.l * fx + y.l * fy;
@@ -42,71 +41,87 @@ __device__ __forceinline__ St merge_st(const St& x, const St& y) {
 }
 }  // namespace
 
+// Grid-stride over (group, row, 4-column piece); one piece per thread and step.
 __global__ __launch_bounds__(256) void fold_kernel(const FoldArgs a) {
-  const int g = blockIdx.y;
-  const int D4 = a.D / 4;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.rows * D4) return;
-  const int64_t row = idx / D4;
-  const int c4 = (int)(idx % D4);
-  const int s0 = a.tab.in_begin[g], s1 = a.tab.in_begin[g + 1];
+  const int D4 = a.D >> 2;
+  const int64_t per_group = a.rows * D4;
+  const int64_t total = per_group * a.tab.ngroups;
   const int64_t sstride = a.rows * a.D;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < total;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const int g = (int)(w / per_group);
+    const int64_t e = w - (int64_t)g * per_group;      // (row, piece) within the group
+    const int64_t row = e / D4;
+    const int64_t off = 4 * e;                          // = row * D + 4 * piece
+    const int s0 = a.tab.in_begin[g], s1 = a.tab.in_begin[g + 1];
+    const int n = s1 - s0;
 
-  St lv[kLevels];
-  St cur;
-  cur.m = kNegInf;
-  cur.l = 0.f;
-  cur.acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int n = s1 - s0;
-  for (int i = 0; i < n; ++i) {
-    const int64_t s = s0 + i;
-    St leaf;
-    leaf.m = a.in_L[s * a.rows + row];
-    leaf.l = (leaf.m == kNegInf) ? 0.f : 1.f;
-    leaf.acc = (leaf.m == kNegInf) ? f32x4_t{0.f, 0.f, 0.f, 0.f}
-                                   : *reinterpret_cast<const f32x4_t*>(a.in_O + s * sstride + row * a.D + 4 * c4);
-    // carry: merge the completed left subtrees of equal size into the new
-    // leaf; the first level whose bit is clear in i takes the result
-    bool carry = true;
+    St lv[kLevels];
+    for (int i0 = 0; i0 < n; i0 += kBatch) {
+      float Lb[kBatch];
+      f32x4_t Ob[kBatch];
 #pragma unroll
-    for (int k = 0; k < kLevels; ++k) {
-      if (carry) {
-        if ((i >> k) & 1) {
-          leaf = merge_st(lv[k], leaf);
-        } else {
-          lv[k] = leaf;
-          carry = false;
+      for (int k = 0; k < kBatch; ++k) {
+        const int64_t s = s0 + i0 + k;
+        const bool ok = i0 + k < n;
+        Lb[k] = ok ? a.in_L[s * a.rows + row] : kNegInf;
+        Ob[k] = ok ? *reinterpret_cast<const f32x4_t*>(a.in_O + s * sstride + off) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int i = i0 + k;
+        if (i < n) {
+          St leaf;
+          leaf.m = Lb[k];
+          leaf.l = (leaf.m == kNegInf) ? 0.f : 1.f;
+          leaf.acc = (leaf.m == kNegInf) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Ob[k];
+          // carry: merge the completed left subtrees of equal size into the
+          // new leaf; the first level whose bit is clear in i takes the result
+          bool carry = true;
+#pragma unroll
+          for (int lvl = 0; lvl < kLevels; ++lvl) {
+            if (carry) {
+              if ((i >> lvl) & 1) {
+                leaf = merge_st(lv[lvl], leaf);
+              } else {
+                lv[lvl] = leaf;
+                carry = false;
+              }
+            }
+          }
         }
       }
     }
-  }
-  // collect the levels still occupied (bits of n), lowest first
-  bool have = false;
+    // collect the levels still occupied (bits of n), lowest first
+    St cur{kNegInf, 0.f, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    bool have = false;
 #pragma unroll
-  for (int k = 0; k < kLevels; ++k) {
-    if ((n >> k) & 1) {
-      cur = have ? merge_st(lv[k], cur) : lv[k];
-      have = true;
+    for (int lvl = 0; lvl < kLevels; ++lvl) {
+      if ((n >> lvl) & 1) {
+        cur = have ? merge_st(lv[lvl], cur) : lv[lvl];
+        have = true;
+      }
     }
-  }
-  const int oi = a.tab.out_index[g];
-  const bool empty = !(cur.l > 0.f);
-  const float inv = empty ? 0.f : 1.f / cur.l;
-  f32x4_t z = cur.acc * inv;
-  if (empty) z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  *reinterpret_cast<f32x4_t*>(a.out_O + (int64_t)oi * sstride + row * a.D + 4 * c4) = z;
-  if (c4 == 0) a.out_L[(int64_t)oi * a.rows + row] = empty ? kNegInf : cur.m + __logf(cur.l);
-  if (a.out_bf16) {
-    u32x2_t w = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
-    *reinterpret_cast<u32x2_t*>(a.out_bf16 + (int64_t)oi * sstride + row * a.D + 4 * c4) = w;
+    const int oi = a.tab.out_index[g];
+    const bool empty = !(cur.l > 0.f);
+    const float inv = empty ? 0.f : 1.f / cur.l;
+    f32x4_t z = cur.acc * inv;
+    if (empty) z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4_t*>(a.out_O + (int64_t)oi * sstride + off) = z;
+    if (off % a.D == 0) a.out_L[(int64_t)oi * a.rows + row] = empty ? kNegInf : cur.m + __logf(cur.l);
+    if (a.out_bf16) {
+      const u32x2_t wv = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+      *reinterpret_cast<u32x2_t*>(a.out_bf16 + (int64_t)oi * sstride + off) = wv;
+    }
   }
 }
 
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s) {
-  const int64_t n = a.rows * (a.D / 4);
-  const int64_t blocks = (n + 255) / 256;
-  if (blocks == 0 || a.tab.ngroups == 0) return hipSuccess;
-  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)blocks, (unsigned)a.tab.ngroups), dim3(256), 0, s, a);
+  const int64_t total = a.rows * (a.D / 4) * a.tab.ngroups;
+  if (total == 0) return hipSuccess;
+  // a few workgroups per CU; each thread walks the pieces grid-stride
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 2048);
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
