@@ -62,8 +62,8 @@ __device__ __forceinline__ uint64_t mask_tile_bits(const_u64* mw, int t0) {
   return (lo >> sh) | (mw[w + 1] << (64 - sh));
 }
 
-template <int D, int NW, int S>
-__global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a) {
+template <int D, int NW, int S, int G>
+__global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeArgs a) {
   constexpr int TILE = 64;
   constexpr int ROWB = 2 * D;              // bytes per row
   constexpr int TB = TILE * ROWB;          // bytes of a K (or V) tile
@@ -74,11 +74,17 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
   constexpr int OPS = 2 * NI / NW;         // loads this wave issues per tile
   static_assert(NI % NW == 0, "loads must split evenly over the waves");
   static_assert(OPS * (S - 2) < 64, "vmcnt range");
+  // G token groups of NW waves each: group g takes tiles g, g+G, g+2G, ...
+  // of the chunk into its own LDS ring; their states are combined at the end.
+  static_assert(G == 1 || (G * NW * 32 * 64 + 2 * G * NW * 64) * 4 <= G * S * STAGE,
+                "the combine buffer reuses the rings");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[G * S * STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv / NW, wave = wv % NW;                 // token group, row wave
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int nch = a.tab.nchunks;
   int bid = blockIdx.x;
   const int c = bid % nch;
@@ -105,18 +111,22 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
   wait_vm<0>();
 
   const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
-  auto tile_bits = [&](int u) -> uint64_t {
-    if (u >= ntiles) return 0ull;
-    const int t0 = t_begin + u * TILE;
+  const int nrounds = (ntiles + G - 1) / G;
+  // validity bits of local tile u of group g (tile g + G*u of the chunk)
+  auto tile_bits = [&](int g, int u) -> uint64_t {
+    const int tt = g + G * u;
+    if (tt >= ntiles) return 0ull;
+    const int t0 = t_begin + tt * TILE;
     const int n = t_end - t0;
     uint64_t bits = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
     if (mw) bits &= mask_tile_bits(mw, t0);
     return bits;
   };
+  uint8_t* myring = smem + grp * (S * STAGE);
   auto issue = [&](int u) {
-    const int t0 = t_begin + u * TILE;
+    const int t0 = t_begin + (grp + G * u) * TILE;
     const int nrows = t_end - t0;
-    const uint32_t kst = lds_addr(smem) + (u % S) * STAGE;
+    const uint32_t kst = lds_addr(myring) + (u % S) * STAGE;
 #pragma unroll
     for (int j = 0; j < NI / NW; ++j) {
       const int ii = wave + NW * j;
@@ -133,44 +143,52 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
   f32x16_t o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16_t{};
-  float m_run = kNegInf;   // running max of raw dot products of row 32w + l32
+  float m_run = kNegInf;   // reference maximum (raw dot products) of row 32w + l32
   float l_run = 0.f;       // this lane half's share of the running sum
   const float c2 = a.scale_log2;
 
-  // ring[k] = validity bits of tile t + k
+  // ring[k] = validity bits of this group's local tile u + k
   uint64_t ring[S];
 #pragma unroll
   for (int k = 0; k < S; ++k) ring[k] = 0ull;
 #pragma unroll
   for (int k = 0; k < S - 1; ++k) {
-    ring[k] = tile_bits(k);
+    ring[k] = tile_bits(grp, k);
     if (ring[k]) issue(k);
   }
 
   // swizzle of the K rows this lane reads: row 32*b2 + swap23(l32) has
   // swap23(row) = 32*b2 + l32, so it is the same for both blocks
   const int swk = D == 64 ? ((l32 >> 1) & 7) : (l32 & 15);
-  for (int t = 0; t < ntiles; ++t) {
+  for (int u = 0; u < nrounds; ++u) {
     int later = 0;
 #pragma unroll
     for (int k = 1; k < S - 1; ++k) later += ring[k] != 0ull;
     wait_tiles<OPS, S>(later);
     barrier_lds();
-    // every wave has finished tile t-1, so its stage may be refilled
-    ring[S - 1] = tile_bits(t + S - 1);
-    if (ring[S - 1]) issue(t + S - 1);
+    // every wave has finished round u-1, so its stages may be refilled
+    ring[S - 1] = tile_bits(grp, u + S - 1);
+    if (ring[S - 1]) issue(u + S - 1);
     const uint64_t bits = ring[0];
-    if (bits) {
-      uint8_t* kst = smem + (t % S) * STAGE;
-      uint8_t* vst = kst + TB;
-      if (bits != ~0ull) {
-        // padding and rows past the chunk: zero their V rows so P = 0 never meets NaN
-        for (int f = tid; f < TILE * (ROWB / 16); f += 64 * NW) {
+    bool partial = false;     // is any group's tile of this round partially valid?
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint64_t bg = g == grp ? bits : tile_bits(g, u);
+      partial |= (bg != 0ull && bg != ~0ull);
+    }
+    uint8_t* kst = myring + (u % S) * STAGE;
+    uint8_t* vst = kst + TB;
+    if (partial) {
+      // padding and rows past the chunk: zero their V rows so P = 0 never meets NaN
+      if (bits != ~0ull && bits != 0ull) {
+        for (int f = tid - grp * 64 * NW; f < TILE * (ROWB / 16); f += 64 * NW) {
           const int r = f / (ROWB / 16), pc = f % (ROWB / 16);
           if (!((bits >> r) & 1ull)) st16(vst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
         }
-        barrier_lds();
       }
+      barrier_lds();
+    }
+    if (bits) {
       // ---- scores S^T for the two 32-token blocks
       f32x16_t sc[2];
 #pragma unroll
@@ -239,17 +257,17 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
       // Transposing reads: in each 16-lane group lane i points at token row
       // (i/4) of a 4-token block and 4 head dims starting at 4*(i%4); it gets
       // back the 4 tokens of head dim i of the group.
-      const int grp = lane >> 4, li = lane & 15;
+      const int lg = lane >> 4, li = lane & 15;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d0 = 32 * db + 16 * (grp & 1) + 4 * (li & 3);
+        const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
         const int chl = d0 >> 3, half = (d0 & 7) * 2;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           u32x2_t part[2];
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const int n = 16 * ks + 8 * (grp >> 1) + 4 * q + (li >> 2);
+            const int n = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
             const uint8_t* src = vst + n * ROWB + ((chl ^ kv_swz<D>(n)) * 16) + half;
             part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
           }
@@ -262,8 +280,45 @@ __global__ __launch_bounds__(64 * NW) void encode_mfma_kernel(const EncodeArgs a
     for (int k = 0; k < S - 1; ++k) ring[k] = ring[k + 1];
   }
 
+  float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if constexpr (G > 1) {
+    // ---- combine the G groups' states in LDS (the rings are idle now):
+    // group g's lane writes its reference max, row sum and unnormalised
+    // accumulators; group 0 merges them in group order.
+    barrier_lds();
+    float* cb = reinterpret_cast<float*>(smem);
+    float* cm = cb + G * NW * 32 * 64;
+    float* cl = cm + G * NW * 64;
+    const int slot = grp * NW + wave;
+    if (grp > 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cb[(slot * 32 + 16 * db + r) * 64 + lane] = o[db][r];
+      cm[slot * 64 + lane] = m_run;
+      cl[slot * 64 + lane] = l_tot;
+    }
+    barrier_lds();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < G; ++g) {
+      const int sg = g * NW + wave;
+      const float mg = cm[sg * 64 + lane];
+      const float lg2 = cl[sg * 64 + lane];
+      const float mn = fmaxf(m_run, mg);
+      if (mn == kNegInf) continue;                       // both empty
+      const float fa = fast_exp2((m_run - mn) * c2);     // 0 for an empty side
+      const float fb = fast_exp2((mg - mn) * c2);
+      l_tot = l_tot * fa + lg2 * fb;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * fa + cb[(sg * 32 + 16 * db + r) * 64 + lane] * fb;
+      m_run = mn;
+    }
+  }
+
   // ---- normalise and store this chunk's state
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : 1.f / l_tot;
   const int slot = a.tab.slot[c];
@@ -292,37 +347,57 @@ bool encode_mfma_supported(int M, int D) {
   return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128 || M == 256);
 }
 
-template <int D, int NW, int S>
+template <int D, int NW, int S, int G>
 static hipError_t launch_mfma_t(const EncodeArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
-  hipLaunchKernelGGL((encode_mfma_kernel<D, NW, S>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((encode_mfma_kernel<D, NW, S, G>), dim3((unsigned)grid), dim3(64 * NW * G), 0, s, a);
   return hipGetLastError();
+}
+
+int encode_mfma_groups(int M, int D) {
+  // Token groups per workgroup: at head dim 64 and 128 latent rows three
+  // 4-wave groups (12 waves, three 48-KB rings) fill a CU as one workgroup,
+  // so a partition needs no split and no fold.
+  const char* e = getenv("FLARE_ENCODE_GROUPS");
+  if (e && atoi(e) >= 1 && atoi(e) <= 3 && D == 64 && M == 128) return atoi(e);
+  return (D == 64 && M == 128) ? 3 : 1;
 }
 
 int encode_mfma_stages(int M, int D) {
   // LDS ring: D=64 stages are 16 KB, D=128 stages 32 KB.  Three 16-KB stages
-  // let three workgroups share a CU when registers allow it.
+  // let three 4-wave groups (or workgroups) share a CU when registers allow.
   const char* e = getenv("FLARE_ENCODE_STAGES");
-  if (D == 64 && e && (atoi(e) == 3 || atoi(e) == 4)) return atoi(e);
+  if (D == 64 && e && (atoi(e) == 3 || atoi(e) == 4) && encode_mfma_groups(M, D) == 1) return atoi(e);
   if (D == 64) return 3;
   return (M >= 128) ? 4 : 3;
+}
+
+int encode_mfma_per_cu(int M, int D) {
+  // workgroups of the chosen variant that fit on one CU (LDS and registers)
+  if (D == 64) return encode_mfma_groups(M, D) > 1 ? 1 : 3;
+  return M >= 128 ? 1 : 2;
 }
 
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
   if (a.D == 64) {
     const bool s3 = encode_mfma_stages(a.M, a.D) == 3;
     switch (a.M) {
-      case 32: return s3 ? launch_mfma_t<64, 1, 3>(a, s) : launch_mfma_t<64, 1, 4>(a, s);
-      case 64: return s3 ? launch_mfma_t<64, 2, 3>(a, s) : launch_mfma_t<64, 2, 4>(a, s);
-      case 128: return s3 ? launch_mfma_t<64, 4, 3>(a, s) : launch_mfma_t<64, 4, 4>(a, s);
-      case 256: return s3 ? launch_mfma_t<64, 8, 3>(a, s) : launch_mfma_t<64, 8, 4>(a, s);
+      case 32: return s3 ? launch_mfma_t<64, 1, 3, 1>(a, s) : launch_mfma_t<64, 1, 4, 1>(a, s);
+      case 64: return s3 ? launch_mfma_t<64, 2, 3, 1>(a, s) : launch_mfma_t<64, 2, 4, 1>(a, s);
+      case 128:
+        switch (encode_mfma_groups(a.M, a.D)) {
+          case 3: return launch_mfma_t<64, 4, 3, 3>(a, s);
+          case 2: return launch_mfma_t<64, 4, 3, 2>(a, s);
+          default: return s3 ? launch_mfma_t<64, 4, 3, 1>(a, s) : launch_mfma_t<64, 4, 4, 1>(a, s);
+        }
+      case 256: return s3 ? launch_mfma_t<64, 8, 3, 1>(a, s) : launch_mfma_t<64, 8, 4, 1>(a, s);
     }
   } else if (a.D == 128) {
     switch (a.M) {
-      case 32: return launch_mfma_t<128, 1, 3>(a, s);
-      case 64: return launch_mfma_t<128, 2, 3>(a, s);
-      case 128: return launch_mfma_t<128, 4, 4>(a, s);
-      case 256: return launch_mfma_t<128, 8, 4>(a, s);
+      case 32: return launch_mfma_t<128, 1, 3, 1>(a, s);
+      case 64: return launch_mfma_t<128, 2, 3, 1>(a, s);
+      case 128: return launch_mfma_t<128, 4, 4, 1>(a, s);
+      case 256: return launch_mfma_t<128, 8, 4, 1>(a, s);
     }
   }
   return hipErrorInvalidValue;

@@ -71,6 +71,7 @@ struct DecodeArgs {
 
 // Encoder kernels. Return hipSuccess or the launch error.
 bool encode_mfma_supported(int M, int D);
+int encode_mfma_per_cu(int M, int D);   // resident workgroups per CU of the chosen variant
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s);
 bool encode_q1_supported(int M, int D);
 hipError_t launch_encode_q1(const EncodeArgs& a, hipStream_t s);
