@@ -374,8 +374,13 @@ flare_status flare_decode(flare_dtype dtype, int B, int H, int N, int M, int D, 
 
 size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D, int R,
                                        const int64_t* offsets) {
-  (void)dtype; (void)B; (void)H; (void)N; (void)M; (void)D; (void)R; (void)offsets;
-  return 0;
+  const std::string saved = g_err;
+  if (check_common(dtype, B, H, N, M, D) != FLARE_OK || check_offsets(N, R, offsets) != FLARE_OK) {
+    g_err = saved;
+    return 0;
+  }
+  // the row term c = rowsum(dZ * Z)
+  return align256((size_t)B * H * M * sizeof(float));
 }
 
 flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
@@ -383,13 +388,47 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
                               const int64_t* offsets, const uint8_t* mask, float scale, const float* Z,
                               const float* L, const void* dZ, float* dQ, void* dK, void* dV, void* workspace,
                               size_t workspace_bytes, flare_stream_t stream) {
-  (void)Q; (void)q_batch_stride; (void)K; (void)V; (void)mask; (void)scale; (void)Z; (void)L; (void)dZ;
-  (void)dQ; (void)dK; (void)dV; (void)workspace; (void)workspace_bytes; (void)stream;
   flare_status st = check_common(dtype, B, H, N, M, D);
   if (st != FLARE_OK) return st;
   st = check_offsets(N, R, offsets);
   if (st != FLARE_OK) return st;
-  return fail(FLARE_EUNSUPPORTED, "encoder backward not built yet");
+  if (!std::isfinite(scale)) return fail(FLARE_EINVAL, "scale must be finite");
+  if (q_batch_stride < 0) return fail(FLARE_EINVAL, "q_batch_stride must be >= 0");
+  if ((int64_t)B * H == 0) return FLARE_OK;
+  if ((int64_t)M > 0 && (!Q || !Z || !L || !dZ || !dQ)) return fail(FLARE_EINVAL, "NULL pointer argument");
+  if (N > 0 && (!K || !V || !dK || !dV)) return fail(FLARE_EINVAL, "NULL pointer argument");
+  const size_t need = flare_encode_bwd_workspace_size(dtype, B, H, N, M, D, R, offsets);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FLARE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.mask = mask;
+  a.Z = Z;
+  a.L = L;
+  a.dZ = dZ;
+  a.c = static_cast<float*>(workspace);
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.q_bstride = q_batch_stride;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.M = M;
+  a.D = D;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const bool bf16 = dtype == FLARE_BF16;
+  hipError_t e = launch_bwd_rowdot(dZ, bf16, Z, (int64_t)B * H * M, D, static_cast<float*>(workspace), s);
+  if (e != hipSuccess) return hip_fail(e, "backward row-term launch");
+  e = launch_bwd_generic(a, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return FLARE_OK;
 }
 
 }  // extern "C"

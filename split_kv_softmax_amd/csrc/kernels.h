@@ -69,6 +69,28 @@ struct DecodeArgs {
   int tokens_per_block;   // tokens handled by one workgroup
 };
 
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const uint8_t* mask;
+  const uint64_t* mask_words;   // validity words (matrix-core path)
+  int64_t mask_words_stride;
+  const float* Z;
+  const float* L;
+  const void* dZ;
+  const float* c;               // [B,H,M] rowsum(dZ * Z)
+  float* dQ;                    // [B,H,M,D]
+  void* dK;                     // [B,H,N,D]
+  void* dV;
+  float* ws_dq;                 // [chunks,B,H,M,D] partial query gradients (matrix-core path)
+  int64_t q_bstride;
+  int B, H, N, M, D;
+  float scale;
+  float scale_log2;
+  ChunkTable tab;               // token chunks (matrix-core path)
+};
+
 // Encoder kernels. Return hipSuccess or the launch error.
 bool encode_mfma_supported(int M, int D);
 int encode_mfma_per_cu(int M, int D);   // resident workgroups per CU of the chosen variant
@@ -79,6 +101,10 @@ hipError_t launch_encode_generic(const EncodeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_mask_words(const uint8_t* mask, int B, int N, uint64_t* words, int64_t stride, hipStream_t s);
 
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
+
+hipError_t launch_bwd_rowdot(const void* dZ, bool bf16, const float* Z, int64_t rows, int D, float* c,
+                             hipStream_t s);
+hipError_t launch_bwd_generic(const BwdArgs& a, bool bf16, hipStream_t s);
 
 bool decode_mfma_supported(int M, int D);
 int decode_waves(int D);
