@@ -129,9 +129,11 @@ flare_status flare_decode(flare_dtype dtype, int B, int H, int N, int M, int D,
                           const float* Z, const uint8_t* token_mask, float scale, void* Y,
                           flare_stream_t stream);
 
-/* Bytes of device workspace flare_encode_bwd needs (0 if none). */
+/* Bytes of device workspace flare_encode_bwd needs (never 0 for valid
+ * arguments: it always holds the per-row term c); masked != 0 when a padding
+ * mask will be passed. */
 size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D,
-                                       int R, const int64_t* offsets);
+                                       int R, const int64_t* offsets, int masked);
 
 /*
  * flare_encode_bwd -- the encoder backward of [FLARE++] (backward paragraph):

@@ -63,7 +63,7 @@ def _load():
     lib.lse_merge.restype = i32
     lib.flare_decode.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp]
     lib.flare_decode.restype = i32
-    lib.flare_encode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64]
+    lib.flare_encode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64, i32]
     lib.flare_encode_bwd_workspace_size.restype = sz
     lib.flare_encode_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp,
                                      vp, vp, vp, vp, vp, vp, sz, vp]
@@ -265,10 +265,10 @@ def decode(Xq: torch.Tensor, Klat: torch.Tensor, Z: torch.Tensor, scale: Optiona
     return Y
 
 
-def encode_bwd_workspace_size(dtype: torch.dtype, B, H, N, M, D, offsets) -> int:
+def encode_bwd_workspace_size(dtype: torch.dtype, B, H, N, M, D, offsets, masked: bool = False) -> int:
     code = BF16 if dtype == torch.bfloat16 else F32
     return int(_load().flare_encode_bwd_workspace_size(code, B, H, N, M, D, len(offsets) - 1,
-                                                       _offsets(offsets)))
+                                                       _offsets(offsets), int(masked)))
 
 
 def encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dQ=None, dK=None, dV=None):
@@ -299,7 +299,7 @@ def encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dQ=None, dK=None, dV=Non
         raise ValueError("dK / dV must match K / V")
     offs = _offsets(offsets)
     code = _dtype_code(K)
-    nbytes = int(lib.flare_encode_bwd_workspace_size(code, B, H, N, M, D, R, offs))
+    nbytes = int(lib.flare_encode_bwd_workspace_size(code, B, H, N, M, D, R, offs, int(mask is not None)))
     ws = _workspace(nbytes, dev)
     with torch.cuda.device(dev):
         _check(lib.flare_encode_bwd(code, B, H, N, M, D, _ptr(Q), qbs, _ptr(K), _ptr(V), R, offs, _ptr(mask),

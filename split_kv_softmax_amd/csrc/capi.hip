@@ -372,15 +372,52 @@ flare_status flare_decode(flare_dtype dtype, int B, int H, int N, int M, int D, 
   return FLARE_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// Backward plan: the row term c, the mask's validity words and one slot of
+// partial query gradients per token chunk (matrix-core path).
+struct BwdPlan {
+  bool mfma = false;
+  std::vector<int32_t> bnd;   // chunk boundaries over [0, N)
+  size_t c_bytes = 0, mw_bytes = 0, dq_bytes = 0, ws_bytes = 0;
+  int64_t mw_stride = 0;
+};
+
+BwdPlan plan_bwd(flare_dtype dt, int B, int H, int N, int M, int D, bool masked) {
+  BwdPlan p;
+  p.mfma = dt == FLARE_BF16 && bwd_mfma_supported(M, D) && N > 0;
+  p.c_bytes = align256((size_t)B * H * M * sizeof(float));
+  if (p.mfma) {
+    // about one workgroup per CU for the query-gradient kernel, chunks of whole tiles
+    const int64_t bh = std::max<int64_t>(1, (int64_t)B * H);
+    int64_t per = std::max<int64_t>(1, (256 + bh - 1) / bh);
+    int64_t len = ((N + per - 1) / per + 63) / 64 * 64;
+    len = std::max<int64_t>(len, 1024);
+    for (int64_t t = 0; t < N; t += len) p.bnd.push_back((int32_t)t);
+    p.bnd.push_back(N);
+    const int nslots = (int)p.bnd.size() - 1;
+    p.dq_bytes = align256((size_t)nslots * B * H * M * D * sizeof(float));
+    if (masked) {
+      p.mw_stride = (N + 63) / 64 + 1;
+      p.mw_bytes = align256((size_t)B * p.mw_stride * sizeof(uint64_t));
+    }
+  }
+  p.ws_bytes = p.c_bytes + p.mw_bytes + p.dq_bytes;
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
 size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D, int R,
-                                       const int64_t* offsets) {
+                                       const int64_t* offsets, int masked) {
   const std::string saved = g_err;
   if (check_common(dtype, B, H, N, M, D) != FLARE_OK || check_offsets(N, R, offsets) != FLARE_OK) {
     g_err = saved;
     return 0;
   }
-  // the row term c = rowsum(dZ * Z)
-  return align256((size_t)B * H * M * sizeof(float));
+  return plan_bwd(dtype, B, H, N, M, D, masked != 0).ws_bytes;
 }
 
 flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
@@ -397,11 +434,19 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   if ((int64_t)B * H == 0) return FLARE_OK;
   if ((int64_t)M > 0 && (!Q || !Z || !L || !dZ || !dQ)) return fail(FLARE_EINVAL, "NULL pointer argument");
   if (N > 0 && (!K || !V || !dK || !dV)) return fail(FLARE_EINVAL, "NULL pointer argument");
-  const size_t need = flare_encode_bwd_workspace_size(dtype, B, H, N, M, D, R, offsets);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(FLARE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+  const BwdPlan plan = plan_bwd(dtype, B, H, N, M, D, mask != nullptr);
+  if ((int)plan.bnd.size() - 1 > kMaxChunks) return fail(FLARE_EUNSUPPORTED, "too many backward chunks");
+  if (!workspace || workspace_bytes < plan.ws_bytes)
+    return fail(FLARE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
                 workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(FLARE_EINVAL, "workspace must be 16-byte aligned");
+  if (plan.mfma) {
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dZ) || !aligned16(dQ) ||
+        (q_batch_stride * 2) % 16 != 0)
+      return fail(FLARE_EINVAL, "Q, K, V, dZ, dQ and the Q batch stride must be 16-byte aligned");
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
   BwdArgs a;
   memset(&a, 0, sizeof(a));
   a.Q = Q;
@@ -411,7 +456,7 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   a.Z = Z;
   a.L = L;
   a.dZ = dZ;
-  a.c = static_cast<float*>(workspace);
+  a.c = reinterpret_cast<float*>(ws);
   a.dQ = dQ;
   a.dK = dK;
   a.dV = dV;
@@ -424,10 +469,30 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   const bool bf16 = dtype == FLARE_BF16;
-  hipError_t e = launch_bwd_rowdot(dZ, bf16, Z, (int64_t)B * H * M, D, static_cast<float*>(workspace), s);
+  hipError_t e = launch_bwd_rowdot(dZ, bf16, Z, (int64_t)B * H * M, D, reinterpret_cast<float*>(ws), s);
   if (e != hipSuccess) return hip_fail(e, "backward row-term launch");
-  e = launch_bwd_generic(a, bf16, s);
-  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  if (!plan.mfma) {
+    e = launch_bwd_generic(a, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return FLARE_OK;
+  }
+  if (plan.mw_bytes) {
+    a.mask_words = reinterpret_cast<const uint64_t*>(ws + plan.c_bytes);
+    a.mask_words_stride = plan.mw_stride;
+    e = launch_mask_words(mask, B, N, reinterpret_cast<uint64_t*>(ws + plan.c_bytes), plan.mw_stride, s);
+    if (e != hipSuccess) return hip_fail(e, "mask launch");
+  }
+  a.ws_dq = reinterpret_cast<float*>(ws + plan.c_bytes + plan.mw_bytes);
+  const int nc = (int)plan.bnd.size() - 1;
+  a.tab.nchunks = nc;
+  for (int i = 0; i <= nc; ++i) a.tab.bnd[i] = plan.bnd[i];
+  for (int i = 0; i < nc; ++i) a.tab.slot[i] = (int16_t)i;
+  e = launch_bwd_dq_mfma(a, s);
+  if (e != hipSuccess) return hip_fail(e, "query-gradient launch");
+  e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, scale, dQ, s);
+  if (e != hipSuccess) return hip_fail(e, "query-gradient reduce launch");
+  e = launch_bwd_kv_generic(a, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
   return FLARE_OK;
 }
 

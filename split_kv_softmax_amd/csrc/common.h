@@ -111,4 +111,33 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// ---- K/V tile rings (encoder and backward)
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  const int s = swap23(r);
+  return D == 64 ? ((s >> 1) & 7) : (s & 15);
+}
+
+template <int OPS, int S>
+__device__ __forceinline__ void wait_tiles(int later) {
+  // wait until at most `later` tiles' worth of this wave's loads are pending
+  if constexpr (S >= 4) {
+    if (later >= 2) { wait_vm<2 * OPS < 64 ? 2 * OPS : 63>(); return; }
+  }
+  if constexpr (S >= 3) {
+    if (later >= 1) { wait_vm<OPS < 64 ? OPS : 63>(); return; }
+  }
+  wait_vm<0>();
+}
+
+// Validity bits of the 64 tokens [t0, t0+64) of batch row `mw` (aligned words),
+// read through the constant address space so they become scalar loads.
+typedef __attribute__((address_space(4))) const uint64_t const_u64;
+__device__ __forceinline__ uint64_t mask_tile_bits(const_u64* mw, int t0) {
+  const int w = t0 >> 6, sh = t0 & 63;
+  const uint64_t lo = mw[w];
+  if (sh == 0) return lo;
+  return (lo >> sh) | (mw[w + 1] << (64 - sh));
+}
+
 }  // namespace flare

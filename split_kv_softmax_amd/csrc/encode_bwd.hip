@@ -154,6 +154,246 @@ __global__ __launch_bounds__(256) void bwd_q_generic_kernel(const BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core query gradient.  Same shape as the encoder: one workgroup per
+// (batch, head, token chunk), wave w owns latent rows [32w, 32w+32), K and V
+// tiles arrive through a direct-load LDS ring.  Per 64-token tile:
+//   S^T  = K Q^T,  dP^T = V dZ^T                 (A = K / V rows, B = Q / dZ)
+//   dS^T = P (dP - c) with P = exp(s S - L)       (L, c per lane: lane = row)
+//   dQ^T += K^T dS^T                               (A = K^T by transposing reads)
+// The chunk's unscaled sum goes to its workspace slot; bwd_dq_reduce adds the
+// chunks in order and applies s.
+// ---------------------------------------------------------------------------
+template <int D, int NW, int S>
+__global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
+  constexpr int TILE = 64;
+  constexpr int ROWB = 2 * D;
+  constexpr int TB = TILE * ROWB;
+  constexpr int STAGE = 2 * TB;
+  constexpr int NI = TB / 1024;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int OPS = 2 * NI / NW;
+  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  static_assert(OPS * (S - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int nch = a.tab.nchunks;
+  int bid = blockIdx.x;
+  const int c = bid % nch;
+  bid /= nch;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int t_begin = a.tab.bnd[c], t_end = a.tab.bnd[c + 1];
+  const int64_t bh = (int64_t)b * a.H + h;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + bh * (int64_t)a.N * D;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + bh * (int64_t)a.N * D;
+  const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + (int64_t)b * a.q_bstride + (int64_t)h * a.M * D;
+  const uint16_t* Gg = static_cast<const uint16_t*>(a.dZ) + bh * (int64_t)a.M * D;
+  const_u64* mw = a.mask_words ? (const_u64*)(a.mask_words + (int64_t)b * a.mask_words_stride) : nullptr;
+
+  const int m = 32 * wave + l32;
+  bf16x8_t qop[KS], gop[KS];
+  {
+    const uint16_t* qrow = Qg + (int64_t)m * D + 8 * hh;
+    const uint16_t* grow = Gg + (int64_t)m * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qop[ks] = __builtin_bit_cast(bf16x8_t, ld16(qrow + 16 * ks));
+      gop[ks] = __builtin_bit_cast(bf16x8_t, ld16(grow + 16 * ks));
+    }
+  }
+  const float Lm = a.L[bh * a.M + m];
+  const float cm = a.c[bh * a.M + m];
+  wait_vm<0>();   // only the ring's loads are in flight from here on
+  const float c2 = a.scale_log2;
+  // P = exp2(s*log2e*S - L*log2e); a row with L = -inf gets P = 0
+  const float nl2 = (Lm == kNegInf) ? __builtin_huge_valf() : Lm * kLog2e;
+
+  const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
+  auto tile_bits = [&](int u) -> uint64_t {
+    if (u >= ntiles) return 0ull;
+    const int t0 = t_begin + u * TILE;
+    const int n = t_end - t0;
+    uint64_t bits = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    if (mw) bits &= mask_tile_bits(mw, t0);
+    return bits;
+  };
+  auto issue = [&](int u) {
+    const int t0 = t_begin + u * TILE;
+    const int nrows = t_end - t0;
+    const uint32_t kst = lds_addr(smem) + (u % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < NI / NW; ++j) {
+      const int ii = wave + NW * j;
+      const int byte = ii * 1024 + lane * 16;
+      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+      const int ch = pc ^ kv_swz<D>(r);
+      const int rr = r < nrows ? r : 0;
+      const int64_t off = (int64_t)(t0 + rr) * D + 8 * ch;
+      dma16(Kg + off, kst + ii * 1024);
+      dma16(Vg + off, kst + TB + ii * 1024);
+    }
+  };
+
+  f32x16_t acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16_t{};
+  uint64_t ring[S];
+#pragma unroll
+  for (int k = 0; k < S; ++k) ring[k] = 0ull;
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) {
+    ring[k] = tile_bits(k);
+    if (ring[k]) issue(k);
+  }
+  const int swk = D == 64 ? ((l32 >> 1) & 7) : (l32 & 15);
+  for (int t = 0; t < ntiles; ++t) {
+    int later = 0;
+#pragma unroll
+    for (int k = 1; k < S - 1; ++k) later += ring[k] != 0ull;
+    wait_tiles<OPS, S>(later);
+    barrier_lds();
+    ring[S - 1] = tile_bits(t + S - 1);
+    if (ring[S - 1]) issue(t + S - 1);
+    const uint64_t bits = ring[0];
+    if (bits) {
+      uint8_t* kst = smem + (t % S) * STAGE;
+      uint8_t* vst = kst + TB;
+      if (bits != ~0ull) {
+        // invalid rows of both K and V become zero: they meet P = 0 and dS = 0
+        for (int f = tid; f < TILE * (ROWB / 16); f += 64 * NW) {
+          const int r = f / (ROWB / 16), pc = f % (ROWB / 16);
+          if (!((bits >> r) & 1ull)) {
+            st16(kst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
+            st16(vst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
+          }
+        }
+        barrier_lds();
+      }
+      f32x16_t sc[2], dp[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        sc[b2] = f32x16_t{};
+        dp[b2] = f32x16_t{};
+        const uint8_t* krow = kst + (32 * b2 + swap23(l32)) * ROWB;
+        const uint8_t* vrow = vst + (32 * b2 + swap23(l32)) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = (2 * ks + hh) ^ swk;
+          sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16)),
+                                qop[ks], sc[b2]);
+          dp[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vrow + ch * 16)),
+                                gop[ks], dp[b2]);
+        }
+      }
+      // register r of lane half hh in block b2 holds token 32*b2 + 16*(r/8) + 8*hh + r%8
+      const uint64_t lb = bits >> (8 * hh);
+      bf16x8_t pk[4];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          float ds[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * g + j;
+            const int tk = 32 * b2 + 16 * (r >> 3) + (r & 7);
+            const float p = fast_exp2(__builtin_fmaf(sc[b2][r], c2, -nl2));
+            ds[j] = ((lb >> tk) & 1ull) ? p * (dp[b2][r] - cm) : 0.f;
+          }
+          u32x4_t w;
+          w[0] = pack_bf16x2(ds[0], ds[1]);
+          w[1] = pack_bf16x2(ds[2], ds[3]);
+          w[2] = pack_bf16x2(ds[4], ds[5]);
+          w[3] = pack_bf16x2(ds[6], ds[7]);
+          pk[2 * b2 + g] = __builtin_bit_cast(bf16x8_t, w);
+        }
+      // dQ^T += K^T dS^T through transposing reads of the K tile
+      const int lg = lane >> 4, li = lane & 15;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+        const int chl = d0 >> 3, half = (d0 & 7) * 2;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x2_t part[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int n = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+            const uint8_t* src = kst + n * ROWB + ((chl ^ kv_swz<D>(n)) * 16) + half;
+            part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+          }
+          const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
+          acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pk[ks], acc[db]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k) ring[k] = ring[k + 1];
+  }
+  // unscaled chunk sum -> workspace slot c (row m, dims d)
+  float* W = a.ws_dq + (((int64_t)a.tab.slot[c] * a.B + b) * a.H + h) * (int64_t)a.M * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4_t v = {acc[db][4 * q], acc[db][4 * q + 1], acc[db][4 * q + 2], acc[db][4 * q + 3]};
+      *reinterpret_cast<f32x4_t*>(W + (int64_t)m * D + 32 * db + 8 * q + 4 * hh) = v;
+    }
+}
+
+// dQ = s * sum over chunk slots (fixed order), one thread per 4 elements
+__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restrict__ ws, int nslots, int64_t n4,
+                                                           float scale, float* __restrict__ dQ) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < nslots; ++k) s += reinterpret_cast<const f32x4_t*>(ws)[(int64_t)k * n4 + i];
+  reinterpret_cast<f32x4_t*>(dQ)[i] = s * scale;
+}
+
+bool bwd_mfma_supported(int M, int D) {
+  return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128 || M == 256);
+}
+
+template <int D, int NW, int S>
+static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, NW, S>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s) {
+  if (a.D == 64) {
+    switch (a.M) {
+      case 32: return launch_dq_t<64, 1, 3>(a, s);
+      case 64: return launch_dq_t<64, 2, 3>(a, s);
+      case 128: return launch_dq_t<64, 4, 3>(a, s);
+      case 256: return launch_dq_t<64, 8, 3>(a, s);
+    }
+  } else if (a.D == 128) {
+    switch (a.M) {
+      case 32: return launch_dq_t<128, 1, 3>(a, s);
+      case 64: return launch_dq_t<128, 2, 3>(a, s);
+      case 128: return launch_dq_t<128, 4, 3>(a, s);
+      case 256: return launch_dq_t<128, 8, 3>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, hipStream_t s) {
+  const int64_t n4 = elems / 4;
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, ws, nslots, n4,
+                     scale, dQ);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_rowdot(const void* dZ, bool bf16, const float* Z, int64_t rows, int D, float* c,
                              hipStream_t s) {
   if (rows == 0) return hipSuccess;
@@ -167,16 +407,19 @@ hipError_t launch_bwd_rowdot(const void* dZ, bool bf16, const float* Z, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_generic(const BwdArgs& a, bool bf16, hipStream_t s) {
+hipError_t launch_bwd_kv_generic(const BwdArgs& a, bool bf16, hipStream_t s) {
   const int64_t toks = (int64_t)a.B * a.H * a.N;
+  if (toks == 0) return hipSuccess;
+  const unsigned g = (unsigned)((toks + 3) / 4);
+  if (bf16) hipLaunchKernelGGL(bwd_kv_generic_kernel<uint16_t>, dim3(g), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(bwd_kv_generic_kernel<float>, dim3(g), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_generic(const BwdArgs& a, bool bf16, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.M;
-  if (toks > 0) {
-    const unsigned g = (unsigned)((toks + 3) / 4);
-    if (bf16) hipLaunchKernelGGL(bwd_kv_generic_kernel<uint16_t>, dim3(g), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(bwd_kv_generic_kernel<float>, dim3(g), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  hipError_t e = launch_bwd_kv_generic(a, bf16, s);
+  if (e != hipSuccess) return e;
   if (rows > 0) {
     const unsigned g = (unsigned)((rows + 3) / 4);
     if (bf16) hipLaunchKernelGGL(bwd_q_generic_kernel<uint16_t>, dim3(g), dim3(256), 0, s, a);

@@ -105,6 +105,10 @@ hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 hipError_t launch_bwd_rowdot(const void* dZ, bool bf16, const float* Z, int64_t rows, int D, float* c,
                              hipStream_t s);
 hipError_t launch_bwd_generic(const BwdArgs& a, bool bf16, hipStream_t s);
+bool bwd_mfma_supported(int M, int D);
+hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, hipStream_t s);
+hipError_t launch_bwd_kv_generic(const BwdArgs& a, bool bf16, hipStream_t s);
 
 bool decode_mfma_supported(int M, int D);
 int decode_waves(int D);

@@ -38,7 +38,7 @@ def lib():
     L.flare_decode.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp]
     L.flare_encode_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp,
                                    vp, vp, vp, vp, sz, vp]
-    L.flare_encode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64]
+    L.flare_encode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64, i32]
     L.flare_encode_bwd_workspace_size.restype = sz
     L.flare_last_error.restype = ctypes.c_char_p
     L.flare_version.restype = ctypes.c_char_p
