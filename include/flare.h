@@ -148,7 +148,10 @@ size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, i
  * over the batch is the caller's).  dK, dV: [B,H,N,D] in dtype; rows of masked
  * tokens are written as 0.  Rows with L = -inf get zero gradients.
  * Offsets are validated as in flare_encode; workspace must hold
- * flare_encode_bwd_workspace_size() bytes.
+ * flare_encode_bwd_workspace_size() bytes, 16-byte aligned.  For bf16 with
+ * D in {64,128} and M in {32,64,128,256} the matrix-core path runs; it needs
+ * Q, K, V, dZ, dQ, dK, dV 16-byte aligned (else FLARE_EINVAL) and sums dQ over
+ * token chunks in a fixed order, so results are bitwise reproducible.
  */
 flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D,
                               const void* Q, int64_t q_batch_stride, const void* K, const void* V,

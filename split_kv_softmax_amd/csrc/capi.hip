@@ -442,8 +442,9 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   if (!aligned16(workspace)) return fail(FLARE_EINVAL, "workspace must be 16-byte aligned");
   if (plan.mfma) {
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dZ) || !aligned16(dQ) ||
+        !aligned16(dK) || !aligned16(dV) ||
         (q_batch_stride * 2) % 16 != 0)
-      return fail(FLARE_EINVAL, "Q, K, V, dZ, dQ and the Q batch stride must be 16-byte aligned");
+      return fail(FLARE_EINVAL, "Q, K, V, dZ, dQ, dK, dV and the Q batch stride must be 16-byte aligned");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -487,12 +488,17 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   a.tab.nchunks = nc;
   for (int i = 0; i <= nc; ++i) a.tab.bnd[i] = plan.bnd[i];
   for (int i = 0; i < nc; ++i) a.tab.slot[i] = (int16_t)i;
-  e = launch_bwd_dq_mfma(a, s);
-  if (e != hipSuccess) return hip_fail(e, "query-gradient launch");
+  // one pass over K, V where the registers allow the fused kernel, else a
+  // separate query-gradient pass; both leave per-chunk partials for the reduce
+  const bool fuse = bwd_kv_fuses_dq(M, D);
+  if (!fuse) {
+    e = launch_bwd_dq_mfma(a, s);
+    if (e != hipSuccess) return hip_fail(e, "query-gradient launch");
+  }
+  e = launch_bwd_kv_mfma(a, fuse, s);
+  if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
   e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, scale, dQ, s);
   if (e != hipSuccess) return hip_fail(e, "query-gradient reduce launch");
-  e = launch_bwd_kv_generic(a, bf16, s);
-  if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
   return FLARE_OK;
 }
 

@@ -346,6 +346,325 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core key/value gradients (FLARE++ appendix, backward pass): one
+// workgroup per (b, h, token chunk); 64-token tiles through a direct-load ring.
+// Phase A (one wave per 32 latent rows, lane = latent row):
+//   S^T = K Q^T, dP^T = V dZ^T, P = exp(s S - L), dS = P (dP - c)
+//   P and dS go to LDS as bf16 [m][token]; with DQ the wave also adds
+//   K^T dS^T into its query-gradient partial, as the query-gradient kernel does.
+// Phase B (each wave one gradient tensor and a slice of output blocks,
+// lane = token):
+//   dV^T = dZ^T P,  dK^T = s Q^T dS        (contraction over the M latents)
+// with dZ^T / Q^T slices held in registers for the whole chunk.  The tile's
+// gradients are staged in the tile's own K/V slot and leave as whole
+// coalesced rows.  Padded tokens get P = dS = 0, hence zero rows; tiles with
+// no valid token are not loaded and only write zeros.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swap_bits2(int x) { return ((x & 1) << 1) | (x >> 1); }
+
+template <int D, int M, int NW, int S, bool DQ>
+__global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
+  constexpr int TILE = 64;
+  constexpr int ROWB = 2 * D;          // bytes of one K/V/gradient row
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int TB = TILE * ROWB;
+  constexpr int STAGE = 2 * TB;
+  constexpr int NI = TB / 1024;
+  constexpr int KS = D / 16;           // contraction steps over the head dim
+  constexpr int KM = M / 16;           // contraction steps over the latents
+  constexpr int DB = D / 32;
+  constexpr int MW = M / 32;           // waves with latent rows in phase A
+  constexpr int OPS = 2 * NI / NW;
+  constexpr int PDS = M * TILE * 2;    // one bf16 [M][64] buffer
+  constexpr int RING = S * STAGE;
+  constexpr int LDS_MAIN = RING + 2 * PDS;
+  constexpr int LDS_STAT = 2 * M * D * 2;
+  constexpr int LDS = LDS_MAIN > LDS_STAT ? LDS_MAIN : LDS_STAT;
+  constexpr int WPT = NW / 2;          // phase-B waves per gradient tensor
+  constexpr int NDW = DB >= WPT ? DB / WPT : 1;
+  constexpr int NNB = DB >= WPT ? 2 : 2 * DB / WPT;
+  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  static_assert(MW <= NW && NW % 2 == 0 && WPT <= 2 * DB, "wave layout");
+  static_assert(OPS * (S - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  uint8_t* pbuf = smem + RING;
+  uint8_t* dsbuf = pbuf + PDS;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lg = lane >> 4, li = lane & 15;
+  const int nch = a.tab.nchunks;
+  int bid = blockIdx.x;
+  const int c = bid % nch;
+  bid /= nch;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int t_begin = a.tab.bnd[c], t_end = a.tab.bnd[c + 1];
+  const int64_t bh = (int64_t)b * a.H + h;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + bh * (int64_t)a.N * D;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + bh * (int64_t)a.N * D;
+  const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
+  const uint16_t* Gg = static_cast<const uint16_t*>(a.dZ) + bh * (int64_t)M * D;
+  uint16_t* dKg = static_cast<uint16_t*>(a.dK) + bh * (int64_t)a.N * D;
+  uint16_t* dVg = static_cast<uint16_t*>(a.dV) + bh * (int64_t)a.N * D;
+  const_u64* mw = a.mask_words ? (const_u64*)(a.mask_words + (int64_t)b * a.mask_words_stride) : nullptr;
+
+  // ---- stationary operands: Q and dZ through LDS ([m][d], row-major) ----
+  for (int f = tid; f < M * CPR; f += 64 * NW) {
+    const int r = f / CPR, ch = f % CPR;
+    const u32x4_t q = ld16(Qg + (int64_t)r * D + 8 * ch);
+    const u32x4_t g = ld16(Gg + (int64_t)r * D + 8 * ch);
+    st16(smem + r * ROWB + ch * 16, q);
+    st16(smem + M * ROWB + r * ROWB + ch * 16, g);
+  }
+  __syncthreads();
+  const bool pa = wave < MW;           // wave has latent rows in phase A
+  const int m = 32 * (pa ? wave : 0) + l32;
+  bf16x8_t qop[KS], gop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qop[ks] = __builtin_bit_cast(bf16x8_t, ld16(smem + m * ROWB + (16 * ks + 8 * hh) * 2));
+    gop[ks] = __builtin_bit_cast(bf16x8_t, ld16(smem + M * ROWB + m * ROWB + (16 * ks + 8 * hh) * 2));
+  }
+  // phase-B role: tensor t (0 = dV from dZ^T, 1 = dK from Q^T), d-blocks, n-blocks
+  const int tsel = wave / WPT, wi = wave % WPT;
+  const int db0 = DB >= WPT ? wi * NDW : wi % DB;
+  const int nb0 = DB >= WPT ? 0 : (wi / DB) * NNB;
+  // A operand rows permuted so that each register group holds 8 consecutive d:
+  // lane i of a 16-lane group reads column swap23(i) of the 4x16 block
+  bf16x8_t ast[NDW][KM];
+  {
+    const uint8_t* src = smem + (tsel == 0 ? M * ROWB : 0);
+#pragma unroll
+    for (int j = 0; j < NDW; ++j)
+#pragma unroll
+      for (int ks = 0; ks < KM; ++ks) {
+        u32x2_t part[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+          const int col = 32 * (db0 + j) + 16 * (lg & 1) + 4 * swap_bits2(li & 3);
+          part[q] = __builtin_bit_cast(
+              u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(src + row * ROWB + col * 2)));
+        }
+        ast[j][ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]});
+      }
+  }
+  const float Lm = a.L[bh * M + m];
+  const float cm = a.c[bh * M + m];
+  wait_vm<0>();
+  barrier_lds();   // the stationary copy is dead from here on: the ring reuses it
+  const float c2 = a.scale_log2;
+  const float nl2 = (Lm == kNegInf) ? __builtin_huge_valf() : Lm * kLog2e;
+
+  const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
+  auto tile_bits = [&](int u) -> uint64_t {
+    if (u >= ntiles) return 0ull;
+    const int t0 = t_begin + u * TILE;
+    const int n = t_end - t0;
+    uint64_t bits = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    if (mw) bits &= mask_tile_bits(mw, t0);
+    return bits;
+  };
+  auto issue = [&](int u) {
+    const int t0 = t_begin + u * TILE;
+    const int nrows = t_end - t0;
+    const uint32_t kst = lds_addr(smem) + (u % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < NI / NW; ++j) {
+      const int ii = wave + NW * j;
+      const int byte = ii * 1024 + lane * 16;
+      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+      const int ch = pc ^ kv_swz<D>(r);
+      const int rr = r < nrows ? r : 0;
+      const int64_t off = (int64_t)(t0 + rr) * D + 8 * ch;
+      dma16(Kg + off, kst + ii * 1024);
+      dma16(Vg + off, kst + TB + ii * 1024);
+    }
+  };
+  // staged gradient rows: 16-byte chunk ch of row n sits at ch ^ (n & (CPR-1))
+  auto out_swz = [](int n) { return n & (CPR - 1); };
+
+  f32x16_t dq[DQ ? DB : 1];
+#pragma unroll
+  for (int i = 0; i < (DQ ? DB : 1); ++i) dq[i] = f32x16_t{};
+  uint64_t ring[S];
+#pragma unroll
+  for (int k = 0; k < S; ++k) ring[k] = 0ull;
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) {
+    ring[k] = tile_bits(k);
+    if (ring[k]) issue(k);
+  }
+  const int swk = D == 64 ? ((l32 >> 1) & 7) : (l32 & 15);
+  for (int t = 0; t < ntiles; ++t) {
+    int later = 0;
+#pragma unroll
+    for (int k = 1; k < S - 1; ++k) later += ring[k] != 0ull;
+    wait_tiles<OPS, S>(later);
+    barrier_lds();
+    ring[S - 1] = tile_bits(t + S - 1);
+    if (ring[S - 1]) issue(t + S - 1);
+    const uint64_t bits = ring[0];
+    const int t0 = t_begin + t * TILE;
+    const int nrows = t_end - t0 < TILE ? t_end - t0 : TILE;
+    if (!bits) {
+      // no valid token: zero gradient rows, nothing loaded
+      for (int f = tid; f < TILE * CPR; f += 64 * NW) {
+        const int r = f / CPR, ch = f % CPR;
+        if (r < nrows) {
+          const int64_t off = (int64_t)(t0 + r) * D + 8 * ch;
+          st16(dKg + off, u32x4_t{0, 0, 0, 0});
+          st16(dVg + off, u32x4_t{0, 0, 0, 0});
+        }
+      }
+    } else {
+      uint8_t* kst = smem + (t % S) * STAGE;
+      uint8_t* vst = kst + TB;
+      if (DQ && bits != ~0ull) {
+        // invalid K rows become zero: they meet dS = 0 in the query gradient
+        for (int f = tid; f < TILE * CPR; f += 64 * NW) {
+          const int r = f / CPR, pc = f % CPR;
+          if (!((bits >> r) & 1ull)) st16(kst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
+        }
+        barrier_lds();
+      }
+      // ---- phase A ----
+      if (pa) {
+        const uint64_t lb = bits >> (8 * hh);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+          const uint8_t* krow = kst + (32 * b2 + swap23(l32)) * ROWB;
+          const uint8_t* vrow = vst + (32 * b2 + swap23(l32)) * ROWB;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const int ch = (2 * ks + hh) ^ swk;
+            sc = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16)),
+                              qop[ks], sc);
+            dp = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vrow + ch * 16)),
+                              gop[ks], dp);
+          }
+          // register r of lane half hh holds token 32*b2 + 16*(r/8) + 8*hh + r%8
+          bf16x8_t pk[2];
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            float pv[8], ds[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int r = 8 * g + j;
+              const int tk = 32 * b2 + 16 * g + j;
+              const bool ok = (lb >> tk) & 1ull;
+              const float p = fast_exp2(__builtin_fmaf(sc[r], c2, -nl2));
+              pv[j] = ok ? p : 0.f;
+              ds[j] = ok ? p * (dp[r] - cm) : 0.f;
+            }
+            const u32x4_t wp = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                                pack_bf16x2(pv[6], pv[7])};
+            const u32x4_t wd = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                                pack_bf16x2(ds[6], ds[7])};
+            const int pc = (4 * b2 + 2 * g + hh) ^ (m & 7);
+            st16(pbuf + m * (TILE * 2) + pc * 16, wp);
+            st16(dsbuf + m * (TILE * 2) + pc * 16, wd);
+            pk[g] = __builtin_bit_cast(bf16x8_t, wd);
+          }
+          if constexpr (DQ) {
+            // dQ^T += K^T dS^T over this block's 32 tokens
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+              const int chl = d0 >> 3, half = (d0 & 7) * 2;
+#pragma unroll
+              for (int g = 0; g < 2; ++g) {
+                u32x2_t part[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                  const int n = 32 * b2 + 16 * g + 8 * (lg >> 1) + 4 * q + (li >> 2);
+                  const uint8_t* src = kst + n * ROWB + ((chl ^ kv_swz<D>(n)) * 16) + half;
+                  part[q] = __builtin_bit_cast(u32x2_t,
+                                               __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+                }
+                const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
+                dq[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pk[g], dq[db]);
+              }
+            }
+          }
+        }
+      }
+      barrier_lds();
+      // ---- phase B: this wave's output blocks, staged into the tile's K/V slot ----
+      {
+        const uint8_t* bsrc = tsel == 0 ? pbuf : dsbuf;
+        uint8_t* stg = tsel == 0 ? vst : kst;
+        const float osc = tsel == 0 ? 1.f : a.scale;
+#pragma unroll
+        for (int nbi = 0; nbi < NNB; ++nbi) {
+          const int nb = nb0 + nbi;
+          f32x16_t acc[NDW];
+#pragma unroll
+          for (int j = 0; j < NDW; ++j) acc[j] = f32x16_t{};
+#pragma unroll
+          for (int ks = 0; ks < KM; ++ks) {
+            u32x2_t part[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+              const int col = 32 * nb + 16 * (lg & 1) + 4 * (li & 3);
+              const int pc = (col >> 3) ^ (row & 7);
+              part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                        (lds_bf16x4*)(bsrc + row * (TILE * 2) + pc * 16 +
+                                                                      (col & 7) * 2)));
+            }
+            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]});
+#pragma unroll
+            for (int j = 0; j < NDW; ++j) acc[j] = mfma32x32x16(ast[j][ks], bop, acc[j]);
+          }
+          // register r of lane half hh: d = 32*db + 16*(r/8) + 8*hh + r%8, token 32*nb + l32
+          const int n = 32 * nb + l32;
+#pragma unroll
+          for (int j = 0; j < NDW; ++j)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const f32x16_t& v = acc[j];
+              const u32x4_t w = {pack_bf16x2(osc * v[8 * g + 0], osc * v[8 * g + 1]),
+                                 pack_bf16x2(osc * v[8 * g + 2], osc * v[8 * g + 3]),
+                                 pack_bf16x2(osc * v[8 * g + 4], osc * v[8 * g + 5]),
+                                 pack_bf16x2(osc * v[8 * g + 6], osc * v[8 * g + 7])};
+              const int ch = 4 * (db0 + j) + 2 * g + hh;
+              st16(stg + n * ROWB + (ch ^ out_swz(n)) * 16, w);
+            }
+        }
+      }
+      barrier_lds();
+      // ---- whole rows out: dK from the K slot, dV from the V slot ----
+      for (int f = tid; f < 2 * TILE * CPR; f += 64 * NW) {
+        const int tsr = f / (TILE * CPR);
+        const int r = (f / CPR) % TILE, ch = f % CPR;
+        if (r < nrows) {
+          const u32x4_t v = ld16((tsr ? vst : kst) + r * ROWB + (ch ^ out_swz(r)) * 16);
+          st16((tsr ? dVg : dKg) + (int64_t)(t0 + r) * D + 8 * ch, v);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k) ring[k] = ring[k + 1];
+  }
+  if constexpr (DQ) {
+    if (pa) {
+      float* W = a.ws_dq + (((int64_t)a.tab.slot[c] * a.B + b) * a.H + h) * (int64_t)M * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t v = {dq[db][4 * q], dq[db][4 * q + 1], dq[db][4 * q + 2], dq[db][4 * q + 3]};
+          *reinterpret_cast<f32x4_t*>(W + (int64_t)m * D + 32 * db + 8 * q + 4 * hh) = v;
+        }
+    }
+  }
+}
+
 // dQ = s * sum over chunk slots (fixed order), one thread per 4 elements
 __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restrict__ ws, int nslots, int64_t n4,
                                                            float scale, float* __restrict__ dQ) {
@@ -384,6 +703,39 @@ hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s) {
     }
   }
   return hipErrorInvalidValue;
+}
+
+template <int D, int M, int NW, int S, bool DQ>
+static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
+  hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
+
+template <bool DQ>
+static hipError_t launch_kv_dq(const BwdArgs& a, hipStream_t s) {
+  if (a.D == 64) {
+    switch (a.M) {
+      case 32: return launch_kv_t<64, 32, 4, 3, DQ>(a, s);
+      case 64: return launch_kv_t<64, 64, 4, 3, DQ>(a, s);
+      case 128: return launch_kv_t<64, 128, 4, 3, DQ>(a, s);
+      case 256: return launch_kv_t<64, 256, 8, 3, DQ>(a, s);
+    }
+  } else if (a.D == 128) {
+    switch (a.M) {
+      case 32: return launch_kv_t<128, 32, 4, 3, DQ>(a, s);
+      case 64: return launch_kv_t<128, 64, 4, 3, DQ>(a, s);
+      case 128: return launch_kv_t<128, 128, 4, 3, DQ>(a, s);
+      case 256: return launch_kv_t<128, 256, 8, 2, DQ>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+bool bwd_kv_fuses_dq(int M, int D) { return !(M == 256 && D == 128); }
+
+hipError_t launch_bwd_kv_mfma(const BwdArgs& a, bool with_dq, hipStream_t s) {
+  return with_dq ? launch_kv_dq<true>(a, s) : launch_kv_dq<false>(a, s);
 }
 
 hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, hipStream_t s) {

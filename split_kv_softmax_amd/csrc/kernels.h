@@ -107,6 +107,10 @@ hipError_t launch_bwd_rowdot(const void* dZ, bool bf16, const float* Z, int64_t 
 hipError_t launch_bwd_generic(const BwdArgs& a, bool bf16, hipStream_t s);
 bool bwd_mfma_supported(int M, int D);
 hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s);
+// key/value gradients on matrix cores; with_dq also writes the query-gradient
+// chunk partials (only where bwd_kv_fuses_dq says the registers allow it)
+bool bwd_kv_fuses_dq(int M, int D);
+hipError_t launch_bwd_kv_mfma(const BwdArgs& a, bool with_dq, hipStream_t s);
 hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, hipStream_t s);
 hipError_t launch_bwd_kv_generic(const BwdArgs& a, bool bf16, hipStream_t s);
 

@@ -50,9 +50,34 @@ def _check(w, x, Z, L, dQ, dK, dV, fp32=False):
         assert (dK[inv] == 0).all() and (dV[inv] == 0).all()
 
 
-@pytest.mark.parametrize("M,D", [(256, 128), (128, 64), (64, 64)])
+# every matrix-core shape: fused (one pass) and split (separate query-gradient pass)
+@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64),
+                                 (32, 128), (64, 128), (128, 128), (256, 128)])
 def test_backward_masked_bf16(M, D):
     w, x = _masked_case(M, D, N=2048, R=4)
+    _check(w, x, *_run(w, x))
+
+
+def test_backward_padding_contents_do_not_matter():
+    """NaN in masked K/V rows changes nothing: the gradients are bitwise those of clean padding."""
+    w, x = _masked_case(128, 64, N=2048, R=4, wid=980)
+    a = _run(w, x)
+    inv = (x["mask"] == 0)[:, None, :, None].expand_as(x["K"])
+    y = dict(x)
+    y["K"] = x["K"].masked_fill(inv, float("nan"))
+    y["V"] = x["V"].masked_fill(inv, float("nan"))
+    O, Lp = fl.encode(y["Q"], y["K"], y["V"], w.offsets, y["mask"], w.scale)
+    Z, L, _ = fl.lse_merge(O, Lp)
+    assert torch.equal(Z, a[0]) and torch.equal(L, a[1])
+    g = fl.encode_bwd(y["Q"], y["K"], y["V"], w.offsets, y["mask"], w.scale, a[0], a[1], y["dZ"])
+    torch.cuda.synchronize()
+    for u, v in zip(g, a[2:]):
+        assert torch.equal(u, v)
+
+
+def test_backward_many_chunks_ragged_tail():
+    """One (b, h) slice, so the tokens split into many chunks; N is not a multiple of 64."""
+    w, x = _masked_case(128, 64, N=40000, R=7, B=1, H=1, wid=990)
     _check(w, x, *_run(w, x))
 
 
