@@ -1,6 +1,6 @@
 """Throughput of the split-KV / FLARE softmax hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cpu-seconds S]
 
 A step is one pass of the whole path over one batch of synthetic input that
 already sits in HBM.  For the default workload (FLARE++, B=1, H=16, N=262144,
@@ -79,9 +79,9 @@ class FlareppStep:
         self.Z = torch.empty((B, H, M, D), **f32)
         self.L = torch.empty((B, H, M), **f32)
         self.Y = torch.empty_like(x["K"])
+        self.names = ["encode1", "merge1", "encode2", "merge2", "decode"]
         self.ev = [_ev() for _ in range(6)]
-        # per-phase (enc1, merge1, enc2, merge2, decode) milliseconds
-        self.phase_ms = [0.0] * 5
+        self.phase_ms = [0.0] * 5       # per-phase milliseconds, summed over collected steps
         self.count = 0
 
     def __call__(self, timed_phases: bool):
@@ -106,31 +106,158 @@ class FlareppStep:
 
     def collect(self):
         torch.cuda.synchronize()
-        for i in range(5):
+        for i in range(len(self.phase_ms)):
             self.phase_ms[i] += self.ev[i].elapsed_time(self.ev[i + 1])
         self.count += 1
 
 
-def cpu_baseline_flarepp(w: W.Workload, x, heads=1):
-    """Time the float64 oracle on `heads` heads of the same inputs (full N)."""
-    import numpy as np
-    from oracle import flare_ref as ref
+class FlareStep:
+    """FLARE block: encode -> merge -> decode of every token (K as token queries, Q as latent keys)."""
+
+    def __init__(self, w: W.Workload, x):
+        self.w, self.x = w, x
+        B, H, N, M, D, R = w.B, w.H, w.N, w.M, w.D, w.R
+        f32 = dict(dtype=torch.float32, device=x["K"].device)
+        self.O = torch.empty((R, B, H, M, D), **f32)
+        self.Lp = torch.empty((R, B, H, M), **f32)
+        self.Z = torch.empty((B, H, M, D), **f32)
+        self.L = torch.empty((B, H, M), **f32)
+        self.Y = torch.empty_like(x["K"])
+        self.names = ["encode", "merge", "decode"]
+        self.ev = [_ev() for _ in range(len(self.names) + 1)]
+        self.phase_ms = [0.0] * len(self.names)
+        self.count = 0
+
+    def __call__(self, timed_phases: bool):
+        x, w, ev = self.x, self.w, self.ev
+        rec = (lambda i: ev[i].record()) if timed_phases else (lambda i: None)
+        rec(0)
+        fl.encode(x["Q"], x["K"], x["V"], w.offsets, None, w.scale, self.O, self.Lp)
+        rec(1)
+        fl.lse_merge(self.O, self.Lp, Z=self.Z, L=self.L)
+        rec(2)
+        fl.decode(x["K"], x["Q"], self.Z, w.scale, None, self.Y)
+        rec(3)
+
+    collect = FlareppStep.collect
+
+
+class EncodeMergeStep:
+    """Encoder over every partition, then the tree merge (single-query split-KV, small encoder)."""
+
+    def __init__(self, w: W.Workload, x):
+        self.w, self.x = w, x
+        B, H, N, M, D, R = w.B, w.H, w.N, w.M, w.D, w.R
+        f32 = dict(dtype=torch.float32, device=x["K"].device)
+        self.O = torch.empty((R, B, H, M, D), **f32)
+        self.Lp = torch.empty((R, B, H, M), **f32)
+        self.Z = torch.empty((B, H, M, D), **f32)
+        self.L = torch.empty((B, H, M), **f32)
+        self.names = ["encode", "merge"]
+        self.ev = [_ev() for _ in range(len(self.names) + 1)]
+        self.phase_ms = [0.0] * len(self.names)
+        self.count = 0
+
+    def __call__(self, timed_phases: bool):
+        x, w, ev = self.x, self.w, self.ev
+        rec = (lambda i: ev[i].record()) if timed_phases else (lambda i: None)
+        rec(0)
+        fl.encode(x["Q"], x["K"], x["V"], w.offsets, x.get("mask"), w.scale, self.O, self.Lp)
+        rec(1)
+        fl.lse_merge(self.O, self.Lp, Z=self.Z, L=self.L)
+        rec(2)
+
+    collect = FlareppStep.collect
+
+
+class FwdBwdStep(EncodeMergeStep):
+    """Masked encoder forward + merge, then the encoder backward with the global statistics."""
+
+    def __init__(self, w: W.Workload, x):
+        super().__init__(w, x)
+        B, H, M, D = w.B, w.H, w.M, w.D
+        dev = x["K"].device
+        self.dQ = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+        self.dK = torch.empty_like(x["K"])
+        self.dV = torch.empty_like(x["V"])
+        self.names = ["encode", "merge", "backward"]
+        self.ev = [_ev() for _ in range(len(self.names) + 1)]
+        self.phase_ms = [0.0] * len(self.names)
+
+    def __call__(self, timed_phases: bool):
+        super().__call__(timed_phases)
+        x, w = self.x, self.w
+        fl.encode_bwd(x["Q"], x["K"], x["V"], w.offsets, x.get("mask"), w.scale, self.Z, self.L, x["dZ"],
+                      self.dQ, self.dK, self.dV)
+        if timed_phases:
+            self.ev[3].record()
+
+
+def _oracle_cores():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
-    sl = [(0, h) for h in range(heads)]
-    # copy the sampled slices to the host before the clock starts
-    xs = {k: (v[:heads] if v.dim() == 3 else v[:, :heads]).cpu() for k, v in x.items()}
-    t0 = time.perf_counter()
-    ref.flarepp_ref(xs["Qt"], xs["Kt"], xs["Vt"], xs["K"], xs["V"], w.offsets, w.scale, slices=sl)
-    dt = time.perf_counter() - t0
-    tokens = w.B * w.N * heads
-    _ = np
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"FLARE++ chain (2 encoders + decode) for {heads} of {w.H} heads, batch 0, full N={w.N}; "
-                      f"{dt:.2f} s wall"}
+        return len(os.sched_getaffinity(0))
+
+
+def _host(t, b, h):
+    return t[h:h + 1].cpu() if t.dim() == 3 else t[b:b + 1, h:h + 1].cpu()
+
+
+def cpu_baseline(w: W.Workload, x, budget_s: float):
+    """Time the float64 oracle on whole (batch, head) slices of the same inputs, full N each,
+    until about ``budget_s`` seconds of CPU work are done; tokens/s = sliced tokens / wall."""
+    from oracle import flare_ref as ref
+    todo = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, spent = 0, 0.0
+    for b, h in todo:
+        xs = {k: _host(v, b, h) for k, v in x.items() if k != "mask"}
+        mk = x["mask"][b:b + 1].cpu() if "mask" in x else None
+        t0 = time.perf_counter()
+        if w.kind == "flarepp":
+            ref.flarepp_ref(xs["Qt"], xs["Kt"], xs["Vt"], xs["K"], xs["V"], w.offsets, w.scale)
+        elif w.kind == "flare":
+            e = ref.encode_ref(xs["Q"], xs["K"], xs["V"], w.offsets, None, w.scale)
+            ref.decode_ref(xs["K"], xs["Q"], e["Z"], w.scale)
+        elif w.kind == "encode_bwd":
+            e = ref.encode_ref(xs["Q"], xs["K"], xs["V"], w.offsets, mk, w.scale)
+            ref.encode_bwd_ref(xs["Q"], xs["K"], xs["V"], mk, w.scale, e["Z"], e["L"], xs["dZ"])
+        else:
+            ref.encode_ref(xs["Q"], xs["K"], xs["V"], w.offsets, None, w.scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    what = {"flarepp": "FLARE++ chain (2 encoders + decode)", "flare": "FLARE block (encode + decode)",
+            "encode_bwd": "masked encoder forward + backward", "splitkv": "split-KV encoder + merge",
+            "encode": "encoder + merge"}[w.kind]
+    return {"value": w.N * done / spent, "unit": "tokens/s", "cores": int(_oracle_cores()), "kind": "oracle",
+            "sample": f"{what} on {done} of {w.B * w.H} (batch, head) slices, full N={w.N} each; "
+                      f"{spent:.2f} s wall"}
+
+
+def roofline_of(w: W.Workload, x, step, ph):
+    """Dominant kernel's algorithmic bytes per launch over its event-timed duration."""
+    kvb = 2 if w.dtype == "bf16" else 4
+    row = w.D * kvb                               # bytes of one K, V, Y, dK or dV row
+    rows = w.B * w.H * w.N
+    if w.kind == "flarepp":
+        ms = 0.5 * (ph["encode1"] + ph["encode2"])
+        return ms, 2 * rows * row, "encode_mfma_kernel<64,4,3,3> (flare_encode, one launch)"
+    if w.kind == "flare":
+        if ph["decode"] > ph["encode"]:
+            return ph["decode"], 2 * rows * row, "decode_mfma_kernel (flare_decode, one launch)"
+        return ph["encode"], 2 * rows * row, "encode_mfma_kernel (flare_encode, one launch)"
+    if w.kind == "encode_bwd":
+        valid = int(x["mask"].sum().item()) * w.H if "mask" in x else rows
+        return (ph["backward"], 2 * valid * row + 2 * rows * row,
+                "flare_encode_bwd call (row term, query-gradient, key/value-gradient and reduce kernels)")
+    return ph["encode"], 2 * rows * row, "flare_encode call (one encoder launch)"
+
+
+STEPS = {"flarepp": FlareppStep, "flare": FlareStep, "splitkv": EncodeMergeStep, "encode": EncodeMergeStep,
+         "encode_bwd": FwdBwdStep}
 
 
 def main():
@@ -138,9 +265,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=W.FLAREPP.name)
+    ap.add_argument("--workload", default=W.FLAREPP.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="about this much oracle work on whole (batch, head) slices")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device 3 times "
                          "(the plain copy that scales the HBM byte counters)")
@@ -153,12 +281,9 @@ def main():
         print("no GPU available", file=sys.stderr)
         sys.exit(2)
     w = W.BY_NAME[args.workload]
-    if w.kind != "flarepp":
-        print("only the FLARE++ workload is wired into this bench", file=sys.stderr)
-        sys.exit(2)
     torch.cuda.set_device(0)
     x = w.make("cuda")
-    step = FlareppStep(w, x)
+    step = STEPS[w.kind](w, x)
     for _ in range(args.warmup):
         step(timed_phases=False)
     torch.cuda.synchronize()
@@ -180,15 +305,16 @@ def main():
     for _ in range(args.steps):
         step(timed_phases=True)
         step.collect()
-    ph = [p / step.count for p in step.phase_ms]
-    enc_ms = 0.5 * (ph[0] + ph[2])
-    kv_bytes = 2 * w.B * w.H * w.N * w.D * 2          # K and V, bf16, read once per encoder launch
-    step_bytes = 6 * w.B * w.H * w.N * w.D * 2        # 2 encoders (K,V) + decode (read K, write Y)
-    achieved = kv_bytes / (enc_ms * 1e-3) / 1e9
+    ph = {n: p / step.count for n, p in zip(step.names, step.phase_ms)}
+    kern_ms, kern_bytes, kern_name = roofline_of(w, x, step, ph)
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     tokens = w.B * w.N * w.H
+    kvb = 2 if w.dtype == "bf16" else 4
+    is_main = w.name == W.FLAREPP.name
 
     line = {
-        "metric": "FLARE encode+decode tokens/sec (B*N*H) at N=256K; % of HBM/MFMA roofline",
+        "metric": "FLARE encode+decode tokens/sec (B*N*H) at N=256K; % of HBM/MFMA roofline" if is_main
+        else f"{w.kind} tokens/sec (B*N*H)",
         "value": tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -198,23 +324,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) inputs rounded to bf16)",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": f"synthetic (seeded N(0,1) inputs{' rounded to bf16' if w.dtype == 'bf16' else ''})",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "R": w.R,
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "encode_mfma_kernel<64,4,3,3> (flare_encode, one launch)",
-                     "kernel_ms": enc_ms, "algorithmic_bytes": kv_bytes,
-                     "source_hash": encoder_source_hash()},
-        "step_roofline": {"algorithmic_bytes": step_bytes,
-                          "achieved_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
-                          "frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "phases_ms": {"encode1": ph[0], "merge1": ph[1], "encode2": ph[2], "merge2": ph[3], "decode": ph[4]},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if is_main else None,
+                     "kernel": kern_name, "kernel_ms": kern_ms, "algorithmic_bytes": kern_bytes},
+        "phases_ms": ph,
         "wall_s_timed": wall,
     }
+    if is_main:
+        step_bytes = 6 * tokens * w.D * kvb        # 2 encoders (K,V) + decode (read K, write Y)
+        line["roofline"]["source_hash"] = encoder_source_hash()
+        line["step_roofline"] = {"algorithmic_bytes": step_bytes,
+                                 "achieved_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                                 "frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if "mask" in x:
+        line["config"]["valid_fraction"] = float(x["mask"].float().mean().item())
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_flarepp(w, x, heads=args.cpu_heads)
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     if args.calibrate_copy:
         del x, step
