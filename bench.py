@@ -256,6 +256,25 @@ def roofline_of(w: W.Workload, x, step, ph):
     return ph["encode"], 2 * rows * row, "flare_encode call (one encoder launch)"
 
 
+def copy_reference(nbytes=1 << 30, reps=5):
+    """Context for the HBM roofline: a plain device-to-device copy of 1 GiB
+    (read + write bytes over its event-timed duration)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = _ev(), _ev()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB_s": 2 * nbytes / (ms * 1e-3) / 1e9, "ms": ms, "what": "1 GiB device-to-device copy, read+write bytes"}
+
+
 STEPS = {"flarepp": FlareppStep, "flare": FlareStep, "splitkv": EncodeMergeStep, "encode": EncodeMergeStep,
          "encode_bwd": FwdBwdStep}
 
@@ -342,6 +361,7 @@ def main():
                                  "frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if "mask" in x:
         line["config"]["valid_fraction"] = float(x["mask"].float().mean().item())
+    line["copy_reference"] = copy_reference()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(line), flush=True)

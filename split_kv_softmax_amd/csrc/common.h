@@ -16,6 +16,8 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// cache-policy operand of the buffer intrinsics: bit 1 is the non-temporal hint
+constexpr int kCachePolicyNT = 2;
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -31,6 +33,12 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maxima of scores straight from the matrix cores: the IEEE maximum that
+// propagates NaN needs no input canonicalisation, so 3-input forms stay one
+// instruction each (scores of padding are replaced by -inf before any max).
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmax2(fmax2(a, b), c); }
 
 // 32x32x16 bf16 matrix-core product, D = A*B + C.
 // Operand layout (lane l, wave of 64): A row i = l%32, columns k = 8*(l/32)+0..7;
@@ -80,16 +88,32 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 // drains them before every LDS read nor at every barrier; the kernel counts
 // and waits for them itself (wait_vm) before a barrier publishes a stage.
 // M0 (which carries the LDS destination) is saved and restored around it.
+// The loads are marked non-temporal: every streamed row is read once.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_wave_base) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"                       // one wait state between an SALU write of M0 and its use
-      "global_load_lds_dwordx4 %2, off\n\t"
+      "global_load_lds_dwordx4 %2, off nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds_wave_base), "v"(g)
+      : "memory");
+}
+
+// The same with a wave-uniform 64-bit base (scalar registers) plus a 32-bit
+// per-lane byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t voff, uint32_t lds_wave_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_wave_base), "v"(voff), "s"(base)
       : "memory");
 }
 
@@ -112,21 +136,48 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // ---- K/V tile rings (encoder and backward)
+// XOR swizzle of the 16-byte chunks of row r of a [64 x D] bf16 tile.  Both
+// read patterns are free of bank conflicts with it:
+//  * row reads (one 16-byte chunk per lane, 16 consecutive rows per group of
+//    16 lanes): the swizzle is a bijection on each parity class of 16 rows
+//    (128-byte rows) or on all 16 rows (256-byte rows);
+//  * transposing reads (4 consecutive rows x 4 consecutive chunks per 32
+//    lanes): the 4 rows land in disjoint aligned groups of 4 chunks.
+// D = 64 also serves any other buffer with 128-byte rows.
 template <int D>
 __device__ __forceinline__ int kv_swz(int r) {
-  const int s = swap23(r);
-  return D == 64 ? ((s >> 1) & 7) : (s & 15);
+  return D == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
 }
 
 template <int OPS, int S>
 __device__ __forceinline__ void wait_tiles(int later) {
   // wait until at most `later` tiles' worth of this wave's loads are pending
+  static_assert(S <= 5, "wait table covers S <= 5");
+  if constexpr (S >= 5) {
+    if (later >= 3) { wait_vm<3 * OPS < 64 ? 3 * OPS : 63>(); return; }
+  }
   if constexpr (S >= 4) {
     if (later >= 2) { wait_vm<2 * OPS < 64 ? 2 * OPS : 63>(); return; }
   }
   if constexpr (S >= 3) {
     if (later >= 1) { wait_vm<OPS < 64 ? OPS : 63>(); return; }
   }
+  wait_vm<0>();
+}
+
+// Wait until at most k * UNIT of this wave's vector-memory operations are
+// pending (k = 0 .. KMAX, uniform); the immediate must be a constant, hence
+// the table.  Counts beyond the counter's range wait for 63, which is
+// stronger: loads complete in issue order.
+template <int UNIT, int KMAX>
+__device__ __forceinline__ void wait_units(int k) {
+  static_assert(KMAX <= 8, "table covers k <= 8");
+#define FL_WU(K)                                                   \
+  if constexpr (K <= KMAX) {                                       \
+    if (k == K) { wait_vm<(UNIT * K < 64 ? UNIT * K : 63)>(); return; } \
+  }
+  FL_WU(1) FL_WU(2) FL_WU(3) FL_WU(4) FL_WU(5) FL_WU(6) FL_WU(7) FL_WU(8)
+#undef FL_WU
   wait_vm<0>();
 }
 

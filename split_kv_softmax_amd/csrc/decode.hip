@@ -115,32 +115,46 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
   // blocks of this wave: tokens n_lo + 32*(wave + NWV*j)
   const int span = n_hi - n_lo - BLK * wave;
   const int nb = span > 0 ? (span + BLK * NWV - 1) / (BLK * NWV) : 0;
-  auto issue = [&](int j) {
+  // this lane's 16-byte piece of each load: byte offset within a full block,
+  // and within row 0 (rows past the run re-read row 0; results not stored)
+  uint32_t voff[NI], voff0[NI];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int byte = ii * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    const int ch = pc ^ row_swz(D, r);
+    voff[ii] = r * ROWB + ch * 16;
+    voff0[ii] = ch * 16;
+  }
+  auto issue = [&](int j, int stage) {
     const int n0 = n_lo + BLK * (wave + NWV * j);
-    const uint32_t st = myring_lds + (j % S) * BB;
+    const uint32_t st = myring_lds + stage * BB;
+    const uint16_t* xb = Xg + (int64_t)n0 * D;
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
-      const int byte = ii * 1024 + lane * 16;
-      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
-      const int ch = pc ^ row_swz(D, r);
-      const int rr = n0 + r < n_hi ? r : 0;   // rows past the run re-read row 0 (results not stored)
-      dma16(Xg + (int64_t)(n0 + rr) * D + 8 * ch, st + ii * 1024);
+      const int r = (ii * 1024) / ROWB + lane / (ROWB / 16);
+      dma16_off(xb, n0 + r < n_hi ? voff[ii] : voff0[ii], st + ii * 1024);
     }
   };
 #pragma unroll
   for (int j = 0; j < S - 1; ++j)
-    if (j < nb) issue(j);
+    if (j < nb) issue(j, j);
 
   const int swx = row_swz(D, l32);
-  for (int j = 0; j < nb; ++j) {
+  // S blocks per trip, so that each block's ring stage is a compile-time constant
+  for (int j0 = 0; j0 < nb; j0 += S)
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    const int j = j0 + st;
+    if (j >= nb) break;
     const int lb = min(S - 2, nb - 1 - j);          // blocks loaded after block j
     const int ls = min(j, S - 1);                   // blocks stored after block j was loaded
     wait_block<NI, ST, S>(lb > 0 ? lb : 0, ls);
-    if (j + S - 1 < nb) issue(j + S - 1);
+    if (j + S - 1 < nb) issue(j + S - 1, (st + S - 1) % S);
     const int n0 = n_lo + BLK * (wave + NWV * j);
     const int n = n0 + l32;
     const bool inb = n < n_hi;
-    const uint8_t* xs = myring + (j % S) * BB + l32 * ROWB;
+    const uint8_t* xs = myring + st * BB + l32 * ROWB;
     bf16x8_t xop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -155,14 +169,21 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
         t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 16 * ks)),
                              xop[ks], t[mb]);
     }
-    float mx = t[0][0];
+    // the token's maximum over its M scores: independent chains of 3-input maxima
+    float mc[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      float x = fmax3(t[mb][0], t[mb][1], t[mb][2]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, t[mb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      for (int r = 3; r < 15; r += 2) x = fmax3(x, t[mb][r], t[mb][r + 1]);
+      mc[mb] = fmax2(x, t[mb][15]);
+    }
+    float mx = mc[0];
+#pragma unroll
+    for (int mb = 1; mb < MB; ++mb) mx = fmax2(mx, mc[mb]);
+    mx = fmax2(mx, __shfl_xor(mx, 32, 64));
     const float nmc = -mx * c2;
-    float lsum = 0.f;
+    // weights rounded to bf16 for the value product
     bf16x8_t pk[MS];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -170,44 +191,52 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       for (int g = 0; g < 2; ++g) {
         float p[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          p[jj] = fast_exp2(__builtin_fmaf(t[mb][8 * g + jj], c2, nmc));
-          lsum += p[jj];
-        }
-        u32x4_t w;
-        w[0] = pack_bf16x2(p[0], p[1]);
-        w[1] = pack_bf16x2(p[2], p[3]);
-        w[2] = pack_bf16x2(p[4], p[5]);
-        w[3] = pack_bf16x2(p[6], p[7]);
+        for (int jj = 0; jj < 8; ++jj) p[jj] = fast_exp2(__builtin_fmaf(t[mb][8 * g + jj], c2, nmc));
+        const u32x4_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                           pack_bf16x2(p[6], p[7])};
         pk[2 * mb + g] = __builtin_bit_cast(bf16x8_t, w);
       }
-    lsum += __shfl_xor(lsum, 32, 64);
+    // the token's sum of the same rounded weights on the matrix cores: ones x P
+    // leaves it in every register of both lane halves
+    f32x16_t lacc = f32x16_t{};
+    {
+      const bf16x8_t ones =
+          __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+      for (int ks = 0; ks < MS; ++ks) lacc = mfma32x32x16(ones, pk[ks], lacc);
+    }
+    const float lsum = lacc[0];
     f32x16_t y[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       y[db] = f32x16_t{};
-      const uint16_t* zrow = &Zt[(32 * db + l32) * ZLD + 8 * hh];
+      // Z^T rows permuted so that register group g of lane half hh holds the 8
+      // consecutive head dims 32*db + 16*g + 8*hh .. +7
+      const uint16_t* zrow = &Zt[(32 * db + swap23(l32)) * ZLD + 8 * hh];
 #pragma unroll
       for (int ks = 0; ks < MS; ++ks)
         y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)),
                              pk[ks], y[db]);
     }
     // Y block out through its own (consumed) ring stage: each lane writes its
-    // token's head dims as 8-byte pieces, then whole 128-byte rows leave with
-    // 16-byte stores.  Buffer stores drop the rows past the run, so every block
-    // issues the same ST stores (the ring's wait counts rely on that).
+    // token's head dims as 16-byte pieces, then whole rows leave with 16-byte
+    // stores.  Buffer stores drop the rows past the run, so every block issues
+    // the same ST stores (the ring's wait counts rely on that).
     const bool keep = inb && tmask[inb ? n - n_lo : 0] != 0;
     const float inv = 1.f / lsum;
-    uint8_t* stg = myring + (j % S) * BB;
+    uint8_t* stg = myring + st * BB;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t w0 = pack_bf16x2(y[db][4 * q] * inv, y[db][4 * q + 1] * inv);
-        const uint32_t w1 = pack_bf16x2(y[db][4 * q + 2] * inv, y[db][4 * q + 3] * inv);
-        const u32x2_t w = {keep ? w0 : 0u, keep ? w1 : 0u};
-        const int pc = (4 * db + q) ^ swx;
-        *reinterpret_cast<u32x2_t*>(stg + l32 * ROWB + pc * 16 + 8 * hh) = w;
+      for (int g = 0; g < 2; ++g) {
+        u32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t v = pack_bf16x2(y[db][8 * g + 2 * e] * inv, y[db][8 * g + 2 * e + 1] * inv);
+          w[e] = keep ? v : 0u;
+        }
+        const int pc = (4 * db + 2 * g + hh) ^ swx;
+        st16(stg + l32 * ROWB + pc * 16, w);
       }
     const int valid_rows = min(BLK, n_hi - n0);
     const __amdgpu_buffer_rsrc_t yr =
@@ -217,7 +246,8 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       const int byte = ii * 1024 + lane * 16;
       const int r = byte / ROWB, pc = (byte % ROWB) / 16;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + byte);
-      __builtin_amdgcn_raw_buffer_store_b128(v, yr, r * ROWB + ((pc ^ row_swz(D, r)) * 16), 0, 0);
+      // non-temporal: the output rows are not read again by this path
+      __builtin_amdgcn_raw_buffer_store_b128(v, yr, r * ROWB + ((pc ^ row_swz(D, r)) * 16), 0, kCachePolicyNT);
     }
   }
 }

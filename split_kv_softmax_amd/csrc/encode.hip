@@ -34,7 +34,7 @@ namespace flare {
 // tile.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled by
 // row so that the operand reads of a wave spread over the LDS banks.
 // ---------------------------------------------------------------------------
-template <int D, int NW, int S, int G>
+template <int D, int NW, int S, int G, int L, bool RS>
 __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeArgs a) {
   constexpr int TILE = 64;
   constexpr int ROWB = 2 * D;              // bytes per row
@@ -95,20 +95,34 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
     return bits;
   };
   uint8_t* myring = smem + grp * (S * STAGE);
-  auto issue = [&](int u) {
+  const uint32_t ring_lds = lds_addr(myring);
+  // this lane's 16-byte piece of each of its loads: byte offset within a full
+  // tile, and within row 0 (rows past the chunk re-read row 0: in bounds,
+  // never used as valid)
+  constexpr int NJ = NI / NW;
+  uint32_t voff[NJ], voff0[NJ];
+  int vrow[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int ii = wave + NW * j;
+    const int byte = ii * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    const int ch = pc ^ kv_swz<D>(r);
+    vrow[j] = r;
+    voff[j] = r * ROWB + ch * 16;
+    voff0[j] = ch * 16;
+  }
+  // K rows of local tile u go to K slot u % S, V rows to V slot u % S (the
+  // second half of the stage).  Rows past the chunk re-read row 0.
+  auto issue_half = [&](int u, int slot, bool is_v) {
     const int t0 = t_begin + (grp + G * u) * TILE;
     const int nrows = t_end - t0;
-    const uint32_t kst = lds_addr(myring) + (u % S) * STAGE;
+    const uint16_t* base = (is_v ? Vg : Kg) + (int64_t)t0 * D;
+    const uint32_t dst = ring_lds + slot * STAGE + (is_v ? TB : 0);
 #pragma unroll
-    for (int j = 0; j < NI / NW; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int ii = wave + NW * j;
-      const int byte = ii * 1024 + lane * 16;
-      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
-      const int ch = pc ^ kv_swz<D>(r);
-      const int rr = r < nrows ? r : 0;    // rows past the chunk re-read row 0 (in bounds, zeroed later)
-      const int64_t off = (int64_t)(t0 + rr) * D + 8 * ch;
-      dma16(Kg + off, kst + ii * 1024);
-      dma16(Vg + off, kst + TB + ii * 1024);
+      dma16_off(base, vrow[j] < nrows ? voff[j] : voff0[j], dst + ii * 1024);
     }
   };
 
@@ -116,143 +130,203 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16_t{};
   float m_run = kNegInf;   // reference maximum (raw dot products) of row 32w + l32
-  float l_run = 0.f;       // this lane half's share of the running sum
+  // running row sum of the weights.  RS: on the matrix cores, ones x P^T puts
+  // the row's sum of the bf16-rounded weights in every register of both lane
+  // halves; else on the vector ALUs, each lane half summing its own tokens'
+  // float32 weights.
+  f32x16_t lacc = f32x16_t{};
+  float l_run = 0.f;
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const float c2 = a.scale_log2;
 
-  // ring[k] = validity bits of this group's local tile u + k
-  uint64_t ring[S];
+  // With lead L = 1 the loop is software-pipelined: round u computes the
+  // scores of tile u+1 on the matrix cores while the vector ALUs turn the
+  // scores of tile u into weights, then adds tile u's weighted values.  Round
+  // u needs K(u+L) and V(u): that pair is "batch u", so the K ring runs L
+  // tiles ahead of the V ring.  (L = 0: scores and weights of a tile in the
+  // same round, for shapes whose registers cannot hold two score tiles.)
+  // vb[k] = validity bits of local tile u + k (k = 0..S-1+L); nb[k] = number
+  // of this wave's loads in batch u + k (0, NJ or 2 NJ).
+  uint64_t vb[S + L];
 #pragma unroll
-  for (int k = 0; k < S; ++k) ring[k] = 0ull;
+  for (int k = 0; k < S + L; ++k) vb[k] = tile_bits(grp, k);
+  int nb[S];
+  if (L == 1 && vb[0]) issue_half(0, 0, false);        // K(0) alone, before batch 0
 #pragma unroll
   for (int k = 0; k < S - 1; ++k) {
-    ring[k] = tile_bits(grp, k);
-    if (ring[k]) issue(k);
+    nb[k] = 0;
+    if (vb[k + L]) { issue_half(k + L, (k + L) % S, false); nb[k] += NJ; }
+    if (vb[k]) { issue_half(k, k % S, true); nb[k] += NJ; }
   }
-
-  // swizzle of the K rows this lane reads: row 32*b2 + swap23(l32) has
-  // swap23(row) = 32*b2 + l32, so it is the same for both blocks
-  const int swk = D == 64 ? ((l32 >> 1) & 7) : (l32 & 15);
-  for (int u = 0; u < nrounds; ++u) {
-    int later = 0;
+  nb[S - 1] = 0;
+  // the scores of tile 0
+  const int swk = kv_swz<D>(swap23(l32));             // rows 32*b2 + swap23(l32)
+  auto scores = [&](const uint8_t* kst, f32x16_t* sc) {
 #pragma unroll
-    for (int k = 1; k < S - 1; ++k) later += ring[k] != 0ull;
-    wait_tiles<OPS, S>(later);
+    for (int b2 = 0; b2 < 2; ++b2) {
+      sc[b2] = f32x16_t{};
+      const uint8_t* krow = kst + (32 * b2 + swap23(l32)) * ROWB;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = (2 * ks + hh) ^ swk;
+        sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16)),
+                              qop[ks], sc[b2]);
+      }
+    }
+  };
+  f32x16_t scn[2];                                     // scores of the next tile (L = 1)
+  if constexpr (L == 1) {
+    int pend = 0;
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k) pend += nb[k];
+    wait_units<NJ, 2 * (S - 1)>(pend / NJ);
     barrier_lds();
-    // every wave has finished round u-1, so its stages may be refilled
-    ring[S - 1] = tile_bits(grp, u + S - 1);
-    if (ring[S - 1]) issue(u + S - 1);
-    const uint64_t bits = ring[0];
-    bool partial = false;     // is any group's tile of this round partially valid?
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint64_t bg = g == grp ? bits : tile_bits(g, u);
-      partial |= (bg != 0ull && bg != ~0ull);
-    }
-    uint8_t* kst = myring + (u % S) * STAGE;
-    uint8_t* vst = kst + TB;
-    if (partial) {
-      // padding and rows past the chunk: zero their V rows so P = 0 never meets NaN
-      if (bits != ~0ull && bits != 0ull) {
-        for (int f = tid - grp * 64 * NW; f < TILE * (ROWB / 16); f += 64 * NW) {
-          const int r = f / (ROWB / 16), pc = f % (ROWB / 16);
-          if (!((bits >> r) & 1ull)) st16(vst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
-        }
-      }
-      barrier_lds();
-    }
-    if (bits) {
-      // ---- scores S^T for the two 32-token blocks
-      f32x16_t sc[2];
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        sc[b2] = f32x16_t{};
-        const uint8_t* krow = kst + (32 * b2 + swap23(l32)) * ROWB;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch = (2 * ks + hh) ^ swk;
-          sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16)),
-                                qop[ks], sc[b2]);
-        }
-      }
-      // register r of lane half hh in block b2 holds token 32*b2 + 16*(r/8) + 8*hh + r%8
-      if (bits != ~0ull) {
-        const uint64_t lb = bits >> (8 * hh);
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int tk = 32 * b2 + 16 * (r >> 3) + (r & 7);
-            if (!((lb >> tk) & 1ull)) sc[b2][r] = kNegInf;
-          }
-      }
-      float mx = sc[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[1][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Lazy reference: the subtracted maximum only moves when this tile's
-      // maximum exceeds it by more than 2^kLazy in the exponent; the constant
-      // cancels in O and L, and every weight stays below 2^kLazy.
-      constexpr float kLazy = 8.f;
-      const bool grow = m_run == kNegInf ? (mx != kNegInf) : ((mx - m_run) * c2 > kLazy);
-      if (__ballot(grow)) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = grow ? fast_exp2((m_run - m_new) * c2) : 1.f;   // 0 when m_run = -inf
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) o[i] *= alpha;
-        m_run = m_new;
-      }
-      const float nmc = -((m_run == kNegInf) ? 0.f : m_run) * c2;
-      bf16x8_t pk[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(__builtin_fmaf(sc[b2][8 * g + j], c2, nmc));
-            lsum += p[j];
-          }
-          u32x4_t w;
-          w[0] = pack_bf16x2(p[0], p[1]);
-          w[1] = pack_bf16x2(p[2], p[3]);
-          w[2] = pack_bf16x2(p[4], p[5]);
-          w[3] = pack_bf16x2(p[6], p[7]);
-          pk[2 * b2 + g] = __builtin_bit_cast(bf16x8_t, w);
-        }
-      l_run += lsum;
-      // ---- O^T += V^T P^T ; k-step ks covers tokens 16ks .. 16ks+15.
-      // Transposing reads: in each 16-lane group lane i points at token row
-      // (i/4) of a 4-token block and 4 head dims starting at 4*(i%4); it gets
-      // back the 4 tokens of head dim i of the group.
-      const int lg = lane >> 4, li = lane & 15;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
-        const int chl = d0 >> 3, half = (d0 & 7) * 2;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          u32x2_t part[2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int n = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
-            const uint8_t* src = vst + n * ROWB + ((chl ^ kv_swz<D>(n)) * 16) + half;
-            part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
-          }
-          const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
-          o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pk[ks], o[db]);
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < S - 1; ++k) ring[k] = ring[k + 1];
+    if (vb[0]) scores(myring, scn);
   }
 
-  float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const int lg = lane >> 4, li = lane & 15;
+  // S rounds per trip so that each round's ring slots are compile-time constants
+  for (int u0 = 0; u0 < nrounds; u0 += S) {
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      const int u = u0 + st;
+      if (u < nrounds) {
+        // batch u = {K(u+L), V(u)} complete for this wave; batches u+1 .. u+S-2 may be in flight
+        int pend = 0;
+#pragma unroll
+        for (int k = 1; k < S - 1; ++k) pend += nb[k];
+        wait_units<NJ, 2 * (S - 2)>(pend / NJ);
+        barrier_lds();
+        // every wave is past round u-1: K slot (u-1+L) % S (held K(u-1+L)) and
+        // V slot (u-1) % S (held V(u-1)) are free for batch u+S-1
+        vb[S - 1 + L] = tile_bits(grp, u + S - 1 + L);
+        nb[S - 1] = 0;
+        if (vb[S - 1 + L]) { issue_half(u + S - 1 + L, (st + S - 1 + L) % S, false); nb[S - 1] += NJ; }
+        if (vb[S - 1]) { issue_half(u + S - 1, (st + S - 1) % S, true); nb[S - 1] += NJ; }
+        const uint64_t bits = vb[0];
+        bool partial = false;     // is any group's tile of this round partially valid?
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint64_t bg = g == grp ? bits : tile_bits(g, u);
+          partial |= (bg != 0ull && bg != ~0ull);
+        }
+        uint8_t* vst = myring + st * STAGE + TB;
+        if (partial) {
+          // padding and rows past the chunk: zero their V rows so P = 0 never meets NaN
+          if (bits != ~0ull && bits != 0ull) {
+            for (int f = tid - grp * 64 * NW; f < TILE * (ROWB / 16); f += 64 * NW) {
+              const int r = f / (ROWB / 16), pc = f % (ROWB / 16);
+              if (!((bits >> r) & 1ull)) st16(vst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
+            }
+          }
+          barrier_lds();
+        }
+        f32x16_t sc[2];
+        // K slot of the next tile (L = 1): its scores are computed in the same
+        // straight-line block as this tile's weights, so the matrix-core work
+        // interleaves with the vector work.  When the next tile has no valid
+        // token the slot holds stale rows; those scores are never used.
+        const uint8_t* knext = myring + ((st + 1) % S) * STAGE;
+        if constexpr (L == 1) {
+          sc[0] = scn[0];
+          sc[1] = scn[1];
+        } else {
+          if (bits) scores(myring + st * STAGE, sc);
+        }
+        if (!bits) {
+          if constexpr (L == 1) scores(knext, scn);
+        } else {
+          // register r of lane half hh in block b2 holds token 32*b2 + 16*(r/8) + 8*hh + r%8
+          if (bits != ~0ull) {
+            const uint64_t lb = bits >> (8 * hh);
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int tk = 32 * b2 + 16 * (r >> 3) + (r & 7);
+                if (!((lb >> tk) & 1ull)) sc[b2][r] = kNegInf;
+              }
+          }
+          // tile maximum: four independent chains of 3-input maxima, then one exchange
+          float mc[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const f32x16_t& v = sc[k >> 1];
+            const int r0 = 8 * (k & 1);
+            float x = fmax3(v[r0], v[r0 + 1], v[r0 + 2]);
+            x = fmax3(x, v[r0 + 3], v[r0 + 4]);
+            x = fmax3(x, v[r0 + 5], v[r0 + 6]);
+            mc[k] = fmax2(x, v[r0 + 7]);
+          }
+          float mx = fmax3(mc[0], mc[1], fmax2(mc[2], mc[3]));
+          mx = fmax2(mx, __shfl_xor(mx, 32, 64));
+          // Lazy reference: the subtracted maximum only moves when this tile's
+          // maximum exceeds it by more than 2^kLazy in the exponent; the constant
+          // cancels in O and L, and every weight stays below 2^kLazy.
+          constexpr float kLazy = 8.f;
+          const bool grow = m_run == kNegInf ? (mx != kNegInf) : ((mx - m_run) * c2 > kLazy);
+          if (__ballot(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? fast_exp2((m_run - m_new) * c2) : 1.f;   // 0 when m_run = -inf
+            if constexpr (RS) lacc *= alpha;
+            else l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) o[i] *= alpha;
+            m_run = m_new;
+          }
+          const float nmc = -((m_run == kNegInf) ? 0.f : m_run) * c2;
+          if constexpr (L == 1) scores(knext, scn);
+          // weights, rounded to bf16 for the value product
+          bf16x8_t pk[4];
+#pragma unroll
+          for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              float p[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sc[b2][8 * g + j], c2, nmc));
+              const u32x4_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                 pack_bf16x2(p[6], p[7])};
+              pk[2 * b2 + g] = __builtin_bit_cast(bf16x8_t, w);
+              if constexpr (!RS) {
+                l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+              }
+            }
+          if constexpr (RS) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) lacc = mfma32x32x16(ones, pk[ks], lacc);
+          }
+          // ---- O^T += V^T P^T ; k-step ks covers tokens 16ks .. 16ks+15.
+          // Transposing reads: in each 16-lane group lane i points at token row
+          // (i/4) of a 4-token block and 4 head dims starting at 4*(i%4); it gets
+          // back the 4 tokens of head dim i of the group.
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+            const int chl = d0 >> 3, half = (d0 & 7) * 2;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              u32x2_t part[2];
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                const int n = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+                const uint8_t* src = vst + n * ROWB + ((chl ^ kv_swz<D>(n)) * 16) + half;
+                part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+              }
+              const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
+              o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pk[ks], o[db]);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < S - 1 + L; ++k) vb[k] = vb[k + 1];
+#pragma unroll
+        for (int k = 0; k < S - 1; ++k) nb[k] = nb[k + 1];
+      }
+    }
+  }
+
+  float l_tot = RS ? lacc[0] : l_run + __shfl_xor(l_run, 32, 64);
   if constexpr (G > 1) {
     // ---- combine the G groups' states in LDS (the rings are idle now):
     // group g's lane writes its reference max, row sum and unnormalised
@@ -319,10 +393,10 @@ bool encode_mfma_supported(int M, int D) {
   return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128 || M == 256);
 }
 
-template <int D, int NW, int S, int G>
+template <int D, int NW, int S, int G, int L = 0, bool RS = true>
 static hipError_t launch_mfma_t(const EncodeArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
-  hipLaunchKernelGGL((encode_mfma_kernel<D, NW, S, G>), dim3((unsigned)grid), dim3(64 * NW * G), 0, s, a);
+  hipLaunchKernelGGL((encode_mfma_kernel<D, NW, S, G, L, RS>), dim3((unsigned)grid), dim3(64 * NW * G), 0, s, a);
   return hipGetLastError();
 }
 
@@ -336,33 +410,53 @@ int encode_mfma_groups(int M, int D) {
 }
 
 int encode_mfma_stages(int M, int D) {
-  // LDS ring: D=64 stages are 16 KB, D=128 stages 32 KB.  Three 16-KB stages
-  // let three 4-wave groups (or workgroups) share a CU when registers allow.
+  // LDS ring: D=64 stages are 16 KB, D=128 stages 32 KB.  Within 160 KB per
+  // CU: three groups of three stages, two groups of up to five, or one ring
+  // of three or four stages per workgroup.
   const char* e = getenv("FLARE_ENCODE_STAGES");
-  if (D == 64 && e && (atoi(e) == 3 || atoi(e) == 4) && encode_mfma_groups(M, D) == 1) return atoi(e);
-  if (D == 64) return 3;
+  const int g = encode_mfma_groups(M, D);
+  if (D == 64 && e) {
+    const int v = atoi(e);
+    if (g == 1 && (v == 3 || v == 4)) return v;
+    if (g == 2 && (v == 3 || v == 4 || v == 5)) return v;
+  }
+  if (D == 64) return g == 2 ? 4 : 3;
   return (M >= 128) ? 4 : 3;
 }
 
 int encode_mfma_per_cu(int M, int D) {
   // workgroups of the chosen variant that fit on one CU (LDS and registers)
-  if (D == 64) return encode_mfma_groups(M, D) > 1 ? 1 : 3;
+  if (D == 64) return encode_mfma_groups(M, D) > 1 ? 1 : (encode_mfma_stages(M, D) == 3 ? 3 : 2);
   return M >= 128 ? 1 : 2;
+}
+
+// Software-pipelined variant (scores of the next tile during this tile's
+// weights) for head dim 64: a tuning option, chosen with FLARE_ENCODE_PIPE.
+template <int NW, int S, int G, bool RS = true>
+static hipError_t launch_d64(const EncodeArgs& a, hipStream_t s, bool pipe) {
+  return pipe ? launch_mfma_t<64, NW, S, G, 1, RS>(a, s) : launch_mfma_t<64, NW, S, G, 0>(a, s);
 }
 
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
   if (a.D == 64) {
     const bool s3 = encode_mfma_stages(a.M, a.D) == 3;
+    const bool pipe = getenv("FLARE_ENCODE_PIPE") != nullptr;
     switch (a.M) {
-      case 32: return s3 ? launch_mfma_t<64, 1, 3, 1>(a, s) : launch_mfma_t<64, 1, 4, 1>(a, s);
-      case 64: return s3 ? launch_mfma_t<64, 2, 3, 1>(a, s) : launch_mfma_t<64, 2, 4, 1>(a, s);
+      case 32: return s3 ? launch_d64<1, 3, 1>(a, s, pipe) : launch_d64<1, 4, 1>(a, s, pipe);
+      case 64: return s3 ? launch_d64<2, 3, 1>(a, s, pipe) : launch_d64<2, 4, 1>(a, s, pipe);
       case 128:
         switch (encode_mfma_groups(a.M, a.D)) {
-          case 3: return launch_mfma_t<64, 4, 3, 3>(a, s);
-          case 2: return launch_mfma_t<64, 4, 3, 2>(a, s);
-          default: return s3 ? launch_mfma_t<64, 4, 3, 1>(a, s) : launch_mfma_t<64, 4, 4, 1>(a, s);
+          case 3:   // registers: two score tiles only with the row sum on the vector ALUs
+            return launch_d64<4, 3, 3, false>(a, s, pipe);
+          case 2:
+            switch (encode_mfma_stages(a.M, a.D)) {
+              case 5: return launch_d64<4, 5, 2>(a, s, pipe);
+              case 4: return launch_d64<4, 4, 2>(a, s, pipe);
+              default: return launch_d64<4, 3, 2>(a, s, pipe);
+            }
+          default: return s3 ? launch_d64<4, 3, 1>(a, s, pipe) : launch_d64<4, 4, 1>(a, s, pipe);
         }
-      case 256: return s3 ? launch_mfma_t<64, 8, 3, 1>(a, s) : launch_mfma_t<64, 8, 4, 1>(a, s);
+      case 256: return s3 ? launch_d64<8, 3, 1>(a, s, pipe) : launch_d64<8, 4, 1>(a, s, pipe);
     }
   } else if (a.D == 128) {
     switch (a.M) {

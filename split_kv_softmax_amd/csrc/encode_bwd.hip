@@ -250,7 +250,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
     ring[k] = tile_bits(k);
     if (ring[k]) issue(k);
   }
-  const int swk = D == 64 ? ((l32 >> 1) & 7) : (l32 & 15);
+  const int swk = kv_swz<D>(swap23(l32));   // rows 32*b2 + swap23(l32)
   for (int t = 0; t < ntiles; ++t) {
     int later = 0;
 #pragma unroll
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
 // workgroup per (b, h, token chunk); 64-token tiles through a direct-load ring.
 // Phase A (one wave per 32 latent rows, lane = latent row):
 //   S^T = K Q^T, dP^T = V dZ^T, P = exp(s S - L), dS = P (dP - c)
-//   P and dS go to LDS as bf16 [m][token]; with DQ the wave also adds
+//   P and dS go to LDS as bf16 [m][token] (128-byte rows, K/V swizzle); with DQ the wave also adds
 //   K^T dS^T into its query-gradient partial, as the query-gradient kernel does.
 // Phase B (each wave one gradient tensor and a slice of output blocks,
 // lane = token):
@@ -484,8 +484,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       dma16(Vg + off, kst + TB + ii * 1024);
     }
   };
-  // staged gradient rows: 16-byte chunk ch of row n sits at ch ^ (n & (CPR-1))
-  auto out_swz = [](int n) { return n & (CPR - 1); };
+  // staged gradient rows: 16-byte chunk ch of row n sits at ch ^ out_swz(n)
+  auto out_swz = [](int n) { return D == 64 ? kv_swz<64>(n) : (n & 15); };
 
   f32x16_t dq[DQ ? DB : 1];
 #pragma unroll
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
     ring[k] = tile_bits(k);
     if (ring[k]) issue(k);
   }
-  const int swk = D == 64 ? ((l32 >> 1) & 7) : (l32 & 15);
+  const int swk = kv_swz<D>(swap23(l32));   // rows 32*b2 + swap23(l32)
   for (int t = 0; t < ntiles; ++t) {
     int later = 0;
 #pragma unroll
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
                                 pack_bf16x2(pv[6], pv[7])};
             const u32x4_t wd = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
                                 pack_bf16x2(ds[6], ds[7])};
-            const int pc = (4 * b2 + 2 * g + hh) ^ (m & 7);
+            const int pc = (4 * b2 + 2 * g + hh) ^ kv_swz<64>(m);
             st16(pbuf + m * (TILE * 2) + pc * 16, wp);
             st16(dsbuf + m * (TILE * 2) + pc * 16, wd);
             pk[g] = __builtin_bit_cast(bf16x8_t, wd);
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
             for (int q = 0; q < 2; ++q) {
               const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
               const int col = 32 * nb + 16 * (lg & 1) + 4 * (li & 3);
-              const int pc = (col >> 3) ^ (row & 7);
+              const int pc = (col >> 3) ^ kv_swz<64>(row);
               part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                                                         (lds_bf16x4*)(bsrc + row * (TILE * 2) + pc * 16 +
                                                                       (col & 7) * 2)));
