@@ -244,7 +244,7 @@ def roofline_of(w: W.Workload, x, step, ph):
     rows = w.B * w.H * w.N
     if w.kind == "flarepp":
         ms = 0.5 * (ph["encode1"] + ph["encode2"])
-        return ms, 2 * rows * row, "encode_mfma_kernel<64,4,3,3> (flare_encode, one launch)"
+        return ms, 2 * rows * row, "encode_mfma_kernel (flare_encode, one launch; both encoders averaged)"
     if w.kind == "flare":
         if ph["decode"] > ph["encode"]:
             return ph["decode"], 2 * rows * row, "decode_mfma_kernel (flare_decode, one launch)"

@@ -394,6 +394,9 @@ BwdPlan plan_bwd(flare_dtype dt, int B, int H, int N, int M, int D, bool masked)
     int64_t per = std::max<int64_t>(1, (256 + bh - 1) / bh);
     int64_t len = ((N + per - 1) / per + 63) / 64 * 64;
     len = std::max<int64_t>(len, 1024);
+    const int forced = env_int("FLARE_BWD_CHUNK", 0);
+    if (forced >= 64) len = (forced + 63) / 64 * 64;
+    while ((N + len - 1) / len > kMaxChunks) len *= 2;
     for (int64_t t = 0; t < N; t += len) p.bnd.push_back((int32_t)t);
     p.bnd.push_back(N);
     const int nslots = (int)p.bnd.size() - 1;

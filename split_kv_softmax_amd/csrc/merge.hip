@@ -22,7 +22,7 @@ namespace flare {
 
 namespace {
 constexpr int kLevels = 16;   // up to 65536 states per group
-constexpr int kBatch = 8;     // leaves loaded together (all in flight at once)
+constexpr int kBatch = 16;    // leaves loaded together (all in flight at once)
 
 struct St {
   float m, l;
