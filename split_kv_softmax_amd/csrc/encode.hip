@@ -405,7 +405,7 @@ int encode_mfma_groups(int M, int D) {
   // 4-wave groups (12 waves, three 48-KB rings) fill a CU as one workgroup,
   // so a partition needs no split and no fold.
   const char* e = getenv("FLARE_ENCODE_GROUPS");
-  if (e && atoi(e) >= 1 && atoi(e) <= 3 && D == 64 && M == 128) return atoi(e);
+  if (e && atoi(e) >= 1 && atoi(e) <= 3 && D == 64 && (M == 128 || M == 64)) return atoi(e);
   return (D == 64 && M == 128) ? 3 : 1;
 }
 
@@ -443,7 +443,9 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
     const bool pipe = getenv("FLARE_ENCODE_PIPE") != nullptr;
     switch (a.M) {
       case 32: return s3 ? launch_d64<1, 3, 1>(a, s, pipe) : launch_d64<1, 4, 1>(a, s, pipe);
-      case 64: return s3 ? launch_d64<2, 3, 1>(a, s, pipe) : launch_d64<2, 4, 1>(a, s, pipe);
+      case 64:
+        if (encode_mfma_groups(a.M, a.D) == 3) return launch_d64<2, 3, 3>(a, s, pipe);
+        return s3 ? launch_d64<2, 3, 1>(a, s, pipe) : launch_d64<2, 4, 1>(a, s, pipe);
       case 128:
         switch (encode_mfma_groups(a.M, a.D)) {
           case 3:   // registers: two score tiles only with the row sum on the vector ALUs

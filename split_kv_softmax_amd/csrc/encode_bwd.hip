@@ -292,6 +292,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
       }
       // register r of lane half hh in block b2 holds token 32*b2 + 16*(r/8) + 8*hh + r%8
       const uint64_t lb = bits >> (8 * hh);
+      const bool full = bits == ~0ull;   // uniform: no per-element masking for whole tiles
       bf16x8_t pk[4];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
@@ -301,9 +302,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int r = 8 * g + j;
-            const int tk = 32 * b2 + 16 * (r >> 3) + (r & 7);
             const float p = fast_exp2(__builtin_fmaf(sc[b2][r], c2, -nl2));
-            ds[j] = ((lb >> tk) & 1ull) ? p * (dp[b2][r] - cm) : 0.f;
+            ds[j] = p * (dp[b2][r] - cm);
+          }
+          if (!full) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int tk = 32 * b2 + 16 * g + j;
+              if (!((lb >> tk) & 1ull)) ds[j] = 0.f;
+            }
           }
           u32x4_t w;
           w[0] = pack_bf16x2(ds[0], ds[1]);
@@ -534,6 +541,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       // ---- phase A ----
       if (pa) {
         const uint64_t lb = bits >> (8 * hh);
+        const bool full = bits == ~0ull;   // uniform: no per-element masking for whole tiles
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2) {
           f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
@@ -555,11 +563,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int r = 8 * g + j;
-              const int tk = 32 * b2 + 16 * g + j;
-              const bool ok = (lb >> tk) & 1ull;
-              const float p = fast_exp2(__builtin_fmaf(sc[r], c2, -nl2));
-              pv[j] = ok ? p : 0.f;
-              ds[j] = ok ? p * (dp[r] - cm) : 0.f;
+              pv[j] = fast_exp2(__builtin_fmaf(sc[r], c2, -nl2));
+              ds[j] = pv[j] * (dp[r] - cm);
+            }
+            if (!full) {
+              // padding and rows past the chunk: exact zeros (their K/V rows may hold anything)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int tk = 32 * b2 + 16 * g + j;
+                if (!((lb >> tk) & 1ull)) {
+                  pv[j] = 0.f;
+                  ds[j] = 0.f;
+                }
+              }
             }
             const u32x4_t wp = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
                                 pack_bf16x2(pv[6], pv[7])};
