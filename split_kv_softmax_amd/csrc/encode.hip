@@ -161,17 +161,29 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
   nb[S - 1] = 0;
   // the scores of tile 0
   const int swk = kv_swz<D>(swap23(l32));             // rows 32*b2 + swap23(l32)
+  // K operands are read in groups of KG k-steps for both 32-token blocks before
+  // the products that use them, so the LDS latency is paid once per group
+  constexpr int KG = D == 64 ? 4 : 2;
   auto scores = [&](const uint8_t* kst, f32x16_t* sc) {
+    sc[0] = f32x16_t{};
+    sc[1] = f32x16_t{};
+    const uint8_t* krow0 = kst + swap23(l32) * ROWB;
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
-      sc[b2] = f32x16_t{};
-      const uint8_t* krow = kst + (32 * b2 + swap23(l32)) * ROWB;
+    for (int k0 = 0; k0 < KS; k0 += KG) {
+      u32x4_t kop[2][KG];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = (2 * ks + hh) ^ swk;
-        sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16)),
-                              qop[ks], sc[b2]);
-      }
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int k = 0; k < KG; ++k)
+          kop[b2][k] = *reinterpret_cast<const u32x4_t*>(krow0 + 32 * b2 * ROWB + (((2 * (k0 + k) + hh) ^ swk) * 16));
+#pragma unroll
+      for (int k = 0; k < KG; ++k)
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+          sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, kop[b2][k]), qop[k0 + k], sc[b2]);
+      // scheduling: all reads of the group, then its products
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KG, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KG, 0);
     }
   };
   f32x16_t scn[2];                                     // scores of the next tile (L = 1)
@@ -300,22 +312,34 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
           // Transposing reads: in each 16-lane group lane i points at token row
           // (i/4) of a 4-token block and 4 head dims starting at 4*(i%4); it gets
           // back the 4 tokens of head dim i of the group.
+          // (the transposing reads of VK k-steps are issued before their products)
+          constexpr int VK = D == 64 ? 2 : 1;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
-            const int chl = d0 >> 3, half = (d0 & 7) * 2;
+          for (int k0 = 0; k0 < 4; k0 += VK) {
+            u32x2_t part[VK][DB][2];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              u32x2_t part[2];
+            for (int kk = 0; kk < VK; ++kk)
 #pragma unroll
-              for (int q = 0; q < 2; ++q) {
-                const int n = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
-                const uint8_t* src = vst + n * ROWB + ((chl ^ kv_swz<D>(n)) * 16) + half;
-                part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+              for (int db = 0; db < DB; ++db) {
+                const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+                const int chl = d0 >> 3, half = (d0 & 7) * 2;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                  const int n = 16 * (k0 + kk) + 8 * (lg >> 1) + 4 * q + (li >> 2);
+                  const uint8_t* src = vst + n * ROWB + ((chl ^ kv_swz<D>(n)) * 16) + half;
+                  part[kk][db][q] =
+                      __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+                }
               }
-              const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
-              o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pk[ks], o[db]);
-            }
+#pragma unroll
+            for (int kk = 0; kk < VK; ++kk)
+#pragma unroll
+              for (int db = 0; db < DB; ++db) {
+                const u32x4_t av = {part[kk][db][0][0], part[kk][db][0][1], part[kk][db][1][0], part[kk][db][1][1]};
+                o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pk[k0 + kk], o[db]);
+              }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * VK * DB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, VK * DB, 0);
           }
         }
 #pragma unroll
@@ -465,7 +489,9 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
       case 32: return launch_mfma_t<128, 1, 3, 1>(a, s);
       case 64: return launch_mfma_t<128, 2, 3, 1>(a, s);
       case 128: return launch_mfma_t<128, 4, 4, 1>(a, s);
-      case 256: return launch_mfma_t<128, 8, 4, 1>(a, s);
+      case 256:
+        return getenv("FLARE_ENCODE_VSUM") ? launch_mfma_t<128, 8, 4, 1, 0, false>(a, s)
+                                           : launch_mfma_t<128, 8, 4, 1>(a, s);
     }
   }
   return hipErrorInvalidValue;
