@@ -352,3 +352,77 @@ def encode_bwd_local_slice(q, k, v, valid, offsets, scale: float, dZ):
         dk += b_
         dv += c_
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# decode backward and the FLARE++ backward chain (FLARE++ backward paragraph:
+# the decoder's contributions to the replicated latents are summed, the
+# decoder's query-gradient is added to the physical-value encoder's, and the
+# sum is propagated through the query-synthesis encoder with that invocation's
+# own saved output and log-normaliser)
+# ----------------------------------------------------------------------------
+def decode_bwd_slice(xq, klat, z, scale: float, dy, valid=None):
+    """Gradients of <dY, Y> for Y = softmax(s xq klat^T) z, one (batch, head) slice.
+
+    A = softmax over the M latents of T = s xq klat^T; dA = dy z^T; the row
+    term delta = rowsum(A * dA) (= rowsum(dy * y)); dT = A * (dA - delta);
+    dxq = s dT klat, dklat = s dT^T xq, dz = A^T dy.  Masked tokens (their Y is
+    0 by definition) take no part: zero dxq rows, no contribution to dklat, dz.
+    """
+    n, D = xq.shape
+    keep = np.ones(n, dtype=bool) if valid is None else np.asarray(valid).astype(bool)
+    T = float(scale) * (xq @ klat.T)                      # [n, M]
+    A = np.exp(T - T.max(axis=1, keepdims=True))
+    A /= A.sum(axis=1, keepdims=True)
+    dyk = np.where(keep[:, None], dy, 0.0)
+    dA = dyk @ z.T
+    delta = (A * dA).sum(axis=1)
+    dT = A * (dA - delta[:, None])
+    dxq = float(scale) * (dT @ klat)
+    dklat = float(scale) * (dT.T @ xq)
+    dz = A.T @ dyk
+    return dxq, dklat, dz
+
+
+def decode_bwd_ref(Xq, Klat, Z, scale: float, dY, token_mask=None,
+                   slices: Optional[List[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
+    """dXq [B, H, N, D], dKlat [B, H, M, D] (one per batch even when Klat is replicated),
+    dZ [B, H, M, D] of <dY, decode(Xq, Klat, Z)>."""
+    Xq, Klat, Z, dY = f64(Xq), f64(Klat), f64(Z), f64(dY)
+    B, H, N, D = Xq.shape
+    M = Klat.shape[-2]
+    mk = np.ones((B, N), dtype=bool) if token_mask is None else u8(token_mask).astype(bool)
+    out = {"dXq": np.full((B, H, N, D), np.nan), "dKlat": np.full((B, H, M, D), np.nan),
+           "dZ": np.full((B, H, M, D), np.nan)}
+    todo = slices if slices is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in todo:
+        a, k, z = decode_bwd_slice(Xq[b, h], _q_slice(Klat, b, h), Z[b, h], scale, dY[b, h], mk[b])
+        out["dXq"][b, h], out["dKlat"][b, h], out["dZ"][b, h] = a, k, z
+    return out
+
+
+def flarepp_bwd_ref(Qt, Kt, Vt, K, V, offsets, scale: float, dY, round_qx_bf16: bool = False,
+                    slices: Optional[List[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
+    """Gradients of <dY, Y> for the FLARE++ chain of flarepp_ref.
+
+    decoder: (dK_dec, dQX_dec, dZ2) = decode backward at (K, Q(X), Z2);
+    physical-value encoder: (dQX_enc, dK_enc, dV) = encoder backward at (Q(X), K, V)
+    with its own (Z2, L2) and dZ2;  dQX = dQX_dec + dQX_enc;
+    query-synthesis encoder: (dQt, dKt, dVt) = encoder backward at (Qt, Kt, Vt) with
+    its own (Q(X), L1) and dQX.  dK = dK_dec + dK_enc.  With ``round_qx_bf16``
+    the second encoder and the decoder see Q(X) rounded to bfloat16 (as the
+    kernels do) and its gradient passes the rounding unchanged.
+    """
+    f = flarepp_ref(Qt, Kt, Vt, K, V, offsets, scale, round_qx_bf16=round_qx_bf16, slices=slices)
+    QX = f["QX"]
+    QXu = QX
+    if round_qx_bf16:
+        import torch
+        QXu = torch.from_numpy(np.nan_to_num(QX)).to(torch.float32).to(torch.bfloat16).to(
+            torch.float64).numpy()
+    d = decode_bwd_ref(K, QXu, f["Z"], scale, dY, slices=slices)
+    g2 = encode_bwd_ref(QXu, K, V, None, scale, f["Z"], f["L"], d["dZ"], slices=slices)
+    dQX = d["dKlat"] + g2["dQ"]
+    g1 = encode_bwd_ref(Qt, Kt, Vt, None, scale, QX, f["QX_L"], dQX, slices=slices)
+    return {"dQt": g1["dQ"], "dKt": g1["dK"], "dVt": g1["dV"], "dK": d["dXq"] + g2["dK"], "dV": g2["dV"],
+            "dQX": dQX, "dQX_dec": d["dKlat"], "dZ2": d["dZ"], "forward": f}

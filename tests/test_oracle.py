@@ -390,3 +390,79 @@ def test_nan_padding_does_not_leak():
     gb = ref.encode_bwd_ref(Q, K2, V2, mask, 0.3, b["Z"], b["L"], dZ)
     for key in ("dQ", "dK", "dV"):
         assert np.array_equal(ga[key], gb[key])
+
+
+# ------------------------------------------- decode backward and the FLARE++ chain
+def test_decode_backward_matches_torch_autograd():
+    """Decode gradients against torch SDPA autograd in float64 (token mask as zero dY rows)."""
+    rng = np.random.default_rng(21)
+    B, H, N, M, D = 2, 2, 40, 6, 8
+    Xq = rng.standard_normal((B, H, N, D))
+    Kl = rng.standard_normal((H, M, D)) * 1.5
+    Z = rng.standard_normal((B, H, M, D))
+    dY = rng.standard_normal((B, H, N, D))
+    tm = (rng.random((B, N)) > 0.25).astype(np.uint8)
+    s = 0.3
+    g = ref.decode_bwd_ref(Xq, Kl, Z, s, dY, token_mask=tm)
+    tx = torch.tensor(Xq, requires_grad=True)
+    tk = torch.tensor(np.broadcast_to(Kl, (B, H, M, D)).copy(), requires_grad=True)
+    tz = torch.tensor(Z, requires_grad=True)
+    Y = F.scaled_dot_product_attention(tx, tk, tz, scale=s)
+    keep = torch.from_numpy(tm.astype(bool))[:, None, :, None]
+    (Y * torch.from_numpy(dY) * keep).sum().backward()
+    np.testing.assert_allclose(g["dXq"], tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dKlat"], tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dZ"], tz.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.all(g["dXq"][~tm.astype(bool)[:, None, :].repeat(H, 1)] == 0)
+
+
+def test_decode_backward_finite_differences():
+    rng = np.random.default_rng(22)
+    xq, kl, z, dy = (rng.standard_normal(sh) for sh in ((9, 4), (3, 4), (3, 4), (9, 4)))
+    s = 0.7
+
+    def f(x, k, zz):
+        return float((ref.decode_slice(x, k, zz, s) * dy).sum())
+
+    gx, gk, gz = ref.decode_bwd_slice(xq, kl, z, s, dy)
+    h = 1e-6
+    for which, X, G in (("x", xq, gx), ("k", kl, gk), ("z", z, gz)):
+        for idx in ((0, 0), (2, 3), (X.shape[0] - 1, 1)):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            args = {"x": lambda A: (A, kl, z), "k": lambda A: (xq, A, z), "z": lambda A: (xq, kl, A)}[which]
+            fd = (f(*args(Xp)) - f(*args(Xm))) / (2 * h)
+            assert abs(fd - G[idx]) < 1e-7, (which, idx, fd, G[idx])
+
+
+def test_decode_backward_closed_form_at_uniform_weights():
+    """Zero latent keys: every token weighs the M latents equally, so dZ[m] = (1/M) sum_n dY[n]
+    and the token queries get no gradient."""
+    rng = np.random.default_rng(23)
+    xq, dy = rng.standard_normal((11, 5)), rng.standard_normal((11, 5))
+    z = rng.standard_normal((4, 5))
+    gx, gk, gz = ref.decode_bwd_slice(xq, np.zeros((4, 5)), z, 0.5, dy)
+    np.testing.assert_allclose(gz, np.broadcast_to(dy.sum(axis=0) / 4, (4, 5)), rtol=1e-13, atol=1e-14)
+    assert np.all(gx == 0)
+    # each token's score gradient sums to zero over the latents, so dKlat sums to zero over m
+    np.testing.assert_allclose(gk.sum(axis=0), 0.0, atol=1e-12)
+
+
+def test_flarepp_backward_matches_autograd_through_sdpa_chain():
+    """The whole chain's gradients against autograd of Q(X) = SDPA(Qt,Kt,Vt), Z = SDPA(Q(X),K,V),
+    Y = SDPA(K, Q(X), Z) in float64 (partitions do not change the exact result)."""
+    rng = np.random.default_rng(24)
+    B, H, N, M, D = 1, 2, 48, 4, 8
+    Qt = rng.standard_normal((H, M, D))
+    Kt, Vt, K, V, dY = (rng.standard_normal((B, H, N, D)) for _ in range(5))
+    s = 1 / math.sqrt(D)
+    g = ref.flarepp_bwd_ref(Qt, Kt, Vt, K, V, [0, 7, 7, 30, 48], s, dY)
+    tq = torch.tensor(np.broadcast_to(Qt, (B, H, M, D)).copy(), requires_grad=True)
+    tkt, tvt, tk, tv = (torch.tensor(a, requires_grad=True) for a in (Kt, Vt, K, V))
+    QX = F.scaled_dot_product_attention(tq, tkt, tvt, scale=s)
+    Z = F.scaled_dot_product_attention(QX, tk, tv, scale=s)
+    Y = F.scaled_dot_product_attention(tk, QX, Z, scale=s)
+    (Y * torch.from_numpy(dY)).sum().backward()
+    for name, t in (("dQt", tq), ("dKt", tkt), ("dVt", tvt), ("dK", tk), ("dV", tv)):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
