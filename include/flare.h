@@ -147,6 +147,8 @@ size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, i
  * dQ: [B,H,M,D] float, one slice per batch even when Q is replicated (the sum
  * over the batch is the caller's).  dK, dV: [B,H,N,D] in dtype; rows of masked
  * tokens are written as 0.  Rows with L = -inf get zero gradients.
+ * dQ_cast (nullable): dQ also written in dtype (the dZ of the encoder that produced Q, in
+ * the FLARE++ chain).  flags: FLARE_BWD_ACCUMULATE_* below, or 0.
  * Offsets are validated as in flare_encode; workspace must hold
  * flare_encode_bwd_workspace_size() bytes, 16-byte aligned.  For bf16 with
  * D in {64,128} and M in {32,64,128,256} the matrix-core path runs; it needs
@@ -157,7 +159,43 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
                               const void* Q, int64_t q_batch_stride, const void* K, const void* V,
                               int R, const int64_t* offsets, const uint8_t* mask, float scale,
                               const float* Z, const float* L, const void* dZ,
-                              float* dQ, void* dK, void* dV,
+                              float* dQ, void* dK, void* dV, void* dQ_cast, int flags,
+                              void* workspace, size_t workspace_bytes, flare_stream_t stream);
+
+/* flags of flare_encode_bwd (bitwise or).  The FLARE++ backward paragraph adds the
+ * decoder's contributions to the encoder's: with these the encoder backward adds into
+ * gradients that a preceding flare_decode_bwd wrote. */
+#define FLARE_BWD_ACCUMULATE_DQ 1   /* dQ += (instead of dQ =) */
+#define FLARE_BWD_ACCUMULATE_DK 2   /* dK += (instead of dK =); dV is always written */
+
+/* Bytes of device workspace flare_decode_bwd needs (masked != 0 when a token mask
+ * will be passed). */
+size_t flare_decode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D,
+                                       int masked);
+
+/*
+ * flare_decode_bwd -- gradients of sum(dY * Y) for Y = flare_decode(Xq, Klat, Z) ([FLARE++],
+ * FLARE++ backward paragraph: each token's local decoder contributes to the gradients of
+ * the replicated latents, summed over the tokens):
+ *     A[n,m]   = softmax_m(scale Xq[n].Klat[m])      dA[n,m] = dY[n].Z[m]
+ *     delta[n] = sum_m A[n,m] dA[n,m]                dT = A (dA - delta)
+ *     dXq[n,:] = scale sum_m dT[n,m] Klat[m,:]       dKlat[m,:] = scale sum_n dT[n,m] Xq[n,:]
+ *     dZ[m,:]  = sum_n A[n,m] dY[n,:]
+ * Xq, dY, dXq: [B,H,N,D] in dtype.  Klat: [H,M,D] (klat_batch_stride 0) or [B,H,M,D].
+ * Z: [B,H,M,D] float.  dKlat, dZ: [B,H,M,D] float, one slice per batch even when Klat is
+ * replicated.  dZ_cast (nullable): dZ also written in dtype (the dZ a following
+ * flare_encode_bwd takes).  token_mask (nullable, [B,N] uint8): tokens with 0 take no part
+ * (their Y is 0): dXq rows written as 0, no contribution to dKlat or dZ.
+ * All pointers are device pointers owned by the caller; workspace must hold
+ * flare_decode_bwd_workspace_size() bytes, 16-byte aligned.  Shapes as flare_decode
+ * (M <= 256).  For bf16 with D in {64,128} and M in {32,64,128} the matrix-core path runs;
+ * it needs every tensor 16-byte aligned (else FLARE_EINVAL) and sums the latent gradients
+ * over token chunks in a fixed order (bitwise reproducible).
+ */
+flare_status flare_decode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D,
+                              const void* Xq, const void* Klat, int64_t klat_batch_stride,
+                              const float* Z, const uint8_t* token_mask, float scale,
+                              const void* dY, void* dXq, float* dKlat, float* dZ, void* dZ_cast,
                               void* workspace, size_t workspace_bytes, flare_stream_t stream);
 
 /* Message describing the last non-OK status returned on this thread ("" if none). */

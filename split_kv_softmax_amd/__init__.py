@@ -20,9 +20,11 @@ from typing import Dict, Optional, Sequence, Tuple
 
 import torch  # noqa: F401  (loaded first so the library binds to torch's HIP runtime)
 
-__all__ = ["FlareError", "encode", "lse_merge", "decode", "encode_bwd", "flare_forward",
-           "flarepp_forward", "encode_workspace_size", "encode_bwd_workspace_size", "library_path",
-           "scale_for"]
+__all__ = ["FlareError", "encode", "lse_merge", "decode", "encode_bwd", "decode_bwd", "flare_forward",
+           "flarepp_forward", "flarepp_backward", "encode_workspace_size", "encode_bwd_workspace_size",
+           "decode_bwd_workspace_size", "library_path", "scale_for", "ACCUMULATE_DQ", "ACCUMULATE_DK"]
+
+ACCUMULATE_DQ, ACCUMULATE_DK = 1, 2   # flags of encode_bwd (FLARE_BWD_ACCUMULATE_*)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libflare.so")
@@ -66,8 +68,13 @@ def _load():
     lib.flare_encode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64, i32]
     lib.flare_encode_bwd_workspace_size.restype = sz
     lib.flare_encode_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp,
-                                     vp, vp, vp, vp, vp, vp, sz, vp]
+                                     vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.flare_encode_bwd.restype = i32
+    lib.flare_decode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.flare_decode_bwd_workspace_size.restype = sz
+    lib.flare_decode_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp, vp, vp, vp,
+                                     vp, sz, vp]
+    lib.flare_decode_bwd.restype = i32
     lib.flare_last_error.restype = ctypes.c_char_p
     lib.flare_version.restype = ctypes.c_char_p
     _lib = lib
@@ -271,8 +278,13 @@ def encode_bwd_workspace_size(dtype: torch.dtype, B, H, N, M, D, offsets, masked
                                                        _offsets(offsets), int(masked)))
 
 
-def encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dQ=None, dK=None, dV=None):
-    """Encoder gradients with the global statistics -> (dQ [B,H,M,D] f32, dK, dV)."""
+def encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dQ=None, dK=None, dV=None, dQ_cast=None,
+               flags: int = 0):
+    """Encoder gradients with the global statistics -> (dQ [B,H,M,D] f32, dK, dV).
+
+    ``flags`` (ACCUMULATE_DQ / ACCUMULATE_DK) add into the given dQ / dK instead of
+    overwriting them; ``dQ_cast`` (a [B,H,M,D] tensor in the input dtype) also receives dQ.
+    """
     lib = _load()
     _kv_check(K, V, Q)
     B, H, N, D = K.shape
@@ -297,6 +309,10 @@ def encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dQ=None, dK=None, dV=Non
         raise ValueError("dQ must be float32 [B,H,M,D]")
     if dK.shape != K.shape or dV.shape != V.shape or dK.dtype != K.dtype or dV.dtype != K.dtype:
         raise ValueError("dK / dV must match K / V")
+    if dQ_cast is not None:
+        _dev(dQ_cast, "dQ_cast")
+        if tuple(dQ_cast.shape) != (B, H, M, D) or dQ_cast.dtype != K.dtype:
+            raise ValueError("dQ_cast must be [B,H,M,D] in the input dtype")
     offs = _offsets(offsets)
     code = _dtype_code(K)
     nbytes = int(lib.flare_encode_bwd_workspace_size(code, B, H, N, M, D, R, offs, int(mask is not None)))
@@ -304,8 +320,55 @@ def encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dQ=None, dK=None, dV=Non
     with torch.cuda.device(dev):
         _check(lib.flare_encode_bwd(code, B, H, N, M, D, _ptr(Q), qbs, _ptr(K), _ptr(V), R, offs, _ptr(mask),
                                     float(scale), _ptr(Z), _ptr(L), _ptr(dZ), _ptr(dQ), _ptr(dK), _ptr(dV),
-                                    _ptr(ws), nbytes, _stream()))
+                                    _ptr(dQ_cast), int(flags), _ptr(ws), nbytes, _stream()))
     return dQ, dK, dV
+
+
+def decode_bwd_workspace_size(dtype: torch.dtype, B, H, N, M, D, masked: bool = False) -> int:
+    code = BF16 if dtype == torch.bfloat16 else F32
+    return int(_load().flare_decode_bwd_workspace_size(code, B, H, N, M, D, int(masked)))
+
+
+def decode_bwd(Xq, Klat, Z, scale, dY, token_mask=None, dXq=None, dKlat=None, dZ=None, dZ_cast=None):
+    """Decode gradients -> (dXq [B,H,N,D] in the input dtype, dKlat [B,H,M,D] f32, dZ [B,H,M,D] f32)."""
+    lib = _load()
+    for t, nm in ((Xq, "Xq"), (Klat, "Klat"), (Z, "Z"), (dY, "dY")):
+        _dev(t, nm)
+    if Xq.dim() != 4:
+        raise ValueError("Xq must be [B,H,N,D]")
+    B, H, N, D = Xq.shape
+    if Klat.dtype != Xq.dtype or dY.dtype != Xq.dtype:
+        raise TypeError("Xq, Klat and dY must share one dtype")
+    if dY.shape != Xq.shape:
+        raise ValueError("dY must match Xq")
+    M, kbs = _q_layout(Klat, B, H, D)
+    if tuple(Z.shape) != (B, H, M, D) or Z.dtype != torch.float32:
+        raise ValueError(f"Z must be float32 [B,H,M,D] = ({B},{H},{M},{D})")
+    token_mask = _mask_check(token_mask, B, N, Xq.device, "token_mask")
+    if scale is None:
+        scale = scale_for(D)
+    dev = Xq.device
+    dXq = torch.empty_like(Xq) if dXq is None else dXq
+    dKlat = torch.empty((B, H, M, D), dtype=torch.float32, device=dev) if dKlat is None else dKlat
+    dZ = torch.empty((B, H, M, D), dtype=torch.float32, device=dev) if dZ is None else dZ
+    if dXq.shape != Xq.shape or dXq.dtype != Xq.dtype:
+        raise ValueError("dXq must match Xq")
+    for t, nm in ((dKlat, "dKlat"), (dZ, "dZ")):
+        _dev(t, nm)
+        if tuple(t.shape) != (B, H, M, D) or t.dtype != torch.float32:
+            raise ValueError(f"{nm} must be float32 [B,H,M,D]")
+    if dZ_cast is not None:
+        _dev(dZ_cast, "dZ_cast")
+        if tuple(dZ_cast.shape) != (B, H, M, D) or dZ_cast.dtype != Xq.dtype:
+            raise ValueError("dZ_cast must be [B,H,M,D] in the input dtype")
+    code = _dtype_code(Xq)
+    nbytes = int(lib.flare_decode_bwd_workspace_size(code, B, H, N, M, D, int(token_mask is not None)))
+    ws = _workspace(nbytes, dev)
+    with torch.cuda.device(dev):
+        _check(lib.flare_decode_bwd(code, B, H, N, M, D, _ptr(Xq), _ptr(Klat), kbs, _ptr(Z), _ptr(token_mask),
+                                    float(scale), _ptr(dY), _ptr(dXq), _ptr(dKlat), _ptr(dZ), _ptr(dZ_cast),
+                                    _ptr(ws), nbytes, _stream()))
+    return dXq, dKlat, dZ
 
 
 def flare_forward(Q, K, V, offsets, mask=None, scale=None, token_mask=None):
@@ -314,6 +377,27 @@ def flare_forward(Q, K, V, offsets, mask=None, scale=None, token_mask=None):
     Z, L, _ = lse_merge(O_part, L_part)
     Y = decode(K, Q, Z, scale, token_mask)
     return {"O_part": O_part, "L_part": L_part, "Z": Z, "L": L, "Y": Y}
+
+
+def flarepp_backward(fwd, Qt, Kt, Vt, K, V, offsets, dY, scale=None):
+    """Gradients of sum(dY * Y) for the FLARE++ chain, from the saved forward ``fwd``
+    (the dict flarepp_forward returns): three C-ABI calls.
+
+    decoder backward at (K, Q(X), Z) -> dK, dQ(X) (decoder part), dZ (also in the
+    input dtype); physical-value encoder backward with its own (Z, L), adding into
+    dQ(X) and dK and writing dV, and writing dQ(X) in the input dtype; query-synthesis
+    encoder backward with its own (Q(X), L) and that dQ(X) -> dQt, dKt, dVt.
+    Q(X) enters the second encoder and the decoder rounded to the input dtype; its
+    gradient passes the rounding unchanged.
+    """
+    QXin = fwd["QX_in"]
+    dZc = torch.empty_like(fwd["Z"], dtype=K.dtype)
+    dK, dQX, _ = decode_bwd(K, QXin, fwd["Z"], scale, dY, dZ_cast=dZc)
+    dQXc = torch.empty_like(dQX, dtype=K.dtype)
+    _, dK, dV = encode_bwd(QXin, K, V, offsets, None, scale, fwd["Z"], fwd["L"], dZc, dQ=dQX, dK=dK,
+                           dQ_cast=dQXc, flags=ACCUMULATE_DQ | ACCUMULATE_DK)
+    dQt, dKt, dVt = encode_bwd(Qt, Kt, Vt, offsets, None, scale, fwd["QX"], fwd["QX_L"], dQXc)
+    return {"dQt": dQt, "dKt": dKt, "dVt": dVt, "dK": dK, "dV": dV, "dQX": dQX}
 
 
 def flarepp_forward(Qt, Kt, Vt, K, V, offsets, scale=None):

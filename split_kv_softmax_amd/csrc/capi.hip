@@ -409,6 +409,46 @@ BwdPlan plan_bwd(flare_dtype dt, int B, int H, int N, int M, int D, bool masked)
   p.ws_bytes = p.c_bytes + p.mw_bytes + p.dq_bytes;
   return p;
 }
+
+// Decode backward plan: per-token statistics (log2-normaliser, delta), the
+// mask's validity words and per-chunk partial latent gradients (matrix-core
+// path).
+struct DecBwdPlan {
+  bool mfma = false;
+  std::vector<int32_t> bnd;   // latent-side chunk boundaries over [0, N)
+  int tokens_per_block = 0;   // token side
+  int64_t stats_stride = 0, mw_stride = 0;
+  size_t stats_bytes = 0, mw_bytes = 0, part_bytes = 0, ws_bytes = 0;
+};
+
+DecBwdPlan plan_decode_bwd(flare_dtype dt, int B, int H, int N, int M, int D, bool masked) {
+  DecBwdPlan p;
+  p.mfma = dt == FLARE_BF16 && decode_bwd_mfma_supported(M, D) && N > 0;
+  p.stats_stride = ((int64_t)N + 63) / 64 * 64;
+  p.stats_bytes = align256((size_t)B * H * p.stats_stride * sizeof(float));
+  if (p.mfma) {
+    const int64_t bh = std::max<int64_t>(1, (int64_t)B * H);
+    // token side: whole blocks of (waves x 32) tokens, about two workgroups per CU
+    const int round = 32 * decode_bwd_waves(D);
+    const int64_t per_slice = std::max<int64_t>(1, 512 / bh);
+    int tpb = (int)std::min<int64_t>(8192, (N + per_slice - 1) / per_slice);
+    p.tokens_per_block = std::min(8192, std::max(round, round_up(tpb, round)));
+    // latent side: about two workgroups per CU, chunks of whole tiles
+    int64_t per = std::max<int64_t>(1, (512 + bh - 1) / bh);
+    int64_t len = std::max<int64_t>(1024, ((N + per - 1) / per + 63) / 64 * 64);
+    while ((N + len - 1) / len > kMaxChunks) len *= 2;
+    for (int64_t t = 0; t < N; t += len) p.bnd.push_back((int32_t)t);
+    p.bnd.push_back(N);
+    const int nslots = (int)p.bnd.size() - 1;
+    if (masked) {
+      p.mw_stride = (N + 63) / 64 + 1;
+      p.mw_bytes = align256((size_t)B * p.mw_stride * sizeof(uint64_t));
+    }
+    p.part_bytes = align256((size_t)nslots * B * H * 2 * M * D * sizeof(float));
+  }
+  p.ws_bytes = 2 * p.stats_bytes + p.mw_bytes + p.part_bytes;
+  return p;
+}
 }  // namespace
 
 extern "C" {
@@ -426,14 +466,15 @@ size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, i
 flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
                               int64_t q_batch_stride, const void* K, const void* V, int R,
                               const int64_t* offsets, const uint8_t* mask, float scale, const float* Z,
-                              const float* L, const void* dZ, float* dQ, void* dK, void* dV, void* workspace,
-                              size_t workspace_bytes, flare_stream_t stream) {
+                              const float* L, const void* dZ, float* dQ, void* dK, void* dV, void* dQ_cast,
+                              int flags, void* workspace, size_t workspace_bytes, flare_stream_t stream) {
   flare_status st = check_common(dtype, B, H, N, M, D);
   if (st != FLARE_OK) return st;
   st = check_offsets(N, R, offsets);
   if (st != FLARE_OK) return st;
   if (!std::isfinite(scale)) return fail(FLARE_EINVAL, "scale must be finite");
   if (q_batch_stride < 0) return fail(FLARE_EINVAL, "q_batch_stride must be >= 0");
+  if (flags & ~(FLARE_BWD_ACCUMULATE_DQ | FLARE_BWD_ACCUMULATE_DK)) return fail(FLARE_EINVAL, "unknown flags");
   if ((int64_t)B * H == 0) return FLARE_OK;
   if ((int64_t)M > 0 && (!Q || !Z || !L || !dZ || !dQ)) return fail(FLARE_EINVAL, "NULL pointer argument");
   if (N > 0 && (!K || !V || !dK || !dV)) return fail(FLARE_EINVAL, "NULL pointer argument");
@@ -445,7 +486,7 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   if (!aligned16(workspace)) return fail(FLARE_EINVAL, "workspace must be 16-byte aligned");
   if (plan.mfma) {
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dZ) || !aligned16(dQ) ||
-        !aligned16(dK) || !aligned16(dV) ||
+        !aligned16(dK) || !aligned16(dV) || !aligned16(dQ_cast) ||
         (q_batch_stride * 2) % 16 != 0)
       return fail(FLARE_EINVAL, "Q, K, V, dZ, dQ, dK, dV and the Q batch stride must be 16-byte aligned");
   }
@@ -472,6 +513,9 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   a.D = D;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.dQ_cast = dQ_cast;
+  a.accumulate_dq = (flags & FLARE_BWD_ACCUMULATE_DQ) != 0;
+  a.accumulate_dk = (flags & FLARE_BWD_ACCUMULATE_DK) != 0;
   const bool bf16 = dtype == FLARE_BF16;
   hipError_t e = launch_bwd_rowdot(dZ, bf16, Z, (int64_t)B * H * M, D, reinterpret_cast<float*>(ws), s);
   if (e != hipSuccess) return hip_fail(e, "backward row-term launch");
@@ -500,8 +544,93 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   }
   e = launch_bwd_kv_mfma(a, fuse, s);
   if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
-  e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, scale, dQ, s);
+  e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, scale, dQ, a.accumulate_dq != 0, dQ_cast, s);
   if (e != hipSuccess) return hip_fail(e, "query-gradient reduce launch");
+  return FLARE_OK;
+}
+
+
+size_t flare_decode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, int M, int D, int masked) {
+  const std::string saved = g_err;
+  if (check_common(dtype, B, H, N, M, D) != FLARE_OK || M > 256) {
+    g_err = saved;
+    return 0;
+  }
+  return plan_decode_bwd(dtype, B, H, N, M, D, masked != 0).ws_bytes;
+}
+
+flare_status flare_decode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Xq,
+                              const void* Klat, int64_t klat_batch_stride, const float* Z,
+                              const uint8_t* token_mask, float scale, const void* dY, void* dXq, float* dKlat,
+                              float* dZ, void* dZ_cast, void* workspace, size_t workspace_bytes,
+                              flare_stream_t stream) {
+  flare_status st = check_common(dtype, B, H, N, M, D);
+  if (st != FLARE_OK) return st;
+  if (M > 256) return fail(FLARE_EUNSUPPORTED, "decode supports M <= 256 (M=%d)", M);
+  if (!std::isfinite(scale)) return fail(FLARE_EINVAL, "scale must be finite");
+  if (klat_batch_stride < 0) return fail(FLARE_EINVAL, "klat_batch_stride must be >= 0");
+  if ((int64_t)B * H == 0) return FLARE_OK;
+  if (M == 0) return fail(FLARE_EINVAL, "decode needs M >= 1 latents");
+  if (!Klat || !Z || !dKlat || !dZ) return fail(FLARE_EINVAL, "NULL pointer argument");
+  if (N > 0 && (!Xq || !dY || !dXq)) return fail(FLARE_EINVAL, "NULL pointer argument");
+  const DecBwdPlan plan = plan_decode_bwd(dtype, B, H, N, M, D, token_mask != nullptr);
+  if (!workspace || workspace_bytes < plan.ws_bytes)
+    return fail(FLARE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(FLARE_EINVAL, "workspace must be 16-byte aligned");
+  if (plan.mfma && (!aligned16(Xq) || !aligned16(Klat) || !aligned16(dY) || !aligned16(dXq) ||
+                    !aligned16(Z) || !aligned16(dKlat) || !aligned16(dZ) || !aligned16(dZ_cast) ||
+                    (klat_batch_stride * 2) % 16 != 0))
+    return fail(FLARE_EINVAL, "Xq, Klat, Z, dY and the gradients must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  DecBwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Xq = Xq;
+  a.Klat = Klat;
+  a.Z = Z;
+  a.token_mask = token_mask;
+  a.dY = dY;
+  a.dXq = dXq;
+  a.dKlat = dKlat;
+  a.dZ = dZ;
+  a.dZ_cast = dZ_cast;
+  a.stats_stride = plan.stats_stride;
+  a.lse2 = reinterpret_cast<float*>(ws);
+  a.delta = reinterpret_cast<float*>(ws + plan.stats_bytes);
+  a.klat_bstride = klat_batch_stride;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.M = M;
+  a.D = D;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const bool bf16 = dtype == FLARE_BF16;
+  hipError_t e;
+  if (!plan.mfma) {
+    e = launch_decode_bwd_generic(a, bf16, s);
+    if (e != hipSuccess) return hip_fail(e, "decode backward launch");
+    return FLARE_OK;
+  }
+  char* p = ws + 2 * plan.stats_bytes;
+  if (plan.mw_bytes) {
+    a.mask_words = reinterpret_cast<const uint64_t*>(p);
+    a.mask_words_stride = plan.mw_stride;
+    e = launch_mask_words(token_mask, B, N, reinterpret_cast<uint64_t*>(p), plan.mw_stride, s);
+    if (e != hipSuccess) return hip_fail(e, "mask launch");
+    p += plan.mw_bytes;
+  }
+  a.ws_part = reinterpret_cast<float*>(p);
+  a.tokens_per_block = plan.tokens_per_block;
+  const int nc = (int)plan.bnd.size() - 1;
+  a.tab.nchunks = nc;
+  for (int i = 0; i <= nc; ++i) a.tab.bnd[i] = plan.bnd[i];
+  for (int i = 0; i < nc; ++i) a.tab.slot[i] = (int16_t)i;
+  e = launch_decode_bwd_mfma(a, s);
+  if (e != hipSuccess) return hip_fail(e, "decode backward launch");
+  e = launch_decode_bwd_reduce(a, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "decode backward reduce launch");
   return FLARE_OK;
 }
 

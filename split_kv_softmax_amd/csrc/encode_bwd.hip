@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void bwd_kv_generic_kernel(const BwdArgs a) {
     const int d = lane + 64 * j;
     if (d < D) {
       stg_(dv + d, av[j]);
-      stg_(dk + d, a.scale * ak[j]);
+      stg_(dk + d, a.scale * ak[j] + (a.accumulate_dk ? ldg_(dk + d) : 0.f));
     }
   }
 }
@@ -150,7 +150,11 @@ __global__ __launch_bounds__(256) void bwd_q_generic_kernel(const BwdArgs a) {
 #pragma unroll
   for (int j = 0; j < MAXDL; ++j) {
     const int d = lane + 64 * j;
-    if (d < D) a.dQ[row * D + d] = a.scale * acc[j];
+    if (d < D) {
+      const float r = a.scale * acc[j] + (a.accumulate_dq ? a.dQ[row * D + d] : 0.f);
+      a.dQ[row * D + d] = r;
+      if (a.dQ_cast) stg_(static_cast<TIn*>(a.dQ_cast) + row * D + d, r);
+    }
   }
 }
 
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
         const int r = f / CPR, ch = f % CPR;
         if (r < nrows) {
           const int64_t off = (int64_t)(t0 + r) * D + 8 * ch;
-          st16(dKg + off, u32x4_t{0, 0, 0, 0});
+          if (!a.accumulate_dk) st16(dKg + off, u32x4_t{0, 0, 0, 0});
           st16(dVg + off, u32x4_t{0, 0, 0, 0});
         }
       }
@@ -659,8 +663,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
         const int tsr = f / (TILE * CPR);
         const int r = (f / CPR) % TILE, ch = f % CPR;
         if (r < nrows) {
-          const u32x4_t v = ld16((tsr ? vst : kst) + r * ROWB + (ch ^ out_swz(r)) * 16);
-          st16((tsr ? dVg : dKg) + (int64_t)(t0 + r) * D + 8 * ch, v);
+          u32x4_t v = ld16((tsr ? vst : kst) + r * ROWB + (ch ^ out_swz(r)) * 16);
+          uint16_t* dst = (tsr ? dVg : dKg) + (int64_t)(t0 + r) * D + 8 * ch;
+          if (!tsr && a.accumulate_dk) {
+            // dK += this gradient (another product already wrote its share)
+            const u32x4_t o = ld16(dst);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(o[e]), bf16hi(v[e]) + bf16hi(o[e]));
+          }
+          st16(dst, v);
         }
       }
     }
@@ -681,14 +692,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   }
 }
 
-// dQ = s * sum over chunk slots (fixed order), one thread per 4 elements
+// dQ = s * sum over chunk slots (fixed order) [+ dQ], one thread per 4
+// elements; optionally also written rounded to bf16.
 __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restrict__ ws, int nslots, int64_t n4,
-                                                           float scale, float* __restrict__ dQ) {
+                                                           float scale, float* __restrict__ dQ, int accumulate,
+                                                           uint16_t* __restrict__ dQ_bf16) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n4) return;
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < nslots; ++k) s += reinterpret_cast<const f32x4_t*>(ws)[(int64_t)k * n4 + i];
-  reinterpret_cast<f32x4_t*>(dQ)[i] = s * scale;
+  f32x4_t r = s * scale;
+  if (accumulate) r += reinterpret_cast<const f32x4_t*>(dQ)[i];
+  reinterpret_cast<f32x4_t*>(dQ)[i] = r;
+  if (dQ_bf16) {
+    const u32x2_t w = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+    reinterpret_cast<u32x2_t*>(dQ_bf16)[i] = w;
+  }
 }
 
 bool bwd_mfma_supported(int M, int D) {
@@ -754,11 +773,12 @@ hipError_t launch_bwd_kv_mfma(const BwdArgs& a, bool with_dq, hipStream_t s) {
   return with_dq ? launch_kv_dq<true>(a, s) : launch_kv_dq<false>(a, s);
 }
 
-hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, hipStream_t s) {
+hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, bool accumulate,
+                                void* dQ_cast, hipStream_t s) {
   const int64_t n4 = elems / 4;
   if (n4 == 0) return hipSuccess;
   hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, ws, nslots, n4,
-                     scale, dQ);
+                     scale, dQ, (int)accumulate, static_cast<uint16_t*>(dQ_cast));
   return hipGetLastError();
 }
 

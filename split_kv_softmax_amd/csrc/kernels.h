@@ -84,11 +84,37 @@ struct BwdArgs {
   void* dK;                     // [B,H,N,D]
   void* dV;
   float* ws_dq;                 // [chunks,B,H,M,D] partial query gradients (matrix-core path)
+  void* dQ_cast;                // [B,H,M,D] dQ also in the input dtype, or null
+  int accumulate_dq;            // dQ += instead of dQ =
+  int accumulate_dk;            // dK += instead of dK =  (dV is always written)
   int64_t q_bstride;
   int B, H, N, M, D;
   float scale;
   float scale_log2;
   ChunkTable tab;               // token chunks (matrix-core path)
+};
+
+struct DecBwdArgs {
+  const void* Xq;               // [B,H,N,D] token queries
+  const void* Klat;             // [B|1,H,M,D] latent keys
+  const float* Z;               // [B,H,M,D] latent values
+  const uint8_t* token_mask;    // [B,N] or null
+  const uint64_t* mask_words;   // validity words of token_mask (matrix-core path)
+  int64_t mask_words_stride;
+  const void* dY;               // [B,H,N,D]
+  void* dXq;                    // [B,H,N,D]
+  float* dKlat;                 // [B,H,M,D]
+  float* dZ;                    // [B,H,M,D]
+  void* dZ_cast;                // [B,H,M,D] in the input dtype, or null
+  float* lse2;                  // [B*H, stats_stride] per-token log2-normaliser of the scaled scores
+  float* delta;                 // [B*H, stats_stride] per-token sum_m A dA
+  int64_t stats_stride;         // N rounded up to whole 64-token tiles
+  float* ws_part;               // [chunks, B*H, 2, M, D] partial dZ and dKlat/s (matrix-core path)
+  int64_t klat_bstride;
+  int B, H, N, M, D;
+  float scale, scale_log2;
+  int tokens_per_block;         // token side (matrix-core path)
+  ChunkTable tab;               // latent side chunks (matrix-core path)
 };
 
 // Encoder kernels. Return hipSuccess or the launch error.
@@ -111,8 +137,15 @@ hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s);
 // chunk partials (only where bwd_kv_fuses_dq says the registers allow it)
 bool bwd_kv_fuses_dq(int M, int D);
 hipError_t launch_bwd_kv_mfma(const BwdArgs& a, bool with_dq, hipStream_t s);
-hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, hipStream_t s);
+hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, bool accumulate,
+                                void* dQ_cast, hipStream_t s);
 hipError_t launch_bwd_kv_generic(const BwdArgs& a, bool bf16, hipStream_t s);
+
+hipError_t launch_decode_bwd_generic(const DecBwdArgs& a, bool bf16, hipStream_t s);
+bool decode_bwd_mfma_supported(int M, int D);
+int decode_bwd_waves(int D);
+hipError_t launch_decode_bwd_mfma(const DecBwdArgs& a, hipStream_t s);
+hipError_t launch_decode_bwd_reduce(const DecBwdArgs& a, bool bf16, hipStream_t s);
 
 bool decode_mfma_supported(int M, int D);
 int decode_waves(int D);

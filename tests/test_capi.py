@@ -37,7 +37,11 @@ def lib():
     L.lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp, vp]
     L.flare_decode.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp]
     L.flare_encode_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp,
-                                   vp, vp, vp, vp, sz, vp]
+                                   vp, vp, vp, vp, i32, vp, sz, vp]
+    L.flare_decode_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp, vp, vp, vp,
+                                   vp, sz, vp]
+    L.flare_decode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.flare_decode_bwd_workspace_size.restype = sz
     L.flare_encode_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64, i32]
     L.flare_encode_bwd_workspace_size.restype = sz
     L.flare_last_error.restype = ctypes.c_char_p
@@ -106,4 +110,21 @@ def test_workspace_contract(lib):
 
 def test_backward_validates_offsets(lib):
     assert lib.flare_encode_bwd(1, 1, 1, 100, 64, 64, FAKE, 0, FAKE, FAKE, 2, offs(0, 70, 60), None, 0.1, FAKE, FAKE,
-                                FAKE, FAKE, FAKE, FAKE, None, 0, None) == EINVAL
+                                FAKE, FAKE, FAKE, FAKE, None, 0, None, 0, None) == EINVAL
+    # unknown flags are rejected before anything else runs
+    assert lib.flare_encode_bwd(1, 1, 1, 100, 64, 64, FAKE, 0, FAKE, FAKE, 2, offs(0, 50, 100), None, 0.1, FAKE,
+                                FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, None, 0, None) == EINVAL
+    assert b"flags" in lib.flare_last_error()
+
+
+def test_decode_backward_validates(lib):
+    """Shape, pointer and workspace checks of the decode backward, before any launch."""
+    assert lib.flare_decode_bwd(1, 1, 1, 100, 300, 64, FAKE, FAKE, 0, FAKE, None, 0.1, FAKE, FAKE, FAKE, FAKE,
+                                None, FAKE, 1 << 20, None) == EUNSUP
+    assert lib.flare_decode_bwd(1, 1, 1, 100, 64, 64, FAKE, None, 0, FAKE, None, 0.1, FAKE, FAKE, FAKE, FAKE,
+                                None, FAKE, 1 << 20, None) == EINVAL
+    n = lib.flare_decode_bwd_workspace_size(1, 1, 2, 1000, 64, 64, 0)
+    assert n > 0 and n == lib.flare_decode_bwd_workspace_size(1, 1, 2, 1000, 64, 64, 0)
+    assert lib.flare_decode_bwd(1, 1, 2, 1000, 64, 64, FAKE, FAKE, 0, FAKE, None, 0.1, FAKE, FAKE, FAKE, FAKE,
+                                None, FAKE, n - 1, None) == EWS
+    assert lib.flare_decode_bwd_workspace_size(1, 1, 2, 1000, 300, 64, 0) == 0     # invalid shape -> 0
