@@ -185,9 +185,544 @@ hipError_t launch_decode_bwd_generic(const DecBwdArgs& a, bool bf16, hipStream_t
   return hipGetLastError();
 }
 
-bool decode_bwd_mfma_supported(int M, int D) { return false; }
-int decode_bwd_waves(int D) { return 4; }
-hipError_t launch_decode_bwd_mfma(const DecBwdArgs& a, hipStream_t s) { return hipErrorInvalidValue; }
-hipError_t launch_decode_bwd_reduce(const DecBwdArgs& a, bool bf16, hipStream_t s) { return hipErrorInvalidValue; }
+// ---------------------------------------------------------------------------
+// Matrix-core token side.  Like the forward decode: a workgroup owns one
+// (batch, head) and a run of tokens, each wave 32 tokens at a time from its own
+// direct-load ring (token queries and output gradients), lane = token:
+//   T^T = Klat Xq^T, dA^T = Z dY^T         (A = latent rows from LDS)
+//   A = softmax over the M latents (lane-local), delta = sum_m A dA
+//   dT = A (dA - delta)
+//   dXq^T = Klat^T dT^T                      (A = Klat^T by transposing reads)
+// dXq rows leave through the consumed ring slot as whole rows; each token's
+// log2-normaliser and delta go to the workspace for the latent side.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tok_swz(int D, int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+
+template <int NI, int ST, int S>
+__device__ __forceinline__ void wait_blk(int later_blocks, int later_stores) {
+  // vector-memory ops issued after block j's loads: later_blocks more blocks of
+  // NI loads and later_stores blocks of ST stores
+#define FL_W(B, T)                                              \
+  if (later_blocks == B && later_stores == T) {                 \
+    wait_vm<(NI * B + ST * T) < 64 ? (NI * B + ST * T) : 63>(); \
+    return;                                                     \
+  }
+  static_assert(S <= 3, "wait table covers S <= 3");
+  static_assert(NI * (S - 2 > 0 ? S - 2 : 0) + ST * (S - 1) < 64, "vmcnt range");
+  FL_W(0, 0) FL_W(0, 1) FL_W(0, 2) FL_W(1, 0) FL_W(1, 1) FL_W(1, 2)
+#undef FL_W
+  wait_vm<0>();
+}
+
+__device__ __forceinline__ int swap_bits2(int x) { return ((x & 1) << 1) | (x >> 1); }
+
+template <int D, int MB, int NWV, int S>
+__global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArgs a) {
+  constexpr int M = 32 * MB;
+  constexpr int KS = D / 16;   // k-steps over the head dim
+  constexpr int DB = D / 32;   // 32-row blocks of dXq^T
+  constexpr int MS = M / 16;   // k-steps over the latents
+  constexpr int KLD = D + 8;   // padded latent rows (bf16 elements)
+  constexpr int BLK = 32;
+  constexpr int ROWB = 2 * D;
+  constexpr int BB = BLK * ROWB;             // bytes of one tensor's block
+  constexpr int NI = BB / 1024;              // direct loads per tensor and block
+  constexpr int ST = NI + 2;                 // stores per block: dXq rows, log2-normaliser, delta
+  constexpr int MAXT = 8192;
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[M * KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Zr[M * KLD];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * S * 2 * BB];
+  __shared__ uint8_t tmask[MAXT];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lg = lane >> 4, li = lane & 15;
+  const int nblk = (a.N + a.tokens_per_block - 1) / a.tokens_per_block;
+  int bid = blockIdx.x;
+  const int tb = bid % nblk;
+  bid /= nblk;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int n_lo = tb * a.tokens_per_block;
+  const int n_hi = min(a.N, n_lo + a.tokens_per_block);
+
+  {  // stage latent keys and values (bf16 rows) and the token mask
+    constexpr int T = 64 * NWV;
+    const uint16_t* kg = static_cast<const uint16_t*>(a.Klat) + (int64_t)b * a.klat_bstride + (int64_t)h * M * D;
+    const float* zg = a.Z + bh * (int64_t)M * D;
+    for (int f = tid; f < M * D / 8; f += T) {
+      const int m = f / (D / 8), c = f % (D / 8);
+      st16(&Kl[m * KLD + 8 * c], ld16(kg + 8 * (int64_t)f));
+      const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zg + 8 * (int64_t)f);
+      const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zg + 8 * (int64_t)f + 4);
+      st16(&Zr[m * KLD + 8 * c], u32x4_t{pack_bf16x2(z0[0], z0[1]), pack_bf16x2(z0[2], z0[3]),
+                                         pack_bf16x2(z1[0], z1[1]), pack_bf16x2(z1[2], z1[3])});
+    }
+    const uint8_t* tm = a.token_mask ? a.token_mask + (int64_t)b * a.N : nullptr;
+    for (int i = tid; i < n_hi - n_lo; i += T) tmask[i] = tm ? tm[n_lo + i] : (uint8_t)1;
+  }
+  __syncthreads();   // also completes the staging loads before the ring starts
+
+  const uint16_t* Xg = static_cast<const uint16_t*>(a.Xq) + bh * (int64_t)a.N * D;
+  const uint16_t* Gg = static_cast<const uint16_t*>(a.dY) + bh * (int64_t)a.N * D;
+  uint16_t* dXg = static_cast<uint16_t*>(a.dXq) + bh * (int64_t)a.N * D;
+  float* lseg = a.lse2 + bh * a.stats_stride;
+  float* delg = a.delta + bh * a.stats_stride;
+  const float c2 = a.scale_log2;
+  uint8_t* myring = ring + wave * (S * 2 * BB);
+  const uint32_t myring_lds = lds_addr(myring);
+
+  const int span = n_hi - n_lo - BLK * wave;
+  const int nb = span > 0 ? (span + BLK * NWV - 1) / (BLK * NWV) : 0;
+  uint32_t voff[NI], voff0[NI];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int byte = ii * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    const int ch = pc ^ tok_swz(D, r);
+    voff[ii] = r * ROWB + ch * 16;
+    voff0[ii] = ch * 16;
+  }
+  auto issue = [&](int j, int stage) {
+    const int n0 = n_lo + BLK * (wave + NWV * j);
+    const uint32_t st = myring_lds + stage * 2 * BB;
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int r = (ii * 1024) / ROWB + lane / (ROWB / 16);
+      const uint32_t vo = n0 + r < n_hi ? voff[ii] : voff0[ii];
+      dma16_off(Xg + (int64_t)n0 * D, vo, st + ii * 1024);
+      dma16_off(Gg + (int64_t)n0 * D, vo, st + BB + ii * 1024);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j)
+    if (j < nb) issue(j, j);
+
+  const int swx = tok_swz(D, l32);
+  const bf16x8_t ones_unused = {};
+  (void)ones_unused;
+  for (int j0 = 0; j0 < nb; j0 += S)
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    const int j = j0 + st;
+    if (j >= nb) break;
+    const int lb = min(S - 2, nb - 1 - j);
+    const int ls = min(j, S - 1);
+    wait_blk<2 * NI, ST, S>(lb > 0 ? lb : 0, ls);
+    if (j + S - 1 < nb) issue(j + S - 1, (st + S - 1) % S);
+    const int n0 = n_lo + BLK * (wave + NWV * j);
+    const int n = n0 + l32;
+    const bool inb = n < n_hi;
+    uint8_t* xs = myring + st * 2 * BB;
+    const uint8_t* gs = xs + BB;
+    bf16x8_t xop[KS], gop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = l32 * ROWB + (((2 * ks + hh) ^ swx) * 16);
+      xop[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + off));
+      gop[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(gs + off));
+    }
+    // scores and dA; register r of block mb holds latent 32*mb + 16*(r/8) + 8*hh + r%8
+    f32x16_t t[MB], da[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      t[mb] = f32x16_t{};
+      da[mb] = f32x16_t{};
+      const uint16_t* krow = &Kl[(32 * mb + swap23(l32)) * KLD + 8 * hh];
+      const uint16_t* zrow = &Zr[(32 * mb + swap23(l32)) * KLD + 8 * hh];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 16 * ks)),
+                             xop[ks], t[mb]);
+        da[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)),
+                              gop[ks], da[mb]);
+      }
+    }
+    float mx = t[0][0];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmax2(mx, t[mb][r]);
+    mx = fmax2(mx, __shfl_xor(mx, 32, 64));
+    const float nmc = -mx * c2;
+    float lsum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        t[mb][r] = fast_exp2(__builtin_fmaf(t[mb][r], c2, nmc));
+        lsum += t[mb][r];
+      }
+    lsum += __shfl_xor(lsum, 32, 64);
+    const float inv = 1.f / lsum;
+    float delta = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        t[mb][r] *= inv;                                  // A
+        delta = __builtin_fmaf(t[mb][r], da[mb][r], delta);
+      }
+    delta += __shfl_xor(delta, 32, 64);
+    bf16x8_t dtk[MS];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = t[mb][8 * g + e] * (da[mb][8 * g + e] - delta);
+        dtk[2 * mb + g] = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                              pack_bf16x2(v[6], v[7])});
+      }
+    // dXq^T = Klat^T dT^T; Klat^T rows (head dims) permuted so that each register
+    // group holds 8 consecutive head dims: lane i of a 16-lane group reads
+    // column swap23(i) of the 4x16 block
+    f32x16_t acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      acc[db] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < MS; ++ks) {
+        u32x2_t part[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+          const int col = 32 * db + 16 * (lg & 1) + 4 * swap_bits2(li & 3);
+          part[q] = __builtin_bit_cast(u32x2_t,
+                                       __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&Kl[row * KLD + col]));
+        }
+        acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]}),
+                               dtk[ks], acc[db]);
+      }
+    }
+    const bool keep = inb && tmask[inb ? n - n_lo : 0] != 0;
+    // stage dXq rows (register group g of lane half hh: dims 32*db + 16*g + 8*hh ..) in the consumed Xq slot
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        u32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t v = pack_bf16x2(a.scale * acc[db][8 * g + 2 * e], a.scale * acc[db][8 * g + 2 * e + 1]);
+          w[e] = keep ? v : 0u;
+        }
+        const int pc = (4 * db + 2 * g + hh) ^ swx;
+        st16(xs + l32 * ROWB + pc * 16, w);
+      }
+    const int valid_rows = min(BLK, n_hi - n0);
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(dXg + (int64_t)n0 * D, 0, valid_rows * ROWB, 0x00020000);
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii) {
+      const int byte = ii * 1024 + lane * 16;
+      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xs + byte);
+      __builtin_amdgcn_raw_buffer_store_b128(v, yr, r * ROWB + ((pc ^ tok_swz(D, r)) * 16), 0, kCachePolicyNT);
+    }
+    // per-token statistics; lanes of the upper half and rows past the run fall outside the range
+    const float lse2 = keep ? (mx * c2 + __log2f(lsum)) : __builtin_huge_valf();
+    const float dl = keep ? delta : 0.f;
+    const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(lseg + n0, 0, valid_rows * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(delg + n0, 0, valid_rows * 4, 0x00020000);
+    const int soff = hh ? (1 << 20) : l32 * 4;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse2), lr, soff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dl), dr, soff, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core latent side.  Like the encoder backward's query-gradient kernel:
+// one workgroup per (batch, head, token chunk), wave w owns latent rows
+// [32w, 32w+32) (lane = latent), 64-token tiles of Xq, dY and the tokens'
+// statistics arrive through a direct-load ring:
+//   S^T = Xq Klat^T, dA^T = dY Z^T          (A = token rows, B = latents in registers)
+//   A = exp2(s log2e S - lse2[n]),  dT = A (dA - delta[n])
+//   dZ^T += dY^T A^T,  dKlat^T += Xq^T dT^T  (A = transposing reads of the tiles)
+// The chunk's sums go to its workspace slot (dKlat without the scale s).
+// ---------------------------------------------------------------------------
+template <int D, int NW, int S>
+__global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs a) {
+  constexpr int TILE = 64;
+  constexpr int ROWB = 2 * D;
+  constexpr int TB = TILE * ROWB;
+  constexpr int STAGE = 2 * TB + 1024;       // Xq tile, dY tile, statistics (512 B used)
+  constexpr int NI = TB / 1024;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int OPS = 2 * NI / NW + 1;       // loads per wave and tile (the statistics share one)
+  constexpr int SPW = 32 / NW;               // 16-byte statistics pieces per wave
+  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  static_assert(OPS * (S - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lg = lane >> 4, li = lane & 15;
+  const int nch = a.tab.nchunks;
+  int bid = blockIdx.x;
+  const int c = bid % nch;
+  bid /= nch;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int t_begin = a.tab.bnd[c], t_end = a.tab.bnd[c + 1];
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int M = a.M;
+  const uint16_t* Xg = static_cast<const uint16_t*>(a.Xq) + bh * (int64_t)a.N * D;
+  const uint16_t* Gg = static_cast<const uint16_t*>(a.dY) + bh * (int64_t)a.N * D;
+  const float* lseg = a.lse2 + bh * a.stats_stride;
+  const float* delg = a.delta + bh * a.stats_stride;
+  const_u64* mw = a.mask_words ? (const_u64*)(a.mask_words + (int64_t)b * a.mask_words_stride) : nullptr;
+
+  const int m = 32 * wave + l32;
+  bf16x8_t kop[KS], zop[KS];
+  {
+    const uint16_t* krow = static_cast<const uint16_t*>(a.Klat) + (int64_t)b * a.klat_bstride +
+                           ((int64_t)h * M + m) * D + 8 * hh;
+    const float* zrow = a.Z + (bh * M + m) * (int64_t)D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kop[ks] = __builtin_bit_cast(bf16x8_t, ld16(krow + 16 * ks));
+      const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zrow + 16 * ks);
+      const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zrow + 16 * ks + 4);
+      zop[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16x2(z0[0], z0[1]), pack_bf16x2(z0[2], z0[3]),
+                                                     pack_bf16x2(z1[0], z1[1]), pack_bf16x2(z1[2], z1[3])});
+    }
+  }
+  wait_vm<0>();   // only the ring's loads are in flight from here on
+  const float c2 = a.scale_log2;
+
+  const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
+  auto tile_bits = [&](int u) -> uint64_t {
+    if (u >= ntiles) return 0ull;
+    const int t0 = t_begin + u * TILE;
+    const int nn = t_end - t0;
+    uint64_t bits = nn >= 64 ? ~0ull : ((1ull << nn) - 1ull);
+    if (mw) bits &= mask_tile_bits(mw, t0);
+    return bits;
+  };
+  auto issue = [&](int u) {
+    const int t0 = t_begin + u * TILE;
+    const int nrows = t_end - t0;
+    const uint32_t kst = lds_addr(smem) + (u % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < NI / NW; ++j) {
+      const int ii = wave + NW * j;
+      const int byte = ii * 1024 + lane * 16;
+      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+      const int ch = pc ^ kv_swz<D>(r);
+      const int rr = r < nrows ? r : 0;
+      const int64_t off = (int64_t)(t0 + rr) * D + 8 * ch;
+      dma16(Xg + off, kst + ii * 1024);
+      dma16(Gg + off, kst + TB + ii * 1024);
+    }
+    // statistics of the tile's 64 tokens: pieces 0..15 the log2-normalisers, 16..31 the deltas
+    // (the arrays are padded to whole tiles, so the reads stay in bounds)
+    if (lane < SPW) {
+      const int p = wave * SPW + lane;
+      const float* src = p < 16 ? lseg + t0 + 4 * p : delg + t0 + 4 * (p - 16);
+      dma16(src, kst + 2 * TB + wave * SPW * 16);
+    }
+  };
+
+  f32x16_t accz[DB], acck[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    accz[i] = f32x16_t{};
+    acck[i] = f32x16_t{};
+  }
+  uint64_t ring[S];
+#pragma unroll
+  for (int k = 0; k < S; ++k) ring[k] = 0ull;
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) {
+    ring[k] = tile_bits(k);
+    if (ring[k]) issue(k);
+  }
+  const int swk = kv_swz<D>(swap23(l32));
+  for (int t = 0; t < ntiles; ++t) {
+    int later = 0;
+#pragma unroll
+    for (int k = 1; k < S - 1; ++k) later += ring[k] != 0ull;
+    wait_tiles<OPS, S>(later);
+    barrier_lds();
+    ring[S - 1] = tile_bits(t + S - 1);
+    if (ring[S - 1]) issue(t + S - 1);
+    const uint64_t bits = ring[0];
+    if (bits) {
+      uint8_t* xst = smem + (t % S) * STAGE;
+      uint8_t* gst = xst + TB;
+      const float* stt = reinterpret_cast<const float*>(xst + 2 * TB);
+      if (bits != ~0ull) {
+        // invalid rows of both tiles become zero: they meet A = dT = 0
+        for (int f = tid; f < TILE * (ROWB / 16); f += 64 * NW) {
+          const int r = f / (ROWB / 16), pc = f % (ROWB / 16);
+          if (!((bits >> r) & 1ull)) {
+            st16(xst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
+            st16(gst + r * ROWB + pc * 16, u32x4_t{0, 0, 0, 0});
+          }
+        }
+        barrier_lds();
+      }
+      const uint64_t lb = bits >> (8 * hh);
+      const bool full = bits == ~0ull;
+      bf16x8_t pa[4], pd[4];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        f32x16_t sc = f32x16_t{}, da = f32x16_t{};
+        const uint8_t* xrow = xst + (32 * b2 + swap23(l32)) * ROWB;
+        const uint8_t* grow = gst + (32 * b2 + swap23(l32)) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = (2 * ks + hh) ^ swk;
+          sc = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xrow + ch * 16)),
+                            kop[ks], sc);
+          da = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(grow + ch * 16)),
+                            zop[ks], da);
+        }
+        // register r of lane half hh holds token 32*b2 + 16*(r/8) + 8*hh + r%8
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int t0 = 32 * b2 + 16 * g + 8 * hh;
+          const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(stt + t0);
+          const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(stt + t0 + 4);
+          const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(stt + 64 + t0);
+          const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(stt + 64 + t0 + 4);
+          float pv[8], dv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * g + e;
+            const float l2 = e < 4 ? l0[e] : l1[e - 4];
+            const float dl = e < 4 ? d0[e] : d1[e - 4];
+            pv[e] = fast_exp2(__builtin_fmaf(sc[r], c2, -l2));
+            dv[e] = pv[e] * (da[r] - dl);
+          }
+          if (!full) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              if (!((lb >> (32 * b2 + 16 * g + e)) & 1ull)) {
+                pv[e] = 0.f;
+                dv[e] = 0.f;
+              }
+            }
+          }
+          pa[2 * b2 + g] = __builtin_bit_cast(
+              bf16x8_t, u32x4_t{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                                pack_bf16x2(pv[6], pv[7])});
+          pd[2 * b2 + g] = __builtin_bit_cast(
+              bf16x8_t, u32x4_t{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3]), pack_bf16x2(dv[4], dv[5]),
+                                pack_bf16x2(dv[6], dv[7])});
+        }
+      }
+      // dZ^T += dY^T A^T and dKlat^T += Xq^T dT^T through transposing reads of the tiles
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+        const int chl = d0 >> 3, half = (d0 & 7) * 2;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          u32x2_t pg[2], px[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int nn = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+            const int off = nn * ROWB + ((chl ^ kv_swz<D>(nn)) * 16) + half;
+            pg[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(gst + off)));
+            px[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(xst + off)));
+          }
+          accz[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, u32x4_t{pg[0][0], pg[0][1], pg[1][0], pg[1][1]}),
+                                  pa[ks], accz[db]);
+          acck[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, u32x4_t{px[0][0], px[0][1], px[1][0], px[1][1]}),
+                                  pd[ks], acck[db]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k) ring[k] = ring[k + 1];
+  }
+  // chunk sums -> workspace slot (row m, dims d): [slot][bh][2][M][D]
+  float* W = a.ws_part + (((int64_t)a.tab.slot[c] * a.B * a.H + bh) * 2) * (int64_t)M * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t off = (int64_t)m * D + 32 * db + 8 * q + 4 * hh;
+      *reinterpret_cast<f32x4_t*>(W + off) = f32x4_t{accz[db][4 * q], accz[db][4 * q + 1], accz[db][4 * q + 2],
+                                                     accz[db][4 * q + 3]};
+      *reinterpret_cast<f32x4_t*>(W + (int64_t)M * D + off) =
+          f32x4_t{acck[db][4 * q], acck[db][4 * q + 1], acck[db][4 * q + 2], acck[db][4 * q + 3]};
+    }
+}
+
+// dZ = sum of the chunk slots, dKlat = s * sum (fixed order); dZ optionally also in bf16
+__global__ __launch_bounds__(256) void dbwd_reduce_kernel(const float* __restrict__ ws, int nslots, int64_t bhs,
+                                                          int64_t md4, float scale, float* __restrict__ dZ,
+                                                          float* __restrict__ dK, uint16_t* __restrict__ dZb) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over bhs * md4
+  if (i >= bhs * md4) return;
+  const int64_t bh = i / md4, e = i % md4;
+  f32x4_t sz = {0.f, 0.f, 0.f, 0.f}, sk = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < nslots; ++k) {
+    const f32x4_t* base = reinterpret_cast<const f32x4_t*>(ws) + ((int64_t)k * bhs + bh) * 2 * md4;
+    sz += base[e];
+    sk += base[md4 + e];
+  }
+  reinterpret_cast<f32x4_t*>(dZ)[i] = sz;
+  reinterpret_cast<f32x4_t*>(dK)[i] = sk * scale;
+  if (dZb) reinterpret_cast<u32x2_t*>(dZb)[i] = u32x2_t{pack_bf16x2(sz[0], sz[1]), pack_bf16x2(sz[2], sz[3])};
+}
+
+bool decode_bwd_mfma_supported(int M, int D) {
+  return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128);
+}
+
+int decode_bwd_waves(int D) { return D == 64 ? 4 : 2; }
+
+template <int D, int MB>
+static hipError_t launch_dbwd_t(const DecBwdArgs& a, hipStream_t s) {
+  constexpr int NWV = D == 64 ? 4 : 2;
+  constexpr int S = D == 64 ? 3 : 2;
+  const int64_t nblk = (a.N + a.tokens_per_block - 1) / a.tokens_per_block;
+  hipLaunchKernelGGL((dbwd_tok_mfma_kernel<D, MB, NWV, S>), dim3((unsigned)(nblk * a.H * a.B)), dim3(64 * NWV), 0,
+                     s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int NW = MB;
+  hipLaunchKernelGGL((dbwd_lat_mfma_kernel<D, NW, 3>), dim3((unsigned)((int64_t)a.tab.nchunks * a.H * a.B)),
+                     dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_bwd_mfma(const DecBwdArgs& a, hipStream_t s) {
+  if (a.tokens_per_block > 8192 || a.tokens_per_block % (32 * decode_bwd_waves(a.D)) != 0)
+    return hipErrorInvalidValue;
+  if (a.D == 64) {
+    switch (a.M) {
+      case 32: return launch_dbwd_t<64, 1>(a, s);
+      case 64: return launch_dbwd_t<64, 2>(a, s);
+      case 128: return launch_dbwd_t<64, 4>(a, s);
+    }
+  } else if (a.D == 128) {
+    switch (a.M) {
+      case 32: return launch_dbwd_t<128, 1>(a, s);
+      case 64: return launch_dbwd_t<128, 2>(a, s);
+      case 128: return launch_dbwd_t<128, 4>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_bwd_reduce(const DecBwdArgs& a, bool bf16, hipStream_t s) {
+  const int64_t bhs = (int64_t)a.B * a.H;
+  const int64_t md4 = (int64_t)a.M * a.D / 4;
+  if (bhs * md4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(dbwd_reduce_kernel, dim3((unsigned)((bhs * md4 + 255) / 256)), dim3(256), 0, s, a.ws_part,
+                     a.tab.nchunks, bhs, md4, a.scale, a.dZ, a.dKlat,
+                     static_cast<uint16_t*>(bf16 ? a.dZ_cast : nullptr));
+  return hipGetLastError();
+}
 
 }  // namespace flare
