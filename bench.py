@@ -242,6 +242,12 @@ def roofline_of(w: W.Workload, x, step, ph):
     kvb = 2 if w.dtype == "bf16" else 4
     row = w.D * kvb                               # bytes of one K, V, Y, dK or dV row
     rows = w.B * w.H * w.N
+    if w.kind == "flarepp" and "encode2_bwd" in ph:
+        # physical-value encoder backward: K, V read, dV written, dK read and written (it adds into the
+        # decoder's key gradient); query-synthesis encoder backward: Kt, Vt read, dKt, dVt written
+        ms = 0.5 * (ph["encode2_bwd"] + ph["encode1_bwd"])
+        return ms, (5 + 4) * rows * row // 2, ("flare_encode_bwd call (row term, key/value-gradient kernel with "
+                                                "fused query gradient, reduce); both encoder backwards averaged")
     if w.kind == "flarepp":
         ms = 0.5 * (ph["encode1"] + ph["encode2"])
         return ms, 2 * rows * row, "encode_mfma_kernel (flare_encode, one launch; both encoders averaged)"
@@ -275,6 +281,43 @@ def copy_reference(nbytes=1 << 30, reps=5):
     return {"GB_s": 2 * nbytes / (ms * 1e-3) / 1e9, "ms": ms, "what": "1 GiB device-to-device copy, read+write bytes"}
 
 
+class FlareppTrainStep(FlareppStep):
+    """FLARE++ forward chain followed by its backward chain (decoder, physical-value
+    encoder, query-synthesis encoder) with preallocated gradients."""
+
+    def __init__(self, w: W.Workload, x):
+        super().__init__(w, x)
+        dev = x["K"].device
+        B, H, M, D = w.B, w.H, w.M, w.D
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.dY = W.normal((B, H, w.N, D), w.wid, W.T_DZ, 1.0, torch.bfloat16, dev)
+        self.dK = torch.empty_like(x["K"])
+        self.dV = torch.empty_like(x["V"])
+        self.dKt = torch.empty_like(x["Kt"])
+        self.dVt = torch.empty_like(x["Vt"])
+        self.dQX = torch.empty((B, H, M, D), **f32)
+        self.dZ2 = torch.empty((B, H, M, D), **f32)
+        self.dQt = torch.empty((B, H, M, D), **f32)
+        self.dZ2c = torch.empty((B, H, M, D), dtype=torch.bfloat16, device=dev)
+        self.dQXc = torch.empty((B, H, M, D), dtype=torch.bfloat16, device=dev)
+        self.names = self.names + ["decode_bwd", "encode2_bwd", "encode1_bwd"]
+        self.ev = [_ev() for _ in range(len(self.names) + 1)]
+        self.phase_ms = [0.0] * len(self.names)
+
+    def __call__(self, timed_phases: bool):
+        super().__call__(timed_phases)
+        x, w, ev = self.x, self.w, self.ev
+        rec = (lambda i: ev[i].record()) if timed_phases else (lambda i: None)
+        fl.decode_bwd(x["K"], self.QXb, self.Z, w.scale, self.dY, None, self.dK, self.dQX, self.dZ2, self.dZ2c)
+        rec(6)
+        fl.encode_bwd(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, self.Z, self.L, self.dZ2c, dQ=self.dQX,
+                      dK=self.dK, dV=self.dV, dQ_cast=self.dQXc, flags=fl.ACCUMULATE_DQ | fl.ACCUMULATE_DK)
+        rec(7)
+        fl.encode_bwd(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.QX, self.QXL, self.dQXc,
+                      dQ=self.dQt, dK=self.dKt, dV=self.dVt)
+        rec(8)
+
+
 STEPS = {"flarepp": FlareppStep, "flare": FlareStep, "splitkv": EncodeMergeStep, "encode": EncodeMergeStep,
          "encode_bwd": FwdBwdStep}
 
@@ -288,6 +331,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="about this much oracle work on whole (batch, head) slices")
+    ap.add_argument("--backward", action="store_true",
+                    help="FLARE++ only: time the forward chain plus its backward chain (a training step "
+                         "of the mixer); not the headline metric")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device 3 times "
                          "(the plain copy that scales the HBM byte counters)")
@@ -302,7 +348,10 @@ def main():
     w = W.BY_NAME[args.workload]
     torch.cuda.set_device(0)
     x = w.make("cuda")
-    step = STEPS[w.kind](w, x)
+    if args.backward and w.kind != "flarepp":
+        print("--backward is defined for the FLARE++ workload only", file=sys.stderr)
+        sys.exit(2)
+    step = FlareppTrainStep(w, x) if args.backward else STEPS[w.kind](w, x)
     for _ in range(args.warmup):
         step(timed_phases=False)
     torch.cuda.synchronize()
@@ -329,11 +378,11 @@ def main():
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     tokens = w.B * w.N * w.H
     kvb = 2 if w.dtype == "bf16" else 4
-    is_main = w.name == W.FLAREPP.name
+    is_main = w.name == W.FLAREPP.name and not args.backward
 
     line = {
         "metric": "FLARE encode+decode tokens/sec (B*N*H) at N=256K; % of HBM/MFMA roofline" if is_main
-        else f"{w.kind} tokens/sec (B*N*H)",
+        else ("FLARE++ forward+backward tokens/sec (B*N*H)" if args.backward else f"{w.kind} tokens/sec (B*N*H)"),
         "value": tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
