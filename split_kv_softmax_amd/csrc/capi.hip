@@ -389,9 +389,11 @@ BwdPlan plan_bwd(flare_dtype dt, int B, int H, int N, int M, int D, bool masked)
   p.mfma = dt == FLARE_BF16 && bwd_mfma_supported(M, D) && N > 0;
   p.c_bytes = align256((size_t)B * H * M * sizeof(float));
   if (p.mfma) {
-    // about one workgroup per CU for the query-gradient kernel, chunks of whole tiles
+    // as many workgroups as the CUs hold at once (one or two per CU, by the
+    // key/value kernel's registers and LDS), chunks of whole tiles
     const int64_t bh = std::max<int64_t>(1, (int64_t)B * H);
-    int64_t per = std::max<int64_t>(1, (256 + bh - 1) / bh);
+    const int64_t slots = 256 * (int64_t)bwd_kv_blocks_per_cu(M, D);
+    int64_t per = std::max<int64_t>(1, (slots + bh - 1) / bh);
     int64_t len = ((N + per - 1) / per + 63) / 64 * 64;
     len = std::max<int64_t>(len, 1024);
     const int forced = env_int("FLARE_BWD_CHUNK", 0);
@@ -544,7 +546,9 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   }
   e = launch_bwd_kv_mfma(a, fuse, s);
   if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
-  e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, scale, dQ, a.accumulate_dq != 0, dQ_cast, s);
+  // the fused kernel's partials already carry s (it contracts s dS); the query-gradient kernel's do not
+  e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, fuse ? 1.f : scale, dQ, a.accumulate_dq != 0,
+                           dQ_cast, s);
   if (e != hipSuccess) return hip_fail(e, "query-gradient reduce launch");
   return FLARE_OK;
 }

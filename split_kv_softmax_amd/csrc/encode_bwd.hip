@@ -361,12 +361,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
 // Matrix-core key/value gradients (FLARE++ appendix, backward pass): one
 // workgroup per (b, h, token chunk); 64-token tiles through a direct-load ring.
 // Phase A (one wave per 32 latent rows, lane = latent row):
-//   S^T = K Q^T, dP^T = V dZ^T, P = exp(s S - L), dS = P (dP - c)
-//   P and dS go to LDS as bf16 [m][token] (128-byte rows, K/V swizzle); with DQ the wave also adds
-//   K^T dS^T into its query-gradient partial, as the query-gradient kernel does.
+//   S^T = K Q^T, dP^T = V dZ^T, P = exp(s S - L), s dS = P (s dP - s c)
+//   P and s dS go to LDS as bf16 [m][token] (128-byte rows, K/V swizzle); with DQ the wave also adds
+//   K^T (s dS)^T into its query-gradient partial (so those partials already carry s).
 // Phase B (each wave one gradient tensor and a slice of output blocks,
 // lane = token):
-//   dV^T = dZ^T P,  dK^T = s Q^T dS        (contraction over the M latents)
+//   dV^T = dZ^T P,  dK^T = Q^T (s dS)      (contraction over the M latents)
 // with dZ^T / Q^T slices held in registers for the whole chunk.  The tile's
 // gradients are staged in the tile's own K/V slot and leave as whole
 // coalesced rows.  Padded tokens get P = dS = 0, hence zero rows; tiles with
@@ -395,6 +395,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   constexpr int WPT = NW / 2;          // phase-B waves per gradient tensor
   constexpr int NDW = DB >= WPT ? DB / WPT : 1;
   constexpr int NNB = DB >= WPT ? 2 : 2 * DB / WPT;
+  constexpr int CPT = 2 * TILE * CPR / (64 * NW);   // copy-out chunks per thread
+  static_assert(CPT % 2 == 0 && CPT * 64 * NW == 2 * TILE * CPR, "copy-out split");
   static_assert(NI % NW == 0, "loads must split evenly over the waves");
   static_assert(MW <= NW && NW % 2 == 0 && WPT <= 2 * DB, "wave layout");
   static_assert(OPS * (S - 2) < 64, "vmcnt range");
@@ -464,10 +466,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       }
   }
   const float Lm = a.L[bh * M + m];
-  const float cm = a.c[bh * M + m];
+  const float cms = a.scale * a.c[bh * M + m];
   wait_vm<0>();
   barrier_lds();   // the stationary copy is dead from here on: the ring reuses it
   const float c2 = a.scale_log2;
+  const float sc1 = a.scale;
   const float nl2 = (Lm == kNegInf) ? __builtin_huge_valf() : Lm * kLog2e;
 
   const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
@@ -509,6 +512,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
     ring[k] = tile_bits(k);
     if (ring[k]) issue(k);
   }
+  // copy-out chunks of this thread: chunk i is 16-byte column ch0 of row r0 + RSTEP*(i % (CPT/2)) of
+  // dK (first half) or dV; RSTEP keeps the staging swizzle of r0
+  constexpr int RSTEP = 64 * NW / CPR;
+  static_assert(RSTEP % 16 == 0, "copy-out rows share one swizzle");
+  const int r0 = tid / CPR, ch0 = tid % CPR;
+  const int lds0 = r0 * ROWB + (ch0 ^ out_swz(r0)) * 16;
+  const int off0 = r0 * D + 8 * ch0;
   const int swk = kv_swz<D>(swap23(l32));   // rows 32*b2 + swap23(l32)
   for (int t = 0; t < ntiles; ++t) {
     int later = 0;
@@ -523,13 +533,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
     const int nrows = t_end - t0 < TILE ? t_end - t0 : TILE;
     if (!bits) {
       // no valid token: zero gradient rows, nothing loaded
-      for (int f = tid; f < TILE * CPR; f += 64 * NW) {
-        const int r = f / CPR, ch = f % CPR;
-        if (r < nrows) {
-          const int64_t off = (int64_t)(t0 + r) * D + 8 * ch;
-          if (!a.accumulate_dk) st16(dKg + off, u32x4_t{0, 0, 0, 0});
-          st16(dVg + off, u32x4_t{0, 0, 0, 0});
-        }
+      const int64_t tb = (int64_t)t0 * D;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const bool isv = i >= CPT / 2;
+        const int k = i % (CPT / 2);
+        if (r0 + RSTEP * k < nrows && (isv || !a.accumulate_dk))
+          st16((isv ? dVg : dKg) + tb + off0 + RSTEP * D * k, u32x4_t{0, 0, 0, 0});
       }
     } else {
       uint8_t* kst = smem + (t % S) * STAGE;
@@ -568,7 +578,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
             for (int j = 0; j < 8; ++j) {
               const int r = 8 * g + j;
               pv[j] = fast_exp2(__builtin_fmaf(sc[r], c2, -nl2));
-              ds[j] = pv[j] * (dp[r] - cm);
+              ds[j] = pv[j] * __builtin_fmaf(dp[r], sc1, -cms);   // s dS: dK and dQ take it unscaled
             }
             if (!full) {
               // padding and rows past the chunk: exact zeros (their K/V rows may hold anything)
@@ -618,60 +628,97 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       {
         const uint8_t* bsrc = tsel == 0 ? pbuf : dsbuf;
         uint8_t* stg = tsel == 0 ? vst : kst;
-        const float osc = tsel == 0 ? 1.f : a.scale;
+        // B operand (P or s dS over 16 latents x 32 tokens) of output block nb, step ks
+        auto bload = [&](int nb, int ks) {
+          u32x2_t part[2];
 #pragma unroll
-        for (int nbi = 0; nbi < NNB; ++nbi) {
-          const int nb = nb0 + nbi;
-          f32x16_t acc[NDW];
-#pragma unroll
-          for (int j = 0; j < NDW; ++j) acc[j] = f32x16_t{};
-#pragma unroll
-          for (int ks = 0; ks < KM; ++ks) {
-            u32x2_t part[2];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
-              const int col = 32 * nb + 16 * (lg & 1) + 4 * (li & 3);
-              const int pc = (col >> 3) ^ kv_swz<64>(row);
-              part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                                                        (lds_bf16x4*)(bsrc + row * (TILE * 2) + pc * 16 +
-                                                                      (col & 7) * 2)));
-            }
-            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]});
-#pragma unroll
-            for (int j = 0; j < NDW; ++j) acc[j] = mfma32x32x16(ast[j][ks], bop, acc[j]);
+          for (int q = 0; q < 2; ++q) {
+            const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+            const int col = 32 * nb + 16 * (lg & 1) + 4 * (li & 3);
+            const int pc = (col >> 3) ^ kv_swz<64>(row);
+            part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                      (lds_bf16x4*)(bsrc + row * (TILE * 2) + pc * 16 + (col & 7) * 2)));
           }
-          // register r of lane half hh: d = 32*db + 16*(r/8) + 8*hh + r%8, token 32*nb + l32
+          return __builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]});
+        };
+        // register r of lane half hh: d = 32*db + 16*(r/8) + 8*hh + r%8, token 32*nb + l32
+        auto stage_out = [&](int nb, const f32x16_t* acc) {
           const int n = 32 * nb + l32;
 #pragma unroll
           for (int j = 0; j < NDW; ++j)
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
               const f32x16_t& v = acc[j];
-              const u32x4_t w = {pack_bf16x2(osc * v[8 * g + 0], osc * v[8 * g + 1]),
-                                 pack_bf16x2(osc * v[8 * g + 2], osc * v[8 * g + 3]),
-                                 pack_bf16x2(osc * v[8 * g + 4], osc * v[8 * g + 5]),
-                                 pack_bf16x2(osc * v[8 * g + 6], osc * v[8 * g + 7])};
+              const u32x4_t w = {pack_bf16x2(v[8 * g + 0], v[8 * g + 1]), pack_bf16x2(v[8 * g + 2], v[8 * g + 3]),
+                                 pack_bf16x2(v[8 * g + 4], v[8 * g + 5]), pack_bf16x2(v[8 * g + 6], v[8 * g + 7])};
               const int ch = 4 * (db0 + j) + 2 * g + hh;
               st16(stg + n * ROWB + (ch ^ out_swz(n)) * 16, w);
             }
+        };
+        // all B operands of the wave in registers at once (M <= 128: 64 VGPRs at most)
+        constexpr bool PRE = M <= 128 && NNB * KM * 4 <= 64;
+        if constexpr (PRE) {
+          // every read issued first, then NNB x NDW independent accumulation chains interleaved
+          bf16x8_t bop[NNB][KM];
+#pragma unroll
+          for (int ks = 0; ks < KM; ++ks)
+#pragma unroll
+            for (int nbi = 0; nbi < NNB; ++nbi) bop[nbi][ks] = bload(nb0 + nbi, ks);
+          f32x16_t acc[NNB][NDW];
+#pragma unroll
+          for (int nbi = 0; nbi < NNB; ++nbi)
+#pragma unroll
+            for (int j = 0; j < NDW; ++j) acc[nbi][j] = f32x16_t{};
+#pragma unroll
+          for (int ks = 0; ks < KM; ++ks)
+#pragma unroll
+            for (int nbi = 0; nbi < NNB; ++nbi)
+#pragma unroll
+              for (int j = 0; j < NDW; ++j) acc[nbi][j] = mfma32x32x16(ast[j][ks], bop[nbi][ks], acc[nbi][j]);
+#pragma unroll
+          for (int nbi = 0; nbi < NNB; ++nbi) stage_out(nb0 + nbi, acc[nbi]);
+        } else {
+#pragma unroll
+          for (int nbi = 0; nbi < NNB; ++nbi) {
+            f32x16_t acc[NDW];
+#pragma unroll
+            for (int j = 0; j < NDW; ++j) acc[j] = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KM; ++ks) {
+              const bf16x8_t bop = bload(nb0 + nbi, ks);
+#pragma unroll
+              for (int j = 0; j < NDW; ++j) acc[j] = mfma32x32x16(ast[j][ks], bop, acc[j]);
+            }
+            stage_out(nb0 + nbi, acc);
+          }
         }
       }
       barrier_lds();
-      // ---- whole rows out: dK from the K slot, dV from the V slot ----
-      for (int f = tid; f < 2 * TILE * CPR; f += 64 * NW) {
-        const int tsr = f / (TILE * CPR);
-        const int r = (f / CPR) % TILE, ch = f % CPR;
-        if (r < nrows) {
-          u32x4_t v = ld16((tsr ? vst : kst) + r * ROWB + (ch ^ out_swz(r)) * 16);
-          uint16_t* dst = (tsr ? dVg : dKg) + (int64_t)(t0 + r) * D + 8 * ch;
-          if (!tsr && a.accumulate_dk) {
-            // dK += this gradient (another product already wrote its share)
-            const u32x4_t o = ld16(dst);
+      // ---- whole rows out: dK from the K slot, dV from the V slot; each thread
+      // owns CPT fixed 16-byte chunks (the first half in dK) ----
+      {
+        const bool whole = nrows == TILE;
+        const int64_t tb = (int64_t)t0 * D;
+        u32x4_t prev[CPT / 2];
+        if (a.accumulate_dk) {
+          // dK += this gradient (another product already wrote its share): old rows first
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(o[e]), bf16hi(v[e]) + bf16hi(o[e]));
+          for (int i = 0; i < CPT / 2; ++i)
+            if (whole || r0 + RSTEP * i < nrows) prev[i] = ld16(dKg + tb + off0 + RSTEP * D * i);
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          const bool isv = i >= CPT / 2;
+          const int k = i % (CPT / 2);
+          if (whole || r0 + RSTEP * k < nrows) {
+            u32x4_t v = ld16((isv ? vst : kst) + lds0 + RSTEP * ROWB * k);
+            if (!isv && a.accumulate_dk) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(prev[k][e]), bf16hi(v[e]) + bf16hi(prev[k][e]));
+            }
+            st16((isv ? dVg : dKg) + tb + off0 + RSTEP * D * k, v);
           }
-          st16(dst, v);
         }
       }
     }
@@ -761,13 +808,19 @@ static hipError_t launch_kv_dq(const BwdArgs& a, hipStream_t s) {
       case 32: return launch_kv_t<128, 32, 4, 3, DQ>(a, s);
       case 64: return launch_kv_t<128, 64, 4, 3, DQ>(a, s);
       case 128: return launch_kv_t<128, 128, 4, 3, DQ>(a, s);
-      case 256: return launch_kv_t<128, 256, 8, 2, DQ>(a, s);
+      case 256:   // no fused query gradient here (bwd_kv_fuses_dq): it would not fit the registers
+        if constexpr (!DQ) return launch_kv_t<128, 256, 8, 2, false>(a, s);
+        break;
     }
   }
   return hipErrorInvalidValue;
 }
 
 bool bwd_kv_fuses_dq(int M, int D) { return !(M == 256 && D == 128); }
+
+// D=64 with M<=128: 4 waves of <=248 VGPRs and <=80 KB of LDS, so two per CU;
+// the other shapes need more than half the LDS or all 256 VGPRs per lane
+int bwd_kv_blocks_per_cu(int M, int D) { return D == 64 && M <= 128 ? 2 : 1; }
 
 hipError_t launch_bwd_kv_mfma(const BwdArgs& a, bool with_dq, hipStream_t s) {
   return with_dq ? launch_kv_dq<true>(a, s) : launch_kv_dq<false>(a, s);
