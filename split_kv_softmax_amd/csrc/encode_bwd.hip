@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swap_bits2(int x) { return ((x & 1) << 1) | (x >> 1); }
 
-template <int D, int M, int NW, int S, bool DQ>
+template <int D, int M, int NW, int S, bool DQ, bool ACC>
 __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   constexpr int TILE = 64;
   constexpr int ROWB = 2 * D;          // bytes of one K/V/gradient row
@@ -531,14 +531,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
     const uint64_t bits = ring[0];
     const int t0 = t_begin + t * TILE;
     const int nrows = t_end - t0 < TILE ? t_end - t0 : TILE;
+    const bool whole = nrows == TILE;
+    const int64_t tb = (int64_t)t0 * D;
     if (!bits) {
       // no valid token: zero gradient rows, nothing loaded
-      const int64_t tb = (int64_t)t0 * D;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const bool isv = i >= CPT / 2;
         const int k = i % (CPT / 2);
-        if (r0 + RSTEP * k < nrows && (isv || !a.accumulate_dk))
+        if (r0 + RSTEP * k < nrows && (isv || !ACC))
           st16((isv ? dVg : dKg) + tb + off0 + RSTEP * D * k, u32x4_t{0, 0, 0, 0});
       }
     } else {
@@ -624,6 +625,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
         }
       }
       barrier_lds();
+      // ACC: dK += this gradient (another product already wrote its share); the
+      // old rows are read here so the loads overlap phase B.  A separate
+      // instantiation, so that the kernel without them has no register-tracked
+      // load in its loop (before reusing such registers the compiler waits for
+      // every outstanding load, the ring's included).
+      u32x4_t prev[ACC ? CPT / 2 : 1];
+      if constexpr (ACC) {
+#pragma unroll
+        for (int k = 0; k < CPT / 2; ++k) {   // rows past the chunk read row 0 (in range, unused)
+          const int rk = r0 + RSTEP * k;
+          prev[k] = ld16(dKg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0);
+        }
+      }
       // ---- phase B: this wave's output blocks, staged into the tile's K/V slot ----
       {
         const uint8_t* bsrc = tsel == 0 ? pbuf : dsbuf;
@@ -697,28 +711,24 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       // ---- whole rows out: dK from the K slot, dV from the V slot; each thread
       // owns CPT fixed 16-byte chunks (the first half in dK) ----
       {
-        const bool whole = nrows == TILE;
-        const int64_t tb = (int64_t)t0 * D;
-        u32x4_t prev[CPT / 2];
-        if (a.accumulate_dk) {
-          // dK += this gradient (another product already wrote its share): old rows first
+        if constexpr (ACC) {
+          // consume the old rows on every path here, so that the compiler's wait for
+          // them sits in this block and no load is left pending into the next tile
 #pragma unroll
-          for (int i = 0; i < CPT / 2; ++i)
-            if (whole || r0 + RSTEP * i < nrows) prev[i] = ld16(dKg + tb + off0 + RSTEP * D * i);
+          for (int k = 0; k < CPT / 2; ++k) asm volatile("" ::"v"(prev[k]));
         }
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
+          // read and add on every row (the staging holds all 64), store only rows in the chunk
           const bool isv = i >= CPT / 2;
           const int k = i % (CPT / 2);
-          if (whole || r0 + RSTEP * k < nrows) {
-            u32x4_t v = ld16((isv ? vst : kst) + lds0 + RSTEP * ROWB * k);
-            if (!isv && a.accumulate_dk) {
+          u32x4_t v = ld16((isv ? vst : kst) + lds0 + RSTEP * ROWB * k);
+          if (ACC && !isv) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(prev[k][e]), bf16hi(v[e]) + bf16hi(prev[k][e]));
-            }
-            st16((isv ? dVg : dKg) + tb + off0 + RSTEP * D * k, v);
+            for (int e = 0; e < 4; ++e)
+              v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(prev[k][e]), bf16hi(v[e]) + bf16hi(prev[k][e]));
           }
+          if (whole || r0 + RSTEP * k < nrows) st16((isv ? dVg : dKg) + tb + off0 + RSTEP * D * k, v);
         }
       }
     }
@@ -790,7 +800,10 @@ hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s) {
 template <int D, int M, int NW, int S, bool DQ>
 static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
-  hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  if (a.accumulate_dk)
+    hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ, false>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
