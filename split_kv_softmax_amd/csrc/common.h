@@ -165,6 +165,19 @@ __device__ __forceinline__ void wait_tiles(int later) {
   wait_vm<0>();
 }
 
+// Wait until at most n (wave-uniform, 0 <= n) of this wave's vector-memory
+// operations are pending; n above NMAX waits as for NMAX.
+template <int NMAX>
+__device__ __forceinline__ void wait_vm_le(int n) {
+  static_assert(NMAX >= 0 && NMAX < 64, "vmcnt range");
+  if constexpr (NMAX == 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= NMAX) { wait_vm<NMAX>(); return; }
+    wait_vm_le<NMAX - 1>(n);
+  }
+}
+
 // Wait until at most k * UNIT of this wave's vector-memory operations are
 // pending (k = 0 .. KMAX, uniform); the immediate must be a constant, hence
 // the table.  Counts beyond the counter's range wait for 63, which is

@@ -397,6 +397,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   constexpr int NNB = DB >= WPT ? 2 : 2 * DB / WPT;
   constexpr int CPT = 2 * TILE * CPR / (64 * NW);   // copy-out chunks per thread
   static_assert(CPT % 2 == 0 && CPT * 64 * NW == 2 * TILE * CPR, "copy-out split");
+  static_assert((S - 2) * OPS + (S - 1) * CPT < 64, "vmcnt range");
   static_assert(NI % NW == 0, "loads must split evenly over the waves");
   static_assert(MW <= NW && NW % 2 == 0 && WPT <= 2 * DB, "wave layout");
   static_assert(OPS * (S - 2) < 64, "vmcnt range");
@@ -521,10 +522,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   const int off0 = r0 * D + 8 * ch0;
   const int swk = kv_swz<D>(swap23(l32));   // rows 32*b2 + swap23(l32)
   for (int t = 0; t < ntiles; ++t) {
+    // Tile t's loads are complete once at most the later tiles' loads and the
+    // stores of the (up to S-1) tiles since its issue are pending: every tile
+    // issues exactly CPT stores per wave (buffer stores, whose range check drops
+    // rows outside the chunk), and any loads of the accumulating variant only
+    // make the count conservative.
     int later = 0;
 #pragma unroll
     for (int k = 1; k < S - 1; ++k) later += ring[k] != 0ull;
-    wait_tiles<OPS, S>(later);
+    wait_vm_le<(S - 2) * OPS + (S - 1) * CPT>(later * OPS + (t < S - 1 ? t : S - 1) * CPT);
     barrier_lds();
     ring[S - 1] = tile_bits(t + S - 1);
     if (ring[S - 1]) issue(t + S - 1);
@@ -533,14 +539,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
     const int nrows = t_end - t0 < TILE ? t_end - t0 : TILE;
     const bool whole = nrows == TILE;
     const int64_t tb = (int64_t)t0 * D;
+    // the tile's gradient rows (bytes past the chunk are dropped); with ACC an
+    // empty tile leaves dK as it is (a zero-length range drops every store)
+    const __amdgpu_buffer_rsrc_t kout =
+        __builtin_amdgcn_make_buffer_rsrc(dKg + tb, 0, (ACC && !bits) ? 0 : nrows * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vout = __builtin_amdgcn_make_buffer_rsrc(dVg + tb, 0, nrows * ROWB, 0x00020000);
     if (!bits) {
       // no valid token: zero gradient rows, nothing loaded
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const bool isv = i >= CPT / 2;
         const int k = i % (CPT / 2);
-        if (r0 + RSTEP * k < nrows && (isv || !ACC))
-          st16((isv ? dVg : dKg) + tb + off0 + RSTEP * D * k, u32x4_t{0, 0, 0, 0});
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0, 0, 0, 0}, isv ? vout : kout, 2 * (off0 + RSTEP * D * k), 0,
+                                               kCachePolicyNT);
       }
     } else {
       uint8_t* kst = smem + (t % S) * STAGE;
@@ -728,7 +739,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
             for (int e = 0; e < 4; ++e)
               v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(prev[k][e]), bf16hi(v[e]) + bf16hi(prev[k][e]));
           }
-          if (whole || r0 + RSTEP * k < nrows) st16((isv ? dVg : dKg) + tb + off0 + RSTEP * D * k, v);
+          __builtin_amdgcn_raw_buffer_store_b128(v, isv ? vout : kout, 2 * (off0 + RSTEP * D * k), 0, kCachePolicyNT);
         }
       }
     }
