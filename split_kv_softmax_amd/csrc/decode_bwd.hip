@@ -222,17 +222,17 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
   constexpr int KS = D / 16;   // k-steps over the head dim
   constexpr int DB = D / 32;   // 32-row blocks of dXq^T
   constexpr int MS = M / 16;   // k-steps over the latents
-  constexpr int KLD = D + 8;   // padded latent rows (bf16 elements)
   constexpr int BLK = 32;
   constexpr int ROWB = 2 * D;
   constexpr int BB = BLK * ROWB;             // bytes of one tensor's block
   constexpr int NI = BB / 1024;              // direct loads per tensor and block
   constexpr int ST = NI + 2;                 // stores per block: dXq rows, log2-normaliser, delta
-  constexpr int MAXT = 8192;
-  __shared__ __attribute__((aligned(16))) uint16_t Kl[M * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Zr[M * KLD];
+  // latent rows unpadded, 16-byte chunk c of row m at c ^ kv_swz(m): conflict-free
+  // for the row reads of the score products and the transposing reads of dXq
+  __shared__ __attribute__((aligned(1024))) uint8_t Kl[M * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t Zr[M * ROWB];
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * S * 2 * BB];
-  __shared__ uint8_t tmask[MAXT];
+  auto lat = [](int m, int c) { return m * ROWB + ((c ^ kv_swz<D>(m)) * 16); };   // byte of chunk c, row m
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -247,22 +247,22 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
   const int n_lo = tb * a.tokens_per_block;
   const int n_hi = min(a.N, n_lo + a.tokens_per_block);
 
-  {  // stage latent keys and values (bf16 rows) and the token mask
+  {  // stage latent keys and values (bf16 rows)
     constexpr int T = 64 * NWV;
     const uint16_t* kg = static_cast<const uint16_t*>(a.Klat) + (int64_t)b * a.klat_bstride + (int64_t)h * M * D;
     const float* zg = a.Z + bh * (int64_t)M * D;
     for (int f = tid; f < M * D / 8; f += T) {
       const int m = f / (D / 8), c = f % (D / 8);
-      st16(&Kl[m * KLD + 8 * c], ld16(kg + 8 * (int64_t)f));
+      st16(Kl + lat(m, c), ld16(kg + 8 * (int64_t)f));
       const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zg + 8 * (int64_t)f);
       const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zg + 8 * (int64_t)f + 4);
-      st16(&Zr[m * KLD + 8 * c], u32x4_t{pack_bf16x2(z0[0], z0[1]), pack_bf16x2(z0[2], z0[3]),
-                                         pack_bf16x2(z1[0], z1[1]), pack_bf16x2(z1[2], z1[3])});
+      st16(Zr + lat(m, c), u32x4_t{pack_bf16x2(z0[0], z0[1]), pack_bf16x2(z0[2], z0[3]), pack_bf16x2(z1[0], z1[1]),
+                                   pack_bf16x2(z1[2], z1[3])});
     }
-    const uint8_t* tm = a.token_mask ? a.token_mask + (int64_t)b * a.N : nullptr;
-    for (int i = tid; i < n_hi - n_lo; i += T) tmask[i] = tm ? tm[n_lo + i] : (uint8_t)1;
   }
   __syncthreads();   // also completes the staging loads before the ring starts
+  // token validity: 64-bit words of the mask (scalar loads), or every token
+  const_u64* mw = a.mask_words ? (const_u64*)(a.mask_words + (int64_t)b * a.mask_words_stride) : nullptr;
 
   const uint16_t* Xg = static_cast<const uint16_t*>(a.Xq) + bh * (int64_t)a.N * D;
   const uint16_t* Gg = static_cast<const uint16_t*>(a.dY) + bh * (int64_t)a.N * D;
@@ -300,8 +300,20 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
     if (j < nb) issue(j, j);
 
   const int swx = tok_swz(D, l32);
-  const bf16x8_t ones_unused = {};
-  (void)ones_unused;
+  // latent-row read offsets: rows 32*mb + swap23(l32) share one swizzle, so the
+  // row block mb is an immediate offset; likewise the transposing reads' rows
+  // 16*ks + .. share one swizzle per (q, db)
+  int koff[KS], toff[2][DB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = lat(swap23(l32), 2 * ks + hh);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int row = 8 * (lg >> 1) + 4 * q + (li >> 2);
+      const int col = 32 * db + 16 * (lg & 1) + 4 * swap_bits2(li & 3);
+      toff[q][db] = lat(row, col >> 3) + (col & 7) * 2;
+    }
   for (int j0 = 0; j0 < nb; j0 += S)
 #pragma unroll
   for (int st = 0; st < S; ++st) {
@@ -329,14 +341,10 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
     for (int mb = 0; mb < MB; ++mb) {
       t[mb] = f32x16_t{};
       da[mb] = f32x16_t{};
-      const uint16_t* krow = &Kl[(32 * mb + swap23(l32)) * KLD + 8 * hh];
-      const uint16_t* zrow = &Zr[(32 * mb + swap23(l32)) * KLD + 8 * hh];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 16 * ks)),
-                             xop[ks], t[mb]);
-        da[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)),
-                              gop[ks], da[mb]);
+        t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Kl + 32 * mb * ROWB + koff[ks])), xop[ks], t[mb]);
+        da[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Zr + 32 * mb * ROWB + koff[ks])), gop[ks], da[mb]);
       }
     }
     float mx = t[0][0];
@@ -388,17 +396,14 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
       for (int ks = 0; ks < MS; ++ks) {
         u32x2_t part[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
-          const int col = 32 * db + 16 * (lg & 1) + 4 * swap_bits2(li & 3);
-          part[q] = __builtin_bit_cast(u32x2_t,
-                                       __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)&Kl[row * KLD + col]));
-        }
+        for (int q = 0; q < 2; ++q)
+          part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                    (lds_bf16x4*)(Kl + 16 * ks * ROWB + toff[q][db])));
         acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]}),
                                dtk[ks], acc[db]);
       }
     }
-    const bool keep = inb && tmask[inb ? n - n_lo : 0] != 0;
+    const bool keep = inb && (!mw || ((mw[n0 >> 6] >> ((n0 & 63) + l32)) & 1ull));
     // stage dXq rows (register group g of lane half hh: dims 32*db + 16*g + 8*hh ..) in the consumed Xq slot
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -679,12 +684,14 @@ bool decode_bwd_mfma_supported(int M, int D) {
   return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128);
 }
 
-int decode_bwd_waves(int D) { return D == 64 ? 4 : 2; }
+// token-side waves per workgroup: at D=64 eight waves with 2-stage rings fill the
+// LDS (128 KB of rings, up to 32 KB of latents), two waves per SIMD
+int decode_bwd_waves(int D) { return D == 64 ? 8 : 2; }
 
 template <int D, int MB>
 static hipError_t launch_dbwd_t(const DecBwdArgs& a, hipStream_t s) {
-  constexpr int NWV = D == 64 ? 4 : 2;
-  constexpr int S = D == 64 ? 3 : 2;
+  constexpr int NWV = D == 64 ? 8 : 2;
+  constexpr int S = 2;
   const int64_t nblk = (a.N + a.tokens_per_block - 1) / a.tokens_per_block;
   hipLaunchKernelGGL((dbwd_tok_mfma_kernel<D, MB, NWV, S>), dim3((unsigned)(nblk * a.H * a.B)), dim3(64 * NWV), 0,
                      s, a);
