@@ -82,6 +82,7 @@ struct EncodePlan {
   size_t mw_bytes = 0;    // validity words of the padding mask (matrix-core path)
   int64_t mw_stride = 0;  // words per batch row
   size_t o_bytes = 0;     // partial outputs of split partitions
+  size_t order_bytes = 0; // heavy-first launch order (masked matrix-core path)
   size_t ws_bytes = 0;
 };
 
@@ -90,6 +91,10 @@ int env_int(const char* name, int dflt) {
   if (!v || !*v) return dflt;
   return atoi(v);
 }
+
+// Masked inputs launch their blocks heaviest first (valid-token count per
+// chunk); FLARE_HEAVY_FIRST=0 keeps the plain block order.
+bool heavy_first_enabled() { return env_int("FLARE_HEAVY_FIRST", 1) != 0; }
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -153,7 +158,10 @@ EncodePlan plan_encode(flare_dtype dt, int B, int H, int N, int M, int D, int R,
   }
   if (p.nslots) p.o_bytes = align256((size_t)p.nslots * per * D * sizeof(float));
   const size_t l_bytes = p.nslots ? align256((size_t)p.nslots * per * sizeof(float)) : 0;
-  p.ws_bytes = p.mw_bytes + p.o_bytes + l_bytes;
+  const int launch_chunks = std::min<int>(kMaxChunks, (int)p.chunks.size());
+  if (p.mw_bytes && launch_chunks > 0 && (int64_t)B * launch_chunks <= kMaxOrderItems)
+    p.order_bytes = align256((size_t)B * H * launch_chunks * sizeof(int32_t));
+  p.ws_bytes = p.mw_bytes + p.o_bytes + l_bytes + p.order_bytes;
   return p;
 }
 
@@ -255,6 +263,13 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, 
     }
     a.tab.bnd[n] = plan.chunks[c0 + n - 1].hi;
     hipError_t e;
+    a.order = nullptr;
+    if (plan.order_bytes && heavy_first_enabled() && (int64_t)B * n <= kMaxOrderItems) {
+      int32_t* order = reinterpret_cast<int32_t*>(ws + plan.ws_bytes - plan.order_bytes);
+      e = launch_heavy_first(a.mask_words, a.mask_words_stride, a.tab, B, H, order, s);
+      if (e != hipSuccess) return hip_fail(e, "launch-order launch");
+      a.order = order;
+    }
     switch (plan.kind) {
       case EncKind::Mfma: e = launch_encode_mfma(a, s); break;
       case EncKind::Q1: e = launch_encode_q1(a, s); break;
@@ -380,7 +395,7 @@ namespace {
 struct BwdPlan {
   bool mfma = false;
   std::vector<int32_t> bnd;   // chunk boundaries over [0, N)
-  size_t c_bytes = 0, mw_bytes = 0, dq_bytes = 0, ws_bytes = 0;
+  size_t c_bytes = 0, mw_bytes = 0, dq_bytes = 0, order_bytes = 0, ws_bytes = 0;
   int64_t mw_stride = 0;
 };
 
@@ -392,7 +407,9 @@ BwdPlan plan_bwd(flare_dtype dt, int B, int H, int N, int M, int D, bool masked)
     // as many workgroups as the CUs hold at once (one or two per CU, by the
     // key/value kernel's registers and LDS), chunks of whole tiles
     const int64_t bh = std::max<int64_t>(1, (int64_t)B * H);
-    const int64_t slots = 256 * (int64_t)bwd_kv_blocks_per_cu(M, D);
+    // masked inputs: twice the chunks, launched heaviest first, so that the
+    // uneven valid lengths even out over the CUs
+    const int64_t slots = 256 * (int64_t)bwd_kv_blocks_per_cu(M, D) * (masked ? 2 : 1);
     int64_t per = std::max<int64_t>(1, (slots + bh - 1) / bh);
     int64_t len = ((N + per - 1) / per + 63) / 64 * 64;
     len = std::max<int64_t>(len, 1024);
@@ -406,9 +423,10 @@ BwdPlan plan_bwd(flare_dtype dt, int B, int H, int N, int M, int D, bool masked)
     if (masked) {
       p.mw_stride = (N + 63) / 64 + 1;
       p.mw_bytes = align256((size_t)B * p.mw_stride * sizeof(uint64_t));
+      if ((int64_t)B * nslots <= kMaxOrderItems) p.order_bytes = align256((size_t)B * H * nslots * sizeof(int32_t));
     }
   }
-  p.ws_bytes = p.c_bytes + p.mw_bytes + p.dq_bytes;
+  p.ws_bytes = p.c_bytes + p.mw_bytes + p.dq_bytes + p.order_bytes;
   return p;
 }
 
@@ -537,6 +555,12 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   a.tab.nchunks = nc;
   for (int i = 0; i <= nc; ++i) a.tab.bnd[i] = plan.bnd[i];
   for (int i = 0; i < nc; ++i) a.tab.slot[i] = (int16_t)i;
+  if (plan.order_bytes && heavy_first_enabled()) {
+    int32_t* order = reinterpret_cast<int32_t*>(ws + plan.c_bytes + plan.mw_bytes + plan.dq_bytes);
+    e = launch_heavy_first(a.mask_words, a.mask_words_stride, a.tab, B, H, order, s);
+    if (e != hipSuccess) return hip_fail(e, "launch-order launch");
+    a.order = order;
+  }
   // one pass over K, V where the registers allow the fused kernel, else a
   // separate query-gradient pass; both leave per-chunk partials for the reduce
   const bool fuse = bwd_kv_fuses_dq(M, D);

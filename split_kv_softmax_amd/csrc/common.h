@@ -197,6 +197,12 @@ __device__ __forceinline__ void wait_units(int k) {
 // Validity bits of the 64 tokens [t0, t0+64) of batch row `mw` (aligned words),
 // read through the constant address space so they become scalar loads.
 typedef __attribute__((address_space(4))) const uint64_t const_u64;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+// Block index of this workgroup through an optional launch order (scalar load).
+__device__ __forceinline__ int ordered_block(const int32_t* order) {
+  return order ? ((const_i32*)order)[blockIdx.x] : (int)blockIdx.x;
+}
 __device__ __forceinline__ uint64_t mask_tile_bits(const_u64* mw, int t0) {
   const int w = t0 >> 6, sh = t0 & 63;
   const uint64_t lo = mw[w];

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
   const int grp = wv / NW, wave = wv % NW;                 // token group, row wave
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int nch = a.tab.nchunks;
-  int bid = blockIdx.x;
+  int bid = ordered_block(a.order);
   const int c = bid % nch;
   bid /= nch;
   const int h = bid % a.H;
@@ -515,6 +515,44 @@ __global__ __launch_bounds__(256) void mask_words_kernel(const uint8_t* __restri
     if (t < N && mr[t] != 0) bits |= 1ull << i;
   }
   words[idx] = bits;
+}
+
+// One workgroup: valid-token count of every (batch, chunk) pair from the mask
+// words, rank by counting (heavier first, ties by index), then the order table.
+__global__ __launch_bounds__(1024) void heavy_first_kernel(const uint64_t* __restrict__ words, int64_t stride,
+                                                           const ChunkTable tab, int B, int H,
+                                                           int32_t* __restrict__ order) {
+  __shared__ int key[kMaxOrderItems];
+  const int nch = tab.nchunks, n = B * nch;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int b = i / nch, c = i % nch;
+    const int lo = tab.bnd[c], hi = tab.bnd[c + 1];
+    const uint64_t* w = words + (int64_t)b * stride;
+    int cnt = 0;
+    for (int k = lo >> 6; k <= (hi - 1) >> 6 && lo < hi; ++k) {
+      uint64_t x = w[k];
+      const int a0 = lo - 64 * k, a1 = hi - 64 * k;   // keep bits [a0, a1) of this word
+      if (a0 > 0) x &= ~0ull << a0;
+      if (a1 < 64) x &= (1ull << a1) - 1ull;
+      cnt += __popcll(x);
+    }
+    key[i] = cnt;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int ki = key[i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += (key[j] > ki) || (key[j] == ki && j < i);
+    const int b = i / nch, c = i % nch;
+    for (int h = 0; h < H; ++h) order[rank * H + h] = (b * H + h) * nch + c;
+  }
+}
+
+hipError_t launch_heavy_first(const uint64_t* mask_words, int64_t mw_stride, const ChunkTable& tab, int B, int H,
+                              int32_t* order, hipStream_t s) {
+  if (B * tab.nchunks > kMaxOrderItems || B * tab.nchunks == 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(heavy_first_kernel, dim3(1), dim3(1024), 0, s, mask_words, mw_stride, tab, B, H, order);
+  return hipGetLastError();
 }
 
 hipError_t launch_mask_words(const uint8_t* mask, int B, int N, uint64_t* words, int64_t stride, hipStream_t s) {

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int nch = a.tab.nchunks;
-  int bid = blockIdx.x;
+  int bid = ordered_block(a.order);
   const int c = bid % nch;
   bid /= nch;
   const int h = bid % a.H;
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int lg = lane >> 4, li = lane & 15;
   const int nch = a.tab.nchunks;
-  int bid = blockIdx.x;
+  int bid = ordered_block(a.order);
   const int c = bid % nch;
   bid /= nch;
   const int h = bid % a.H;

@@ -35,6 +35,7 @@ struct EncodeArgs {
   float scale;        // s
   float scale_log2;   // s * log2(e)
   ChunkTable tab;
+  const int32_t* order;   // launch order of the (b, h, chunk) blocks, heaviest first, or null
 };
 
 // Group g folds input states [in_begin[g], in_begin[g+1]) of `in` into output
@@ -92,6 +93,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   ChunkTable tab;               // token chunks (matrix-core path)
+  const int32_t* order;         // launch order of the (b, h, chunk) blocks, heaviest first, or null
 };
 
 struct DecBwdArgs {
@@ -125,6 +127,15 @@ bool encode_q1_supported(int M, int D);
 hipError_t launch_encode_q1(const EncodeArgs& a, hipStream_t s);
 hipError_t launch_encode_generic(const EncodeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_mask_words(const uint8_t* mask, int B, int N, uint64_t* words, int64_t stride, hipStream_t s);
+// Heavy-first launch order for masked inputs.  Block (b, h, c) of a chunked
+// launch is numbered (b*H + h)*nchunks + c; order[i] is the block that the i-th
+// launched workgroup runs.  The (batch, chunk) pairs are ranked by their count
+// of valid tokens (descending, ties in index order), every head of a pair
+// following it, so that the long chunks start first and the short ones fill in.
+// At most kMaxOrderItems pairs (B * nchunks); order holds B*H*nchunks entries.
+constexpr int kMaxOrderItems = 1024;
+hipError_t launch_heavy_first(const uint64_t* mask_words, int64_t mw_stride, const ChunkTable& tab, int B, int H,
+                              int32_t* order, hipStream_t s);
 
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 

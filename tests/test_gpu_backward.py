@@ -140,3 +140,20 @@ def test_backward_is_deterministic():
     b = _run(w, x)
     for u, v in zip(a[2:], b[2:]):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("M,D", [(128, 64), (256, 128)])
+def test_heavy_first_launch_order_changes_no_bit(M, D, monkeypatch):
+    """Masked inputs launch their chunks heaviest first; each chunk writes its own
+    state and partial, so the forward states and all gradients are the same bits
+    with the plain block order."""
+    w, x = _masked_case(M, D, N=16384, R=4, B=3, wid=1990)
+    outs = []
+    for flag in ("1", "0"):
+        monkeypatch.setenv("FLARE_HEAVY_FIRST", flag)
+        O, Lp = fl.encode(x["Q"], x["K"], x["V"], w.offsets, x["mask"], w.scale)
+        outs.append((O, Lp) + _run(w, x))
+    torch.cuda.synchronize()
+    for u, v in zip(*outs):
+        assert torch.equal(u, v)
+    _check(w, x, *outs[0][2:])
