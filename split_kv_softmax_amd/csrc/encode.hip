@@ -18,6 +18,80 @@
 
 namespace flare {
 
+// Combine the G token groups' states of one chunk in LDS (the rings are idle
+// by then) and store the chunk's normalised state: group g's lanes write their
+// reference maximum, row sum and unnormalised accumulators; group 0 merges them
+// in group order, normalises and writes O and L (to the output partition or to
+// a workspace slot of a split partition).
+template <int D, int NW, int G>
+__device__ __forceinline__ void finish_chunk(uint8_t* smem, const EncodeArgs& a, int grp, int wave, int lane,
+                                             f32x16_t (&o)[D / 32], float m_run, float l_tot, int b, int h,
+                                             int c) {
+  constexpr int DB = D / 32;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const float c2 = a.scale_log2;
+  if constexpr (G > 1) {
+    // ---- combine the G groups' states in LDS (the rings are idle now):
+    // group g's lane writes its reference max, row sum and unnormalised
+    // accumulators; group 0 merges them in group order.
+    barrier_lds();
+    float* cb = reinterpret_cast<float*>(smem);
+    float* cm = cb + G * NW * 32 * 64;
+    float* cl = cm + G * NW * 64;
+    const int slot = grp * NW + wave;
+    if (grp > 0) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cb[(slot * 32 + 16 * db + r) * 64 + lane] = o[db][r];
+      cm[slot * 64 + lane] = m_run;
+      cl[slot * 64 + lane] = l_tot;
+    }
+    barrier_lds();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < G; ++g) {
+      const int sg = g * NW + wave;
+      const float mg = cm[sg * 64 + lane];
+      const float lg2 = cl[sg * 64 + lane];
+      const float mn = fmaxf(m_run, mg);
+      if (mn == kNegInf) continue;                       // both empty
+      const float fa = fast_exp2((m_run - mn) * c2);     // 0 for an empty side
+      const float fb = fast_exp2((mg - mn) * c2);
+      l_tot = l_tot * fa + lg2 * fb;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * fa + cb[(sg * 32 + 16 * db + r) * 64 + lane] * fb;
+      m_run = mn;
+    }
+  }
+
+  // ---- normalise and store this chunk's state
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : 1.f / l_tot;
+  const int slot = a.tab.slot[c];
+  float* Ob;
+  float* Lb;
+  if (slot < 0) {
+    const int r = -slot - 1;
+    Ob = a.O_part + (((int64_t)r * a.B + b) * a.H + h) * (int64_t)a.M * D;
+    Lb = a.L_part + (((int64_t)r * a.B + b) * a.H + h) * (int64_t)a.M;
+  } else {
+    Ob = a.ws_O + (((int64_t)slot * a.B + b) * a.H + h) * (int64_t)a.M * D;
+    Lb = a.ws_L + (((int64_t)slot * a.B + b) * a.H + h) * (int64_t)a.M;
+  }
+  const int m = 32 * wave + l32;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4_t v = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv};
+      *reinterpret_cast<f32x4_t*>(Ob + (int64_t)m * D + 32 * db + 8 * q + 4 * hh) = v;
+    }
+  if (hh == 0) Lb[m] = empty ? kNegInf : (m_run * a.scale + __logf(l_tot));
+}
+
 // ---------------------------------------------------------------------------
 // bf16 matrix-core encoder.  One workgroup = one (batch, head, chunk) and all
 // M = 32*NW latent rows, so each K/V byte is read from HBM exactly once.
@@ -351,66 +425,329 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
   }
 
   float l_tot = RS ? lacc[0] : l_run + __shfl_xor(l_run, 32, 64);
-  if constexpr (G > 1) {
-    // ---- combine the G groups' states in LDS (the rings are idle now):
-    // group g's lane writes its reference max, row sum and unnormalised
-    // accumulators; group 0 merges them in group order.
-    barrier_lds();
-    float* cb = reinterpret_cast<float*>(smem);
-    float* cm = cb + G * NW * 32 * 64;
-    float* cl = cm + G * NW * 64;
-    const int slot = grp * NW + wave;
-    if (grp > 0) {
+  finish_chunk<D, NW, G>(smem, a, grp, wave, lane, o, m_run, l_tot, b, h, c);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 matrix-core encoder for inputs without a padding mask, pipelined by two
+// tiles.  Same data flow as encode_mfma_kernel (one workgroup = one (batch,
+// head, chunk) and all M rows; G token groups of NW waves, each with its own
+// ring), but each wave's round u holds independent pieces of work:
+//   * the weighted values of tile u          (matrix cores; weights from round u-1),
+//   * the online softmax of tile u+1         (vector ALUs; scores from round u-1),
+//     and the row sums of its weights        (matrix cores),
+//   * the scores of tile u+2                 (matrix cores).
+// Instruction-group barriers interleave the products of a round with its
+// vector instructions, so the matrix cores work while the same wave issues
+// its exponentials (a wave that issues a run of products back to back stalls
+// on each one instead).
+//
+// The K ring runs two tiles ahead of the V ring: "batch" u carries K(u+2) and
+// V(u) into K slot (u+2)%S and V slot u%S, and round u issues batch u+S-1 once
+// the round's barrier shows every wave past round u-1 (the last reader of both
+// slots).  Rows past the chunk re-read row 0 of the tile (finite values whose
+// weights are exactly 0), so a partial tile only masks its scores.
+// ---------------------------------------------------------------------------
+template <int D, int NW, int S, int G>
+__global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArgs a) {
+  constexpr int TILE = 64;
+  constexpr int ROWB = 2 * D;              // bytes per row
+  constexpr int TB = TILE * ROWB;          // bytes of a K (or V) tile
+  constexpr int RING = 2 * S * TB;         // S K slots, then S V slots
+  constexpr int NI = TB / 1024;            // 1 KB direct loads per tile and tensor
+  constexpr int NJ = NI / NW;              // ... issued by each wave
+  constexpr int KS = D / 16;               // k-steps of the score product
+  constexpr int DB = D / 32;               // 32-row blocks of O^T
+  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  static_assert(S >= 4 && 2 * NJ * (S - 1) < 64, "ring depth / vmcnt range");
+  static_assert(S * TB <= 65536, "slot offsets within a K or V ring are immediate LDS offsets");
+  static_assert(G == 1 || (G * NW * 32 * 64 + 2 * G * NW * 64) * 4 <= G * RING,
+                "the combine buffer reuses the rings");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[G * RING];
+
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv / NW, wave = wv % NW;
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lg = lane >> 4, li = lane & 15;
+  const int nch = a.tab.nchunks;
+  int bid = blockIdx.x;
+  const int c = bid % nch;
+  bid /= nch;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int t_begin = a.tab.bnd[c], t_end = a.tab.bnd[c + 1];
+  const int64_t bh = (int64_t)b * a.H + h;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + bh * (int64_t)a.N * D;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + bh * (int64_t)a.N * D;
+  const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + (int64_t)b * a.q_bstride +
+                       (int64_t)h * a.M * D;
+
+  bf16x8_t qop[KS];
+  {
+    const uint16_t* qrow = Qg + (int64_t)(32 * wave + l32) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qop[ks] = __builtin_bit_cast(bf16x8_t, ld16(qrow + 16 * ks));
+  }
+  wait_vm<0>();   // afterwards only the ring's loads are in flight
+
+  // Local tiles 0 .. ntg-1 of this group are chunk tiles grp, grp+G, ...; only
+  // the chunk's last tile can be partial.
+  const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
+  const int nrounds = (ntiles + G - 1) / G;   // the same for every wave: one barrier per round
+  const int ntg = ntiles > grp ? (ntiles - grp + G - 1) / G : 0;
+  const int tail = t_end - t_begin - (ntiles - 1) * TILE;   // tokens of the chunk's last tile
+  const bool owns_last = ntiles > 0 && (ntiles - 1) % G == grp;
+  auto nval = [&](int u) -> int {
+    if (u >= ntg) return 0;
+    return (u == ntg - 1 && owns_last) ? tail : TILE;
+  };
+
+  uint8_t* ring = smem + grp * RING;
+  const uint32_t ring_lds = lds_addr(ring);
+  uint32_t voff[NJ], voff0[NJ];
+  int vrow[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int byte = (wave + NW * j) * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    const int ch = pc ^ kv_swz<D>(r);
+    vrow[j] = r;
+    voff[j] = r * ROWB + ch * 16;
+    voff0[j] = ch * 16;
+  }
+  // K (is_v false) or V rows of local tile u into ring slot `slot`
+  auto issue = [&](int u, int slot, bool is_v) {
+    const int t0 = t_begin + (grp + G * u) * TILE;
+    const int nrows = t_end - t0;
+    const uint16_t* base = (is_v ? Vg : Kg) + (int64_t)t0 * D;
+    const uint32_t dst = ring_lds + (is_v ? S + slot : slot) * TB;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16_off(base, vrow[j] < nrows ? voff[j] : voff0[j], dst + (wave + NW * j) * 1024);
+  };
+
+  // Per-lane LDS addresses in slot 0; slots and k-steps are immediate offsets
+  // (the swizzle depends on the row modulo 16 only).
+  //  * score product, A operand: K row swap23(l32) (+32 per block), 16-byte chunk (2k+hh) ^ swizzle
+  //  * value product, A operand by transposing reads: in each 16-lane group lane i
+  //    points at token row (i/4) of a 4-token block and 4 head dims from 4*(i%4)
+  uint32_t kaddr[KS], vaddr[DB][2];
+  {
+    const int swk = kv_swz<D>(swap23(l32));
+#pragma unroll
+    for (int k = 0; k < KS; ++k) kaddr[k] = ring_lds + swap23(l32) * ROWB + (((2 * k + hh) ^ swk) * 16);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int n0 = 8 * (lg >> 1) + 4 * q + (li >> 2);
+        const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+        vaddr[db][q] = ring_lds + S * TB + n0 * ROWB + (((d0 >> 3) ^ kv_swz<D>(n0)) * 16) + (d0 & 7) * 2;
+      }
+  }
+  typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
+
+  const float c2 = a.scale_log2;
+  // Row sums on a 16x16x32 product: fed the weight operand of the 32x32x16
+  // product as its B, lane l contributes row l%32, tokens 8*(l/32)+0..7 as
+  // column l%16, contraction block l/16.  Selector rows 0 and 8 pick blocks 0
+  // and 2 (rows 0..15), rows 4 and 12 blocks 1 and 3 (rows 16..31), so that
+  // register 0 of lane l (result row 4*(l/16), column l%16) is the sum of
+  // row l%32: both lane halves hold their row's sum, like the softmax state.
+  // The other result registers stay 0.
+  bf16x8_t sel;
+  {
+    const int si = lane & 15, kb = lane >> 4;
+    const bool on = ((si == 0 || si == 8) && (kb & 1) == 0) || ((si == 4 || si == 12) && (kb & 1) == 1);
+    const uint32_t w = on ? 0x3f803f80u : 0u;
+    sel = __builtin_bit_cast(bf16x8_t, u32x4_t{w, w, w, w});
+  }
+
+  // scores of the tile in K slot `slot`: register r of lane half hh in block b2
+  // holds token 32*b2 + 16*(r/8) + 8*hh + r%8 of latent row l32
+  auto scores = [&](int slot, f32x16_t* sc) {
+    u32x4_t kop[KS][2];
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) kop[k][b2] = *(lds_u32x4*)(uintptr_t)(kaddr[k] + slot * TB + 32 * b2 * ROWB);
+    sc[0] = f32x16_t{};
+    sc[1] = f32x16_t{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, kop[k][b2]), qop[k], sc[b2]);
+  };
+  f32x16_t o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x16_t{};
+  float lsum = 0.f;          // running row sum of the weights (row l32, both lane halves)
+  // weighted values of the tile in V slot `slot` with weights pk
+  auto values = [&](int slot, const bf16x8_t* pk) {
+    u32x2_t part[4][DB][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cb[(slot * 32 + 16 * db + r) * 64 + lane] = o[db][r];
-      cm[slot * 64 + lane] = m_run;
-      cl[slot * 64 + lane] = l_tot;
+        for (int q = 0; q < 2; ++q)
+          part[ks][db][q] = __builtin_bit_cast(
+              u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                           (lds_bf16x4*)(uintptr_t)(vaddr[db][q] + slot * TB + 16 * ks * ROWB)));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4_t av = {part[ks][db][0][0], part[ks][db][0][1], part[ks][db][1][0], part[ks][db][1][1]};
+        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pk[ks], o[db]);
+      }
+  };
+  // scores of tokens at or past n of the tile become -inf (n = 0: a tile
+  // past the group's end, whose slots hold stale or never-written rows)
+  auto mask_tail = [&](f32x16_t* sc, int n) {
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tk = 32 * b2 + 16 * (r >> 3) + 8 * hh + (r & 7);
+        if (tk >= n) sc[b2][r] = kNegInf;
+      }
+  };
+  // Weights of a (masked) score tile against the reference maximum m_run:
+  // p = exp2(s log2(e) (score - m_run)) rounded to bf16, and the tile's row
+  // sums of the rounded weights (matrix cores).  The reference is not checked
+  // against the tile here: a tile whose row sum exceeds 2^12 (or is inf/NaN:
+  // no reference yet, or a score far above it) is redone by `rebase`, so every
+  // accepted weight is at most 2^12.
+  float m_run = kNegInf;     // reference maximum of row l32 (raw dot products)
+  float nmc = __builtin_huge_valf();   // -m_run s log2(e); +inf while m_run = -inf (forces a rebase)
+  auto weights = [&](const f32x16_t* sc, bf16x8_t* pk, float nm) -> float {
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sc[b2][8 * g + j], c2, nm));
+        const u32x4_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                           pack_bf16x2(p[6], p[7])};
+        pk[2 * b2 + g] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    f32x4_t ts = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < 4; ++ks) ts = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk[ks], ts, 0, 0, 0);
+    return ts[0];
+  };
+  constexpr float kSumMax = 4096.f;
+  // Rare path: rows whose tile sum failed the check move their reference to
+  // the tile's maximum (the online-softmax rescale of the value accumulators
+  // and the row sum by exp2(s log2(e) (m_old - m_new)), 0 from an empty
+  // state), then the tile's weights and sums are recomputed.
+  auto rebase = [&](const f32x16_t* sc, bf16x8_t* pk, float& ts) {
+    float mc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x16_t& v = sc[k >> 1];
+      const int r0 = 8 * (k & 1);
+      float x = fmax3(v[r0], v[r0 + 1], v[r0 + 2]);
+      x = fmax3(x, v[r0 + 3], v[r0 + 4]);
+      x = fmax3(x, v[r0 + 5], v[r0 + 6]);
+      mc[k] = fmax2(x, v[r0 + 7]);
     }
-    barrier_lds();
-    if (grp > 0) return;
+    float mx = fmax3(mc[0], mc[1], fmax2(mc[2], mc[3]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmax2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const bool bad = !(ts <= kSumMax);
+    const float m_new = (bad && mx != kNegInf) ? fmax2(mx, m_run) : m_run;
+    const float alpha = (m_new == m_run) ? 1.f : fast_exp2((m_run - m_new) * c2);   // 0 when m_run = -inf
+    lsum *= alpha;
 #pragma unroll
-    for (int g = 1; g < G; ++g) {
-      const int sg = g * NW + wave;
-      const float mg = cm[sg * 64 + lane];
-      const float lg2 = cl[sg * 64 + lane];
-      const float mn = fmaxf(m_run, mg);
-      if (mn == kNegInf) continue;                       // both empty
-      const float fa = fast_exp2((m_run - mn) * c2);     // 0 for an empty side
-      const float fb = fast_exp2((mg - mn) * c2);
-      l_tot = l_tot * fa + lg2 * fb;
+    for (int i = 0; i < DB; ++i) o[i] *= alpha;
+    m_run = m_new;
+    nmc = m_run == kNegInf ? __builtin_huge_valf() : -m_run * c2;
+    ts = weights(sc, pk, m_run == kNegInf ? 0.f : nmc);
+  };
+  auto softmax_tile = [&](const f32x16_t* sc, bf16x8_t* pk) {
+    float ts = weights(sc, pk, nmc);
+    if (__ballot(!(ts <= kSumMax))) rebase(sc, pk, ts);
+    lsum += ts;
+  };
+
+  // ---- V slots start as zeros: a round past the group's end multiplies
+  // weights that are exactly 0 with whatever its slot holds, which must not
+  // be NaN.  (Completed before the barrier that precedes the first load.)
+  for (int i = tid - grp * 64 * NW; i < S * TB / 16; i += 64 * NW)
+    st16(ring + S * TB + 16 * i, u32x4_t{0, 0, 0, 0});
+  barrier_lds();
+
+  // ---- prologue: K(0), K(1), then batches 0 .. S-3 (batch S-2 would reuse K(0)'s slot).
+  // Batch t holds (t+2 < ntg) + (t < ntg) loads of NJ each.
+  auto clampS2 = [](int x) { return x < 0 ? 0 : (x > S - 2 ? S - 2 : x); };
+  if (ntg > 0) issue(0, 0, false);
+  if (ntg > 1) issue(1, 1, false);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+  for (int k = 0; k < S - 2; ++k) {
+    if (k + 2 < ntg) issue(k + 2, (k + 2) % S, false);
+    if (k < ntg) issue(k, k % S, true);
+  }
+  wait_units<NJ, 2 * (S - 2)>(clampS2(ntg - 2) + clampS2(ntg));   // K(0), K(1) landed
+  barrier_lds();
+  // scores and weights of tile t live in buffer t % 2: round u reads the
+  // weights of tile u and the scores of tile u+1 and writes the weights of
+  // tile u+1 and the scores of tile u+2
+  f32x16_t scb[2][2];
+  bf16x8_t pkb[2][4];
+  {
+    scores(0, scb[0]);
+    scores(1, scb[1]);
+    if (nval(0) < TILE) mask_tail(scb[0], nval(0));
+    softmax_tile(scb[0], pkb[0]);
+  }
+  barrier_lds();             // every wave is done with K slots 0 and 1
+  if (S < ntg) issue(S, 0, false);
+  if (S - 2 < ntg) issue(S - 2, S - 2, true);
+
+  // ---- rounds, 2S per trip so that ring slots and buffer parities are
+  // compile-time constants
+  for (int u0 = 0; u0 < nrounds; u0 += 2 * S) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * fa + cb[(sg * 32 + 16 * db + r) * 64 + lane] * fb;
-      m_run = mn;
+    for (int sr = 0; sr < 2 * S; ++sr) {
+      const int u = u0 + sr, st = sr % S;
+      if (u < nrounds) {
+        // batch u = {K(u+2), V(u)} complete for this wave; batches u+1 .. u+S-2 may be in flight
+        wait_units<NJ, 2 * (S - 2)>(clampS2(ntg - u - 3) + clampS2(ntg - u - 1));
+        barrier_lds();
+        // every wave is past round u-1: K slot (u+1)%S and V slot (u-1)%S are free
+        if (u + S + 1 < ntg) issue(u + S + 1, (st + 1) % S, false);
+        if (u + S - 1 < ntg) issue(u + S - 1, (st + S - 1) % S, true);
+        const int e = sr % 2, f = 1 - e;     // tile u: buffer e; tile u+1: buffer f; tile u+2: buffer e
+        const int n1 = nval(u + 1);
+        if (n1 < TILE) mask_tail(scb[f], n1);
+        // one straight-line block: the value products of tile u, the weights
+        // of tile u+1 and their row sums, the score products of tile u+2
+        values(st, pkb[e]);
+        float ts = weights(scb[f], pkb[f], nmc);
+        scores((st + 2) % S, scb[e]);
+        // order: all operand reads (V, then K), a few exponentials while they
+        // arrive, then each product with exponentials and conversions between
+        // (vector groups take vector and transcendental instructions)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8 * DB + 2 * KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * DB + 2 * KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+        }
+        if (__ballot(!(ts <= kSumMax))) rebase(scb[f], pkb[f], ts);
+        lsum += ts;
+      }
     }
   }
 
-  // ---- normalise and store this chunk's state
-  const bool empty = !(l_tot > 0.f);
-  const float inv = empty ? 0.f : 1.f / l_tot;
-  const int slot = a.tab.slot[c];
-  float* Ob;
-  float* Lb;
-  if (slot < 0) {
-    const int r = -slot - 1;
-    Ob = a.O_part + (((int64_t)r * a.B + b) * a.H + h) * (int64_t)a.M * D;
-    Lb = a.L_part + (((int64_t)r * a.B + b) * a.H + h) * (int64_t)a.M;
-  } else {
-    Ob = a.ws_O + (((int64_t)slot * a.B + b) * a.H + h) * (int64_t)a.M * D;
-    Lb = a.ws_L + (((int64_t)slot * a.B + b) * a.H + h) * (int64_t)a.M;
-  }
-  const int m = 32 * wave + l32;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4_t v = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv};
-      *reinterpret_cast<f32x4_t*>(Ob + (int64_t)m * D + 32 * db + 8 * q + 4 * hh) = v;
-    }
-  if (hh == 0) Lb[m] = empty ? kNegInf : (m_run * a.scale + __logf(l_tot));
+  finish_chunk<D, NW, G>(smem, a, grp, wave, lane, o, m_run, lsum, b, h, c);
 }
 
 bool encode_mfma_supported(int M, int D) {
@@ -461,7 +798,21 @@ static hipError_t launch_d64(const EncodeArgs& a, hipStream_t s, bool pipe) {
   return pipe ? launch_mfma_t<64, NW, S, G, 1, RS>(a, s) : launch_mfma_t<64, NW, S, G, 0>(a, s);
 }
 
+// The two-tile pipelined encoder serves bf16 inputs without a padding mask at
+// head dim 64 and 128 latent rows (two 4-wave groups, four-stage rings);
+// FLARE_ENCODE_ILV=0 selects encode_mfma_kernel instead (for comparison).
+bool encode_ilv_selected(const EncodeArgs& a) {
+  const char* e = getenv("FLARE_ENCODE_ILV");
+  if (e && atoi(e) == 0) return false;
+  return a.D == 64 && a.M == 128 && a.mask_words == nullptr;
+}
+
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
+  if (encode_ilv_selected(a)) {
+    const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
+    hipLaunchKernelGGL((encode_ilv_kernel<64, 4, 4, 2>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.D == 64) {
     const bool s3 = encode_mfma_stages(a.M, a.D) == 3;
     const bool pipe = getenv("FLARE_ENCODE_PIPE") != nullptr;
