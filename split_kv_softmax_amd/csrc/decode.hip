@@ -141,6 +141,19 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     if (j < nb) issue(j, j);
 
   const int swx = row_swz(D, l32);
+  // Row sums on a 16x16x32 product: fed the weight operand of the 32x32x16
+  // product as its B, lane l contributes token l%32, latents 8*(l/32)+0..7 of
+  // the k-step as column l%16, contraction block l/16.  Selector rows 0 and 8
+  // pick blocks 0 and 2 (tokens 0..15), rows 4 and 12 blocks 1 and 3 (tokens
+  // 16..31), so register 0 of lane l (result row 4*(l/16), column l%16) sums
+  // token l%32 in both lane halves.
+  bf16x8_t sel;
+  {
+    const int si = lane & 15, kb = lane >> 4;
+    const bool on = ((si == 0 || si == 8) && (kb & 1) == 0) || ((si == 4 || si == 12) && (kb & 1) == 1);
+    const uint32_t w = on ? 0x3f803f80u : 0u;
+    sel = __builtin_bit_cast(bf16x8_t, u32x4_t{w, w, w, w});
+  }
   // S blocks per trip, so that each block's ring stage is a compile-time constant
   for (int j0 = 0; j0 < nb; j0 += S)
 #pragma unroll
@@ -159,64 +172,92 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       xop[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xs + (((2 * ks + hh) ^ swx) * 16)));
-    f32x16_t t[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      t[mb] = f32x16_t{};
+    // Weights against a zero reference, streamed over the latent blocks: the
+    // scores of block mb, their weights exp2(s log2(e) T), the row sums and the
+    // value products that use them, so the products of one block overlap the
+    // exponentials of the next.  A token whose row sum leaves [2^-64, 2^64]
+    // (overflow, underflow, NaN) sends the wave through the exact form below,
+    // which subtracts the token's maximum first.  Either way the weights are
+    // the same softmax up to the bf16 rounding of p.
+    auto scores_of = [&](int mb) -> f32x16_t {
+      f32x16_t t = f32x16_t{};
       const uint16_t* krow = &Kl[(32 * mb + swap23(l32)) * KLD + 8 * hh];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 16 * ks)),
-                             xop[ks], t[mb]);
-    }
-    // the token's maximum over its M scores: independent chains of 3-input maxima
-    float mc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float x = fmax3(t[mb][0], t[mb][1], t[mb][2]);
-#pragma unroll
-      for (int r = 3; r < 15; r += 2) x = fmax3(x, t[mb][r], t[mb][r + 1]);
-      mc[mb] = fmax2(x, t[mb][15]);
-    }
-    float mx = mc[0];
-#pragma unroll
-    for (int mb = 1; mb < MB; ++mb) mx = fmax2(mx, mc[mb]);
-    mx = fmax2(mx, __shfl_xor(mx, 32, 64));
-    const float nmc = -mx * c2;
-    // weights rounded to bf16 for the value product
-    bf16x8_t pk[MS];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+        t = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 16 * ks)), xop[ks],
+                         t);
+      return t;
+    };
+    auto weigh = [&](const f32x16_t& t, float nm, bf16x8_t* pk2) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         float p[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) p[jj] = fast_exp2(__builtin_fmaf(t[mb][8 * g + jj], c2, nmc));
+        for (int jj = 0; jj < 8; ++jj) p[jj] = fast_exp2(__builtin_fmaf(t[8 * g + jj], c2, nm));
         const u32x4_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                            pack_bf16x2(p[6], p[7])};
-        pk[2 * mb + g] = __builtin_bit_cast(bf16x8_t, w);
+        pk2[g] = __builtin_bit_cast(bf16x8_t, w);
       }
-    // the token's sum of the same rounded weights on the matrix cores: ones x P
-    // leaves it in every register of both lane halves
-    f32x16_t lacc = f32x16_t{};
-    {
+    };
+    f32x16_t y[DB];
+    f32x4_t ls4;
+    auto accumulate = [&](int ks, const bf16x8_t& pk) {
+      ls4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk, ls4, 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        // Z^T rows permuted so that register group g of lane half hh holds the 8
+        // consecutive head dims 32*db + 16*g + 8*hh .. +7
+        const uint16_t* zrow = &Zt[(32 * db + swap23(l32)) * ZLD + 8 * hh];
+        y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)), pk,
+                             y[db]);
+      }
+    };
+    auto clear = [&]() {
+      ls4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) y[db] = f32x16_t{};
+    };
+    clear();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      bf16x8_t pk2[2];
+      weigh(scores_of(mb), 0.f, pk2);
+      accumulate(2 * mb, pk2[0]);
+      accumulate(2 * mb + 1, pk2[1]);
+    }
+    float lsum = ls4[0];
+    if (__ballot(!(lsum >= 0x1p-64f && lsum <= 0x1p64f))) {
+      // exact form: the token's maximum over its M scores first.  Its row sums
+      // come from ones x P on the 32x32x16 product, which only adds a token's
+      // own weights (the selector form multiplies the neighbouring token's
+      // weights by 0, and 0 x NaN from a padded row would leak across).
+      f32x16_t t[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) t[mb] = scores_of(mb);
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmax2(mx, t[mb][r]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmax2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float nmc = -mx * c2;
+      clear();
+      f32x16_t lacc = f32x16_t{};
       const bf16x8_t ones =
           __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
-      for (int ks = 0; ks < MS; ++ks) lacc = mfma32x32x16(ones, pk[ks], lacc);
-    }
-    const float lsum = lacc[0];
-    f32x16_t y[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      y[db] = f32x16_t{};
-      // Z^T rows permuted so that register group g of lane half hh holds the 8
-      // consecutive head dims 32*db + 16*g + 8*hh .. +7
-      const uint16_t* zrow = &Zt[(32 * db + swap23(l32)) * ZLD + 8 * hh];
-#pragma unroll
-      for (int ks = 0; ks < MS; ++ks)
-        y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)),
-                             pk[ks], y[db]);
+      for (int mb = 0; mb < MB; ++mb) {
+        bf16x8_t pk2[2];
+        weigh(t[mb], nmc, pk2);
+        accumulate(2 * mb, pk2[0]);
+        accumulate(2 * mb + 1, pk2[1]);
+        lacc = mfma32x32x16(ones, pk2[0], lacc);
+        lacc = mfma32x32x16(ones, pk2[1], lacc);
+      }
+      lsum = lacc[0];
     }
     // Y block out through its own (consumed) ring stage: each lane writes its
     // token's head dims as 16-byte pieces, then whole rows leave with 16-byte

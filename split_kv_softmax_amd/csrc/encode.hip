@@ -622,7 +622,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   // accepted weight is at most 2^12.
   float m_run = kNegInf;     // reference maximum of row l32 (raw dot products)
   float nmc = __builtin_huge_valf();   // -m_run s log2(e); +inf while m_run = -inf (forces a rebase)
-  auto weights = [&](const f32x16_t* sc, bf16x8_t* pk, float nm) -> float {
+  auto weights = [&](const f32x16_t* sc, bf16x8_t* pk, float nm, bool own_rows_only = false) -> float {
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
@@ -634,6 +634,17 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
                            pack_bf16x2(p[6], p[7])};
         pk[2 * b2 + g] = __builtin_bit_cast(bf16x8_t, w);
       }
+    if (own_rows_only) {
+      // ones x P^T on the 32x32x16 product adds only the row's own weights
+      // (the selector form multiplies the neighbouring row's weights by 0,
+      // and 0 x NaN would leak across rows)
+      const bf16x8_t ones =
+          __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+      f32x16_t la = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) la = mfma32x32x16(ones, pk[ks], la);
+      return la[0];
+    }
     f32x4_t ts = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
     for (int ks = 1; ks < 4; ++ks) ts = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk[ks], ts, 0, 0, 0);
@@ -643,7 +654,8 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   // Rare path: rows whose tile sum failed the check move their reference to
   // the tile's maximum (the online-softmax rescale of the value accumulators
   // and the row sum by exp2(s log2(e) (m_old - m_new)), 0 from an empty
-  // state), then the tile's weights and sums are recomputed.
+  // state), then the tile's weights and sums are recomputed, the sums with
+  // each row's own weights only.
   auto rebase = [&](const f32x16_t* sc, bf16x8_t* pk, float& ts) {
     float mc[4];
 #pragma unroll
@@ -668,7 +680,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
     for (int i = 0; i < DB; ++i) o[i] *= alpha;
     m_run = m_new;
     nmc = m_run == kNegInf ? __builtin_huge_valf() : -m_run * c2;
-    ts = weights(sc, pk, m_run == kNegInf ? 0.f : nmc);
+    ts = weights(sc, pk, m_run == kNegInf ? 0.f : nmc, true);
   };
   auto softmax_tile = [&](const f32x16_t* sc, bf16x8_t* pk) {
     float ts = weights(sc, pk, nmc);
