@@ -7,12 +7,14 @@
 // and a state without a partner passes through; one merge takes
 // m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m), acc = acc1 e^(m1-m) + acc2 e^(m2-m).
 //
-// A thread owns one (row, 4 columns) and visits the leaves in order keeping
-// one partial state per tree level (a binary counter): after leaf i the
-// levels whose bit is set in i are merged into it.  Because i is the same for
-// every thread the branches are uniform and the level slots stay in
-// registers.  Leftover levels are merged from the lowest upwards, which is
-// exactly the round schedule above with its pass-through survivors.
+// A thread owns one (row, 4 columns).  Up to 16 states it loads them all at
+// once and runs the rounds of the 16-leaf tree on them (absent leaves empty).
+// Beyond that it visits the leaves in order keeping one partial state per tree
+// level (a binary counter): after leaf i the levels whose bit is set in i are
+// merged into it.  Because i is the same for every thread the branches are
+// uniform and the level slots stay in registers.  Leftover levels are merged
+// from the lowest upwards, which is exactly the round schedule above with its
+// pass-through survivors.
 #include <algorithm>
 
 #include "common.h"
@@ -54,52 +56,82 @@ __global__ __launch_bounds__(256) void fold_kernel(const FoldArgs a) {
     const int64_t row = e / D4;
     const int64_t off = 4 * e;                          // = row * D + 4 * piece
     const int s0 = a.tab.in_begin[g], s1 = a.tab.in_begin[g + 1];
-    const int n = s1 - s0;
+    const int n = s1 - s0;     // >= 0; a group without states writes the empty state
 
-    St lv[kLevels];
-    for (int i0 = 0; i0 < n; i0 += kBatch) {
+    St cur{kNegInf, 0.f, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    if (n == 0) {
+      // no states: the empty state
+    } else if (n <= kBatch) {
+      // Up to 16 states: every load issued at once (indices past the group
+      // re-read its last state), absent leaves replaced by empty states, and
+      // the four rounds of the 16-leaf tree.  Merging a state with an empty
+      // one returns it bit for bit (factor exp(0) = 1 on its side, exactly 0
+      // on the empty side), so this is the tree with pass-through survivors.
+      St t[kBatch];
       float Lb[kBatch];
       f32x4_t Ob[kBatch];
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
-        const int64_t s = s0 + i0 + k;
-        const bool ok = i0 + k < n;
-        Lb[k] = ok ? a.in_L[s * a.rows + row] : kNegInf;
-        Ob[k] = ok ? *reinterpret_cast<const f32x4_t*>(a.in_O + s * sstride + off) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int64_t s = s0 + (k < n ? k : n - 1);
+        Lb[k] = a.in_L[s * a.rows + row];
+        Ob[k] = *reinterpret_cast<const f32x4_t*>(a.in_O + s * sstride + off);
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
-        const int i = i0 + k;
-        if (i < n) {
-          St leaf;
-          leaf.m = Lb[k];
-          leaf.l = (leaf.m == kNegInf) ? 0.f : 1.f;
-          leaf.acc = (leaf.m == kNegInf) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Ob[k];
-          // carry: merge the completed left subtrees of equal size into the
-          // new leaf; the first level whose bit is clear in i takes the result
-          bool carry = true;
+        const bool leaf = k < n && Lb[k] != kNegInf;
+        t[k].m = leaf ? Lb[k] : kNegInf;
+        t[k].l = leaf ? 1.f : 0.f;
+        t[k].acc = leaf ? Ob[k] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-          for (int lvl = 0; lvl < kLevels; ++lvl) {
-            if (carry) {
-              if ((i >> lvl) & 1) {
-                leaf = merge_st(lv[lvl], leaf);
-              } else {
-                lv[lvl] = leaf;
-                carry = false;
+      for (int w2 = 1; w2 < kBatch; w2 *= 2)
+#pragma unroll
+        for (int i = 0; i < kBatch; i += 2 * w2) t[i] = merge_st(t[i], t[i + w2]);
+      cur = t[0];
+    } else {
+      St lv[kLevels];
+      for (int i0 = 0; i0 < n; i0 += kBatch) {
+        float Lb[kBatch];
+        f32x4_t Ob[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int64_t s = s0 + (i0 + k < n ? i0 + k : n - 1);
+          Lb[k] = a.in_L[s * a.rows + row];
+          Ob[k] = *reinterpret_cast<const f32x4_t*>(a.in_O + s * sstride + off);
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int i = i0 + k;
+          if (i < n) {
+            St leaf;
+            leaf.m = Lb[k];
+            leaf.l = (leaf.m == kNegInf) ? 0.f : 1.f;
+            leaf.acc = (leaf.m == kNegInf) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Ob[k];
+            // carry: merge the completed left subtrees of equal size into the
+            // new leaf; the first level whose bit is clear in i takes the result
+            bool carry = true;
+#pragma unroll
+            for (int lvl = 0; lvl < kLevels; ++lvl) {
+              if (carry) {
+                if ((i >> lvl) & 1) {
+                  leaf = merge_st(lv[lvl], leaf);
+                } else {
+                  lv[lvl] = leaf;
+                  carry = false;
+                }
               }
             }
           }
         }
       }
-    }
-    // collect the levels still occupied (bits of n), lowest first
-    St cur{kNegInf, 0.f, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    bool have = false;
+      // collect the levels still occupied (bits of n), lowest first
+      bool have = false;
 #pragma unroll
-    for (int lvl = 0; lvl < kLevels; ++lvl) {
-      if ((n >> lvl) & 1) {
-        cur = have ? merge_st(lv[lvl], cur) : lv[lvl];
-        have = true;
+      for (int lvl = 0; lvl < kLevels; ++lvl) {
+        if ((n >> lvl) & 1) {
+          cur = have ? merge_st(lv[lvl], cur) : lv[lvl];
+          have = true;
+        }
       }
     }
     const int oi = a.tab.out_index[g];
