@@ -30,7 +30,7 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
-COUNTERS = os.path.join(HERE, "profiles", "encode_mfma_flarepp_N262144_hbm_counters.md")
+COUNTERS = os.path.join(HERE, "profiles", "encode_flarepp_N262144_hbm_counters.md")
 ENCODER_SOURCES = [os.path.join(HERE, "split_kv_softmax_amd", "csrc", f)
                    for f in ("encode.hip", "common.h", "kernels.h")]
 
@@ -272,7 +272,7 @@ def roofline_of(w: W.Workload, x, step, ph):
                                                 "fused query gradient, reduce); both encoder backwards averaged")
     if w.kind == "flarepp":
         ms = 0.5 * (ph["encode1"] + ph["encode2"])
-        return ms, 2 * rows * row, "encode_mfma_kernel (flare_encode, one launch; both encoders averaged)"
+        return ms, 2 * rows * row, "encode_ilv_kernel (flare_encode, one launch; both encoders averaged)"
     if w.kind == "flare":
         if ph["decode"] > ph["encode"]:
             return ph["decode"], 2 * rows * row, "decode_mfma_kernel (flare_decode, one launch)"
