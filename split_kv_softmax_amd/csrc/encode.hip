@@ -882,24 +882,39 @@ __global__ __launch_bounds__(256) void mask_words_kernel(const uint8_t* __restri
 
 // One workgroup: valid-token count of every (batch, chunk) pair from the mask
 // words, rank by counting (heavier first, ties by index), then the order table.
+// The counts are spread over all threads: consecutive threads take
+// consecutive words of one pair (coalesced loads, LDS atomics), so no thread
+// walks a whole chunk.
 __global__ __launch_bounds__(1024) void heavy_first_kernel(const uint64_t* __restrict__ words, int64_t stride,
                                                            const ChunkTable tab, int B, int H,
                                                            int32_t* __restrict__ order) {
   __shared__ int key[kMaxOrderItems];
+  __shared__ int maxw_s;
   const int nch = tab.nchunks, n = B * nch;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+  if (threadIdx.x == 0) {
+    int mw = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int lo = tab.bnd[c], hi = tab.bnd[c + 1];
+      if (hi > lo) mw = max(mw, ((hi - 1) >> 6) - (lo >> 6) + 1);
+    }
+    maxw_s = mw;
+  }
+  for (int i = threadIdx.x; i < n; i += blockDim.x) key[i] = 0;
+  __syncthreads();
+  const int W = maxw_s;
+  const int64_t total = (int64_t)n * W;
+  for (int64_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const int i = (int)(idx / W), kk = (int)(idx % W);
     const int b = i / nch, c = i % nch;
     const int lo = tab.bnd[c], hi = tab.bnd[c + 1];
-    const uint64_t* w = words + (int64_t)b * stride;
-    int cnt = 0;
-    for (int k = lo >> 6; k <= (hi - 1) >> 6 && lo < hi; ++k) {
-      uint64_t x = w[k];
-      const int a0 = lo - 64 * k, a1 = hi - 64 * k;   // keep bits [a0, a1) of this word
-      if (a0 > 0) x &= ~0ull << a0;
-      if (a1 < 64) x &= (1ull << a1) - 1ull;
-      cnt += __popcll(x);
-    }
-    key[i] = cnt;
+    const int k = (lo >> 6) + kk;
+    if (lo >= hi || k > ((hi - 1) >> 6)) continue;
+    uint64_t x = words[(int64_t)b * stride + k];
+    const int a0 = lo - 64 * k, a1 = hi - 64 * k;   // keep bits [a0, a1) of this word
+    if (a0 > 0) x &= ~0ull << a0;
+    if (a1 < 64) x &= (1ull << a1) - 1ull;
+    const int cnt = __popcll(x);
+    if (cnt) atomicAdd(&key[i], cnt);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
