@@ -90,6 +90,46 @@ def test_bf16_encoder_split_partitions():
     _check_encode(w, x)
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_bf16_encoder_partitions_shorter_than_a_tile_per_group(masked):
+    """Partitions of 1, 63, 64, 65, 127, 128, 129 and 0 tokens: fewer 64-token
+    tiles than the encoder's token groups, partial last tiles, an empty one."""
+    offs = [0, 1, 64, 128, 193, 320, 448, 577, 577, 800]
+    w, x = _enc_case(128, 64, N=offs[-1], R=len(offs) - 1, masked=masked)
+    w = w.with_(offsets=offs)
+    if masked:
+        x["mask"][:, 1:64] = 1          # keep the 63-token partition fully valid
+    _check_encode(w, x)
+
+
+def test_nan_query_row_stays_in_its_row():
+    """A NaN in one latent query row makes only that row NaN (the oracle says so);
+    rows whose weights share a matrix-core product with it stay exact."""
+    for M, masked in ((128, False), (128, True), (64, False)):
+        w, x = _enc_case(M, 64, N=1300, R=3, masked=masked)
+        x["Q"][:, 5] = float("nan")
+        _check_encode(w, x)             # NaN reference entries are skipped, every other one compared
+        O_part, _ = fl.encode(x["Q"], x["K"], x["V"], w.offsets, x.get("mask"), w.scale)
+        torch.cuda.synchronize()
+        o = O_part.cpu()
+        assert not torch.isnan(o[:, :, :, 21]).any() and not torch.isnan(o[:, :, :, 37]).any()
+
+
+def test_decode_nan_token_stays_in_its_row():
+    """An unmasked token row holding NaN gives NaN only in its own output row."""
+    B, H, N, M, D = 1, 2, 300, 128, 64
+    Xq = W.normal((B, H, N, D), 612, W.T_K, 1.0, torch.bfloat16, DEV)
+    Xq[0, :, 40] = float("nan")
+    Kl = W.normal((H, M, D), 612, W.T_Q, 1.0, torch.bfloat16, DEV)
+    Z = W.normal((B, H, M, D), 612, W.T_V, 1.0, torch.float32, DEV)
+    Y = fl.decode(Xq, Kl, Z, 0.125)
+    torch.cuda.synchronize()
+    Yc = Y.float().cpu()
+    assert torch.isnan(Yc[0, :, 40]).all()
+    ref_y = ref.decode_ref(Xq, Kl, Z, 0.125)           # NaN in row 40 only
+    compare_bf16(Y, ref_y, "Y")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_single_query_split_kv(D):
     w, x = _enc_case(1, D, N=5000, R=7, B=2, H=3, q_per_batch=True)
