@@ -789,22 +789,10 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Only the shape whose key/value kernel cannot also hold the query-gradient
+// accumulators (bwd_kv_fuses_dq) runs this kernel.
 hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s) {
-  if (a.D == 64) {
-    switch (a.M) {
-      case 32: return launch_dq_t<64, 1, 3>(a, s);
-      case 64: return launch_dq_t<64, 2, 3>(a, s);
-      case 128: return launch_dq_t<64, 4, 3>(a, s);
-      case 256: return launch_dq_t<64, 8, 3>(a, s);
-    }
-  } else if (a.D == 128) {
-    switch (a.M) {
-      case 32: return launch_dq_t<128, 1, 3>(a, s);
-      case 64: return launch_dq_t<128, 2, 3>(a, s);
-      case 128: return launch_dq_t<128, 4, 3>(a, s);
-      case 256: return launch_dq_t<128, 8, 3>(a, s);
-    }
-  }
+  if (a.D == 128 && a.M == 256) return launch_dq_t<128, 8, 3>(a, s);
   return hipErrorInvalidValue;
 }
 
