@@ -99,7 +99,7 @@ bool heavy_first_enabled() { return env_int("FLARE_HEAVY_FIRST", 1) != 0; }
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 // Chunk length for a partition of n tokens.
-int chunk_len_for(EncKind kind, int B, int H, int R, int M, int D, int64_t max_part) {
+int chunk_len_for(EncKind kind, int B, int H, int R, int M, int D, int64_t max_part, bool masked) {
   if (max_part <= 0) return 1;
   switch (kind) {
     case EncKind::Mfma: {
@@ -107,7 +107,7 @@ int chunk_len_for(EncKind kind, int B, int H, int R, int M, int D, int64_t max_p
       // 256 CUs, but long enough chunks that the partial states stay a few
       // percent of the K/V bytes (state bytes / K,V bytes = 2M / chunk_len).
       const int64_t base = (int64_t)B * H * R;
-      const int64_t target = 256 * (int64_t)encode_mfma_per_cu(M, D);
+      const int64_t target = 256 * (int64_t)encode_mfma_per_cu(M, D, masked);
       int split = env_int("FLARE_ENCODE_SPLIT", 0);
       if (split <= 0) split = (int)std::max<int64_t>(1, (target + base - 1) / base);
       int len = round_up((int)((max_part + split - 1) / split), 64);
@@ -129,7 +129,7 @@ EncodePlan plan_encode(flare_dtype dt, int B, int H, int N, int M, int D, int R,
   p.kind = encode_kind(dt, M, D);
   int64_t max_part = 0;
   for (int r = 0; r < R; ++r) max_part = std::max<int64_t>(max_part, off[r + 1] - off[r]);
-  const int len = chunk_len_for(p.kind, B, H, R, M, D, max_part);
+  const int len = chunk_len_for(p.kind, B, H, R, M, D, max_part, masked);
   p.first_chunk.resize(R + 1);
   for (int r = 0; r < R; ++r) {
     p.first_chunk[r] = (int)p.chunks.size();

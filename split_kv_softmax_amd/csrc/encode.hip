@@ -448,9 +448,11 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
 // slots).  Rows past the chunk re-read row 0 of the tile (finite values whose
 // weights are exactly 0), so a partial tile only masks its scores.
 // ---------------------------------------------------------------------------
-template <int D, int NW, int S, int G>
+template <int D, int NW, int S, int G, int TILE>
 __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArgs a) {
-  constexpr int TILE = 64;
+  constexpr int NB = TILE / 32;            // 32-token blocks of the score product
+  constexpr int NK = TILE / 16;            // 16-token k-steps of the value product
+  static_assert(TILE == 32 || TILE == 64, "tile of 32 or 64 tokens");
   constexpr int ROWB = 2 * D;              // bytes per row
   constexpr int TB = TILE * ROWB;          // bytes of a K (or V) tile
   constexpr int RING = 2 * S * TB;         // S K slots, then S V slots
@@ -567,17 +569,17 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   // scores of the tile in K slot `slot`: register r of lane half hh in block b2
   // holds token 32*b2 + 16*(r/8) + 8*hh + r%8 of latent row l32
   auto scores = [&](int slot, f32x16_t* sc) {
-    u32x4_t kop[KS][2];
+    u32x4_t kop[KS][NB];
 #pragma unroll
     for (int k = 0; k < KS; ++k)
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) kop[k][b2] = *(lds_u32x4*)(uintptr_t)(kaddr[k] + slot * TB + 32 * b2 * ROWB);
-    sc[0] = f32x16_t{};
-    sc[1] = f32x16_t{};
+      for (int b2 = 0; b2 < NB; ++b2) kop[k][b2] = *(lds_u32x4*)(uintptr_t)(kaddr[k] + slot * TB + 32 * b2 * ROWB);
+#pragma unroll
+    for (int b2 = 0; b2 < NB; ++b2) sc[b2] = f32x16_t{};
 #pragma unroll
     for (int k = 0; k < KS; ++k)
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, kop[k][b2]), qop[k], sc[b2]);
+      for (int b2 = 0; b2 < NB; ++b2) sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, kop[k][b2]), qop[k], sc[b2]);
   };
   f32x16_t o[DB];
 #pragma unroll
@@ -585,9 +587,9 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   float lsum = 0.f;          // running row sum of the weights (row l32, both lane halves)
   // weighted values of the tile in V slot `slot` with weights pk
   auto values = [&](int slot, const bf16x8_t* pk) {
-    u32x2_t part[4][DB][2];
+    u32x2_t part[NK][DB][2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
               u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                            (lds_bf16x4*)(uintptr_t)(vaddr[db][q] + slot * TB + 16 * ks * ROWB)));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const u32x4_t av = {part[ks][db][0][0], part[ks][db][0][1], part[ks][db][1][0], part[ks][db][1][1]};
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   // past the group's end, whose slots hold stale or never-written rows)
   auto mask_tail = [&](f32x16_t* sc, int n) {
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
+    for (int b2 = 0; b2 < NB; ++b2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tk = 32 * b2 + 16 * (r >> 3) + 8 * hh + (r & 7);
@@ -624,7 +626,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   float nmc = __builtin_huge_valf();   // -m_run s log2(e); +inf while m_run = -inf (forces a rebase)
   auto weights = [&](const f32x16_t* sc, bf16x8_t* pk, float nm, bool own_rows_only = false) -> float {
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
+    for (int b2 = 0; b2 < NB; ++b2)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         float p[8];
@@ -642,12 +644,12 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
           __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
       f32x16_t la = f32x16_t{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) la = mfma32x32x16(ones, pk[ks], la);
+      for (int ks = 0; ks < NK; ++ks) la = mfma32x32x16(ones, pk[ks], la);
       return la[0];
     }
     f32x4_t ts = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk[0], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-    for (int ks = 1; ks < 4; ++ks) ts = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk[ks], ts, 0, 0, 0);
+    for (int ks = 1; ks < NK; ++ks) ts = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk[ks], ts, 0, 0, 0);
     return ts[0];
   };
   constexpr float kSumMax = 4096.f;
@@ -657,9 +659,9 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   // state), then the tile's weights and sums are recomputed, the sums with
   // each row's own weights only.
   auto rebase = [&](const f32x16_t* sc, bf16x8_t* pk, float& ts) {
-    float mc[4];
+    float mc[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 2 * NB; ++k) {
       const f32x16_t& v = sc[k >> 1];
       const int r0 = 8 * (k & 1);
       float x = fmax3(v[r0], v[r0 + 1], v[r0 + 2]);
@@ -710,8 +712,8 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   // scores and weights of tile t live in buffer t % 2: round u reads the
   // weights of tile u and the scores of tile u+1 and writes the weights of
   // tile u+1 and the scores of tile u+2
-  f32x16_t scb[2][2];
-  bf16x8_t pkb[2][4];
+  f32x16_t scb[2][NB];
+  bf16x8_t pkb[2][NK];
   {
     scores(0, scb[0]);
     scores(1, scb[1]);
@@ -746,10 +748,10 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
         // order: all operand reads (V, then K), a few exponentials while they
         // arrive, then each product with exponentials and conversions between
         // (vector groups take vector and transcendental instructions)
-        __builtin_amdgcn_sched_group_barrier(0x100, 8 * DB + 2 * KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NK * DB + NB * KS, 0);
         __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
 #pragma unroll
-        for (int i = 0; i < 4 * DB + 2 * KS; ++i) {
+        for (int i = 0; i < NK * DB + NB * KS; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
         }
@@ -797,8 +799,9 @@ int encode_mfma_stages(int M, int D) {
   return (M >= 128) ? 4 : 3;
 }
 
-int encode_mfma_per_cu(int M, int D) {
+int encode_mfma_per_cu(int M, int D, bool masked) {
   // workgroups of the chosen variant that fit on one CU (LDS and registers)
+  if (encode_ilv_used(M, D, masked)) return 1;
   if (D == 64) return encode_mfma_groups(M, D) > 1 ? 1 : (encode_mfma_stages(M, D) == 3 ? 3 : 2);
   return M >= 128 ? 1 : 2;
 }
@@ -811,18 +814,25 @@ static hipError_t launch_d64(const EncodeArgs& a, hipStream_t s, bool pipe) {
 }
 
 // The two-tile pipelined encoder serves bf16 inputs without a padding mask at
-// head dim 64 and 128 latent rows (two 4-wave groups, four-stage rings);
-// FLARE_ENCODE_ILV=0 selects encode_mfma_kernel instead (for comparison).
-bool encode_ilv_selected(const EncodeArgs& a) {
+// head dim 64: 128 latent rows as two 4-wave groups with 64-token tiles, 64
+// rows as four 2-wave groups with 32-token tiles (8 waves and 128 KB of
+// four-stage rings either way, one workgroup per CU); FLARE_ENCODE_ILV=0
+// selects encode_mfma_kernel instead (for comparison).
+bool encode_ilv_used(int M, int D, bool masked) {
   const char* e = getenv("FLARE_ENCODE_ILV");
   if (e && atoi(e) == 0) return false;
-  return a.D == 64 && a.M == 128 && a.mask_words == nullptr;
+  return D == 64 && (M == 128 || M == 64) && !masked;
 }
+
+static bool encode_ilv_selected(const EncodeArgs& a) { return encode_ilv_used(a.M, a.D, a.mask_words != nullptr); }
 
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
   if (encode_ilv_selected(a)) {
     const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
-    hipLaunchKernelGGL((encode_ilv_kernel<64, 4, 4, 2>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    if (a.M == 128)
+      hipLaunchKernelGGL((encode_ilv_kernel<64, 4, 4, 2, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((encode_ilv_kernel<64, 2, 4, 4, 32>), dim3((unsigned)grid), dim3(512), 0, s, a);
     return hipGetLastError();
   }
   if (a.D == 64) {

@@ -121,7 +121,8 @@ struct DecBwdArgs {
 
 // Encoder kernels. Return hipSuccess or the launch error.
 bool encode_mfma_supported(int M, int D);
-int encode_mfma_per_cu(int M, int D);   // resident workgroups per CU of the chosen variant
+int encode_mfma_per_cu(int M, int D, bool masked);   // resident workgroups per CU of the chosen variant
+bool encode_ilv_used(int M, int D, bool masked);     // the pipelined encoder serves this shape
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s);
 bool encode_q1_supported(int M, int D);
 hipError_t launch_encode_q1(const EncodeArgs& a, hipStream_t s);
