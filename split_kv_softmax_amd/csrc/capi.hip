@@ -117,8 +117,15 @@ int chunk_len_for(EncKind kind, int B, int H, int R, int M, int D, int64_t max_p
     }
     case EncKind::Q1:
       return 4096;
-    default:
-      return 2048;
+    default: {
+      // The vector kernel walks a chunk's 64-token tiles one after another
+      // (latency-bound), so aim for about 2048 workgroups (one per chunk and
+      // group of four latent rows), with chunks of at least 128 tokens.
+      const int64_t base = (int64_t)B * H * R * ((M + 3) / 4);
+      const int64_t split = std::max<int64_t>(1, (2048 + base - 1) / base);
+      const int len = round_up((int)((max_part + split - 1) / split), 64);
+      return std::max(len, 128);
+    }
   }
 }
 
