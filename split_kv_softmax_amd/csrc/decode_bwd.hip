@@ -337,42 +337,70 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
     }
     // scores and dA; register r of block mb holds latent 32*mb + 16*(r/8) + 8*hh + r%8
     f32x16_t t[MB], da[MB];
+    auto scores = [&]() {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        t[mb] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Kl + 32 * mb * ROWB + koff[ks])), xop[ks], t[mb]);
+      }
+    };
+    scores();
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      t[mb] = f32x16_t{};
       da[mb] = f32x16_t{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Kl + 32 * mb * ROWB + koff[ks])), xop[ks], t[mb]);
+      for (int ks = 0; ks < KS; ++ks)
         da[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Zr + 32 * mb * ROWB + koff[ks])), gop[ks], da[mb]);
-      }
     }
-    float mx = t[0][0];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmax2(mx, t[mb][r]);
-    mx = fmax2(mx, __shfl_xor(mx, 32, 64));
-    const float nmc = -mx * c2;
+    // Unnormalised weights p = exp2(s log2(e) (T - ref)) against a zero
+    // reference, and their sum l; a token whose sum leaves [2^-64, 2^64]
+    // (overflow, underflow, NaN) sends the wave through the exact form with
+    // ref = the token's maximum.  The sum adds the token's own fp32 weights
+    // (lane-local), so sum_m A = 1 holds to rounding.
+    float ref2 = 0.f;   // the reference in log2 units
     float lsum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        t[mb][r] = fast_exp2(__builtin_fmaf(t[mb][r], c2, nmc));
+        t[mb][r] = fast_exp2(t[mb][r] * c2);
         lsum += t[mb][r];
       }
     lsum += __shfl_xor(lsum, 32, 64);
+    if (__ballot(!(lsum >= 0x1p-64f && lsum <= 0x1p64f))) {
+      // (a compiler barrier: the latent rows are read again here rather than
+      // kept in registers from the first products)
+      asm volatile("" ::: "memory");
+      scores();
+      float mx = t[0][0];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmax2(mx, t[mb][r]);
+      mx = fmax2(mx, __shfl_xor(mx, 32, 64));
+      ref2 = mx * c2;
+      lsum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          t[mb][r] = fast_exp2(__builtin_fmaf(t[mb][r], c2, -ref2));
+          lsum += t[mb][r];
+        }
+      lsum += __shfl_xor(lsum, 32, 64);
+    }
+    // A = p / l; delta = sum_m A dA; dT = A (dA - delta) = (p (dA - delta)) / l, the
+    // 1/l joining the scale s of dXq below
     const float inv = 1.f / lsum;
     float delta = 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        t[mb][r] *= inv;                                  // A
-        delta = __builtin_fmaf(t[mb][r], da[mb][r], delta);
-      }
+      for (int r = 0; r < 16; ++r) delta = __builtin_fmaf(t[mb][r], da[mb][r], delta);
     delta += __shfl_xor(delta, 32, 64);
+    delta *= inv;
     bf16x8_t dtk[MS];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -404,6 +432,7 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
       }
     }
     const bool keep = inb && (!mw || ((mw[n0 >> 6] >> ((n0 & 63) + l32)) & 1ull));
+    const float sl = a.scale * inv;   // s / l
     // stage dXq rows (register group g of lane half hh: dims 32*db + 16*g + 8*hh ..) in the consumed Xq slot
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -412,7 +441,7 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
         u32x4_t w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t v = pack_bf16x2(a.scale * acc[db][8 * g + 2 * e], a.scale * acc[db][8 * g + 2 * e + 1]);
+          const uint32_t v = pack_bf16x2(sl * acc[db][8 * g + 2 * e], sl * acc[db][8 * g + 2 * e + 1]);
           w[e] = keep ? v : 0u;
         }
         const int pc = (4 * db + 2 * g + hh) ^ swx;
@@ -429,7 +458,7 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
       __builtin_amdgcn_raw_buffer_store_b128(v, yr, r * ROWB + ((pc ^ tok_swz(D, r)) * 16), 0, kCachePolicyNT);
     }
     // per-token statistics; lanes of the upper half and rows past the run fall outside the range
-    const float lse2 = keep ? (mx * c2 + __log2f(lsum)) : __builtin_huge_valf();
+    const float lse2 = keep ? (ref2 + __log2f(lsum)) : __builtin_huge_valf();
     const float dl = keep ? delta : 0.f;
     const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(lseg + n0, 0, valid_rows * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(delg + n0, 0, valid_rows * 4, 0x00020000);
