@@ -1,6 +1,7 @@
 """Throughput of the split-KV / FLARE softmax hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cpu-seconds S]
+                    [--backward] [--fused] [--graph]
 
 A step is one pass of the whole path over one batch of synthetic input that
 already sits in HBM.  For the default workload (FLARE++, B=1, H=16, N=262144,
@@ -78,10 +79,34 @@ def _collect(step):
     step.pending = []
 
 
-class FlareppStep:
-    """The FLARE++ forward chain with preallocated outputs."""
+class Step:
+    """A step as named phases run back to back; with timed_phases an event is
+    recorded before the first phase and after each one."""
 
-    def __init__(self, w: W.Workload, x):
+    def _phases(self, phases):
+        self.phases = phases
+        self.names = [n for n, _ in phases]
+        self.phase_ms = [0.0] * len(phases)   # per-phase milliseconds, summed over collected steps
+        self.count = 0
+        self.pending = []
+
+    def __call__(self, timed_phases: bool):
+        if timed_phases:
+            _new_events(self)
+            self.ev[0].record()
+        for i, (_, fn) in enumerate(self.phases):
+            fn()
+            if timed_phases:
+                self.ev[i + 1].record()
+
+    collect = _collect
+
+
+class FlareppStep(Step):
+    """The FLARE++ forward chain with preallocated outputs; fused: each encoder
+    and its merge as one call (flare_encode_merge)."""
+
+    def __init__(self, w: W.Workload, x, fused=False):
         self.w, self.x = w, x
         B, H, N, M, D, R = w.B, w.H, w.N, w.M, w.D, w.R
         dev = x["K"].device
@@ -96,75 +121,27 @@ class FlareppStep:
         self.Z = torch.empty((B, H, M, D), **f32)
         self.L = torch.empty((B, H, M), **f32)
         self.Y = torch.empty_like(x["K"])
-        self.names = ["encode1", "merge1", "encode2", "merge2", "decode"]
-        self.ev = [_ev() for _ in range(6)]
-        self.phase_ms = [0.0] * 5       # per-phase milliseconds, summed over collected steps
-        self.count = 0
-        self.pending = []
-
-    def __call__(self, timed_phases: bool):
-        if timed_phases:
-            _new_events(self)
-        x, w, ev = self.x, self.w, self.ev
-        if timed_phases:
-            ev[0].record()
-        fl.encode(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.O1, self.L1)
-        if timed_phases:
-            ev[1].record()
-        fl.lse_merge(self.O1, self.L1, Z=self.QX, L=self.QXL, Z_bf16=self.QXb)
-        if timed_phases:
-            ev[2].record()
-        fl.encode(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, self.O2, self.L2)
-        if timed_phases:
-            ev[3].record()
-        fl.lse_merge(self.O2, self.L2, Z=self.Z, L=self.L)
-        if timed_phases:
-            ev[4].record()
-        fl.decode(x["K"], self.QXb, self.Z, w.scale, None, self.Y)
-        if timed_phases:
-            ev[5].record()
-
-    collect = _collect
+        dec = ("decode", lambda: fl.decode(x["K"], self.QXb, self.Z, w.scale, None, self.Y))
+        if fused:
+            self._phases([
+                ("encode_merge1", lambda: fl.encode_merge(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, True,
+                                                          self.O1, self.L1, self.QX, self.QXL, self.QXb)),
+                ("encode_merge2", lambda: fl.encode_merge(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, False,
+                                                          self.O2, self.L2, self.Z, self.L)),
+                dec])
+        else:
+            self._phases([
+                ("encode1", lambda: fl.encode(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.O1, self.L1)),
+                ("merge1", lambda: fl.lse_merge(self.O1, self.L1, Z=self.QX, L=self.QXL, Z_bf16=self.QXb)),
+                ("encode2", lambda: fl.encode(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, self.O2, self.L2)),
+                ("merge2", lambda: fl.lse_merge(self.O2, self.L2, Z=self.Z, L=self.L)),
+                dec])
 
 
-class FlareStep:
-    """FLARE block: encode -> merge -> decode of every token (K as token queries, Q as latent keys)."""
-
-    def __init__(self, w: W.Workload, x):
-        self.w, self.x = w, x
-        B, H, N, M, D, R = w.B, w.H, w.N, w.M, w.D, w.R
-        f32 = dict(dtype=torch.float32, device=x["K"].device)
-        self.O = torch.empty((R, B, H, M, D), **f32)
-        self.Lp = torch.empty((R, B, H, M), **f32)
-        self.Z = torch.empty((B, H, M, D), **f32)
-        self.L = torch.empty((B, H, M), **f32)
-        self.Y = torch.empty_like(x["K"])
-        self.names = ["encode", "merge", "decode"]
-        self.ev = [_ev() for _ in range(len(self.names) + 1)]
-        self.phase_ms = [0.0] * len(self.names)
-        self.count = 0
-        self.pending = []
-
-    def __call__(self, timed_phases: bool):
-        if timed_phases:
-            _new_events(self)
-        x, w, ev = self.x, self.w, self.ev
-        rec = (lambda i: ev[i].record()) if timed_phases else (lambda i: None)
-        rec(0)
-        fl.encode(x["Q"], x["K"], x["V"], w.offsets, None, w.scale, self.O, self.Lp)
-        rec(1)
-        fl.lse_merge(self.O, self.Lp, Z=self.Z, L=self.L)
-        rec(2)
-        fl.decode(x["K"], x["Q"], self.Z, w.scale, None, self.Y)
-        rec(3)
-
-    collect = FlareppStep.collect
-
-
-class EncodeMergeStep:
+class EncodeMergeStep(Step):
     """Encoder over every partition, then the tree merge (single-query split-KV, small encoder)."""
 
-    def __init__(self, w: W.Workload, x):
+    def __init__(self, w: W.Workload, x, fused=False, extra=()):
         self.w, self.x = w, x
         B, H, N, M, D, R = w.B, w.H, w.N, w.M, w.D, w.R
         f32 = dict(dtype=torch.float32, device=x["K"].device)
@@ -172,47 +149,38 @@ class EncodeMergeStep:
         self.Lp = torch.empty((R, B, H, M), **f32)
         self.Z = torch.empty((B, H, M, D), **f32)
         self.L = torch.empty((B, H, M), **f32)
-        self.names = ["encode", "merge"]
-        self.ev = [_ev() for _ in range(len(self.names) + 1)]
-        self.phase_ms = [0.0] * len(self.names)
-        self.count = 0
-        self.pending = []
+        mask = x.get("mask")
+        if fused:
+            phases = [("encode_merge", lambda: fl.encode_merge(x["Q"], x["K"], x["V"], w.offsets, mask, w.scale,
+                                                               False, self.O, self.Lp, self.Z, self.L))]
+        else:
+            phases = [("encode", lambda: fl.encode(x["Q"], x["K"], x["V"], w.offsets, mask, w.scale, self.O,
+                                                   self.Lp)),
+                      ("merge", lambda: fl.lse_merge(self.O, self.Lp, Z=self.Z, L=self.L))]
+        self._phases(phases + list(extra))
 
-    def __call__(self, timed_phases: bool):
-        if timed_phases:
-            _new_events(self)
-        x, w, ev = self.x, self.w, self.ev
-        rec = (lambda i: ev[i].record()) if timed_phases else (lambda i: None)
-        rec(0)
-        fl.encode(x["Q"], x["K"], x["V"], w.offsets, x.get("mask"), w.scale, self.O, self.Lp)
-        rec(1)
-        fl.lse_merge(self.O, self.Lp, Z=self.Z, L=self.L)
-        rec(2)
 
-    collect = FlareppStep.collect
+class FlareStep(EncodeMergeStep):
+    """FLARE block: encode -> merge -> decode of every token (K as token queries, Q as latent keys)."""
+
+    def __init__(self, w: W.Workload, x, fused=False):
+        self.Y = torch.empty_like(x["K"])
+        super().__init__(w, x, fused, [("decode", lambda: fl.decode(x["K"], x["Q"], self.Z, w.scale, None,
+                                                                     self.Y))])
 
 
 class FwdBwdStep(EncodeMergeStep):
     """Masked encoder forward + merge, then the encoder backward with the global statistics."""
 
-    def __init__(self, w: W.Workload, x):
-        super().__init__(w, x)
+    def __init__(self, w: W.Workload, x, fused=False):
         B, H, M, D = w.B, w.H, w.M, w.D
         dev = x["K"].device
         self.dQ = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
         self.dK = torch.empty_like(x["K"])
         self.dV = torch.empty_like(x["V"])
-        self.names = ["encode", "merge", "backward"]
-        self.ev = [_ev() for _ in range(len(self.names) + 1)]
-        self.phase_ms = [0.0] * len(self.names)
-
-    def __call__(self, timed_phases: bool):
-        super().__call__(timed_phases)
-        x, w = self.x, self.w
-        fl.encode_bwd(x["Q"], x["K"], x["V"], w.offsets, x.get("mask"), w.scale, self.Z, self.L, x["dZ"],
-                      self.dQ, self.dK, self.dV)
-        if timed_phases:
-            self.ev[3].record()
+        bwd = ("backward", lambda: fl.encode_bwd(x["Q"], x["K"], x["V"], w.offsets, x.get("mask"), w.scale, self.Z,
+                                                 self.L, x["dZ"], self.dQ, self.dK, self.dV))
+        super().__init__(w, x, fused, [bwd])
 
 
 def _oracle_cores():
@@ -270,18 +238,23 @@ def roofline_of(w: W.Workload, x, step, ph):
         ms = 0.5 * (ph["encode2_bwd"] + ph["encode1_bwd"])
         return ms, (5 + 4) * rows * row // 2, ("flare_encode_bwd call (row term, key/value-gradient kernel with "
                                                 "fused query gradient, reduce); both encoder backwards averaged")
+    if w.kind == "flarepp" and "encode_merge1" in ph:
+        ms = 0.5 * (ph["encode_merge1"] + ph["encode_merge2"])
+        return ms, 2 * rows * row, ("encode_ilv_kernel with the merge inside (flare_encode_merge, one launch; "
+                                    "both encoders averaged)")
     if w.kind == "flarepp":
         ms = 0.5 * (ph["encode1"] + ph["encode2"])
         return ms, 2 * rows * row, "encode_ilv_kernel (flare_encode, one launch; both encoders averaged)"
     if w.kind == "flare":
-        if ph["decode"] > ph["encode"]:
+        enc = ph.get("encode", ph.get("encode_merge"))
+        if ph["decode"] > enc:
             return ph["decode"], 2 * rows * row, "decode_mfma_kernel (flare_decode, one launch)"
-        return ph["encode"], 2 * rows * row, "encode_mfma_kernel (flare_encode, one launch)"
+        return enc, 2 * rows * row, "encode_mfma_kernel (flare_encode, one launch)"
     if w.kind == "encode_bwd":
         valid = int(x["mask"].sum().item()) * w.H if "mask" in x else rows
         return (ph["backward"], 2 * valid * row + 2 * rows * row,
                 "flare_encode_bwd call (row term, query-gradient, key/value-gradient and reduce kernels)")
-    return ph["encode"], 2 * rows * row, "flare_encode call (one encoder launch)"
+    return ph.get("encode", ph.get("encode_merge")), 2 * rows * row, "flare_encode call (one encoder launch)"
 
 
 def copy_reference(nbytes=1 << 30, reps=5):
@@ -307,8 +280,8 @@ class FlareppTrainStep(FlareppStep):
     """FLARE++ forward chain followed by its backward chain (decoder, physical-value
     encoder, query-synthesis encoder) with preallocated gradients."""
 
-    def __init__(self, w: W.Workload, x):
-        super().__init__(w, x)
+    def __init__(self, w: W.Workload, x, fused=False):
+        super().__init__(w, x, fused)
         dev = x["K"].device
         B, H, M, D = w.B, w.H, w.M, w.D
         f32 = dict(dtype=torch.float32, device=dev)
@@ -322,22 +295,14 @@ class FlareppTrainStep(FlareppStep):
         self.dQt = torch.empty((B, H, M, D), **f32)
         self.dZ2c = torch.empty((B, H, M, D), dtype=torch.bfloat16, device=dev)
         self.dQXc = torch.empty((B, H, M, D), dtype=torch.bfloat16, device=dev)
-        self.names = self.names + ["decode_bwd", "encode2_bwd", "encode1_bwd"]
-        self.ev = [_ev() for _ in range(len(self.names) + 1)]
-        self.phase_ms = [0.0] * len(self.names)
-
-    def __call__(self, timed_phases: bool):
-        super().__call__(timed_phases)
-        x, w, ev = self.x, self.w, self.ev
-        rec = (lambda i: ev[i].record()) if timed_phases else (lambda i: None)
-        fl.decode_bwd(x["K"], self.QXb, self.Z, w.scale, self.dY, None, self.dK, self.dQX, self.dZ2, self.dZ2c)
-        rec(6)
-        fl.encode_bwd(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, self.Z, self.L, self.dZ2c, dQ=self.dQX,
-                      dK=self.dK, dV=self.dV, dQ_cast=self.dQXc, flags=fl.ACCUMULATE_DQ | fl.ACCUMULATE_DK)
-        rec(7)
-        fl.encode_bwd(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.QX, self.QXL, self.dQXc,
-                      dQ=self.dQt, dK=self.dKt, dV=self.dVt)
-        rec(8)
+        self._phases(self.phases + [
+            ("decode_bwd", lambda: fl.decode_bwd(x["K"], self.QXb, self.Z, w.scale, self.dY, None, self.dK, self.dQX,
+                                                 self.dZ2, self.dZ2c)),
+            ("encode2_bwd", lambda: fl.encode_bwd(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, self.Z, self.L,
+                                                  self.dZ2c, dQ=self.dQX, dK=self.dK, dV=self.dV, dQ_cast=self.dQXc,
+                                                  flags=fl.ACCUMULATE_DQ | fl.ACCUMULATE_DK)),
+            ("encode1_bwd", lambda: fl.encode_bwd(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.QX,
+                                                  self.QXL, self.dQXc, dQ=self.dQt, dK=self.dKt, dV=self.dVt))])
 
 
 STEPS = {"flarepp": FlareppStep, "flare": FlareStep, "splitkv": EncodeMergeStep, "encode": EncodeMergeStep,
@@ -358,6 +323,12 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="FLARE++ only: time the forward chain plus its backward chain (a training step "
                          "of the mixer); not the headline metric")
+    ap.add_argument("--fused", action="store_true",
+                    help="each encoder and its merge as one call (flare_encode_merge: the merge runs in the "
+                         "encoder launch)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and replay it for the warm-up and timed steps "
+                         "(the per-phase pass stays eager)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device 3 times "
                          "(the plain copy that scales the HBM byte counters)")
@@ -375,9 +346,23 @@ def main():
     if args.backward and w.kind != "flarepp":
         print("--backward is defined for the FLARE++ workload only", file=sys.stderr)
         sys.exit(2)
-    step = FlareppTrainStep(w, x) if args.backward else STEPS[w.kind](w, x)
+    step = FlareppTrainStep(w, x, args.fused) if args.backward else STEPS[w.kind](w, x, args.fused)
+    run = lambda: step(timed_phases=False)  # noqa: E731
+    if args.graph:
+        # one eager step on a side stream sizes the library's cached workspace
+        # and counters outside the capture
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        run = graph.replay
     for _ in range(args.warmup):
-        step(timed_phases=False)
+        run()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, synchronised on both sides
@@ -386,7 +371,7 @@ def main():
     t_start.record()
     wall0 = time.perf_counter()
     for _ in range(args.steps):
-        step(timed_phases=False)
+        run()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -420,7 +405,9 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": f"synthetic (seeded N(0,1) inputs{' rounded to bf16' if w.dtype == 'bf16' else ''})",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "R": w.R,
-                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU",
+                   "encode_merge": "one call" if args.fused else "two calls",
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if is_main else None,
                      "kernel": kern_name, "kernel_ms": kern_ms, "algorithmic_bytes": kern_bytes},

@@ -114,6 +114,39 @@ flare_status lse_merge(int R, int64_t rows, int D, const float* O_part, const fl
                        float* Z, float* L, void* Z_bf16, flare_stream_t stream);
 
 /*
+ * flare_encode_merge -- flare_encode followed by lse_merge of its R states,
+ * in one call ([FLARE++]: the encoder, then the exact merge of eqs. 21-23;
+ * [RING]: the tree schedule).  Outputs O_part, L_part, Z, L and Z_bf16 are
+ * exactly those of flare_encode then lse_merge(R, B*H*M, D, O_part, L_part,
+ * Z, L, Z_bf16) (same arithmetic in the same order, so bit for bit); the
+ * arguments they share mean the same and are validated the same way, and the
+ * workspace is flare_encode_workspace_size() bytes.
+ *
+ * On the matrix-core path (see flare_encode's supported shapes), when one
+ * encoder launch covers every token chunk (up to 256 chunks) and R <= 256, the
+ * merge runs inside that launch: the last workgroup to finish a partition that
+ * was cut into chunks folds that partition, and the last one to finish a
+ * (batch, head) slice merges its partitions, so the call makes a single launch
+ * (plus the mask preparation of masked inputs).  Otherwise it makes the
+ * launches of the two calls.
+ *
+ * counters: device array of B*H*(R+1) uint32, 4-byte aligned, owned by the caller.
+ * It must hold zeros when the call runs, and every call puts it back to zero
+ * by the time its work on the stream has finished (allocate it zeroed once and
+ * keep it).  Two calls whose work may overlap in time on one device (other
+ * streams, or a graph replayed alongside) need separate counter arrays; a
+ * counter array left nonzero by a failed launch must be zeroed again before
+ * the next call.  The call issues no memset and no allocation, so it may be
+ * captured in a HIP graph.
+ */
+flare_status flare_encode_merge(flare_dtype dtype, int B, int H, int N, int M, int D,
+                                const void* Q, int64_t q_batch_stride, const void* K, const void* V,
+                                int R, const int64_t* offsets, const uint8_t* mask, float scale,
+                                float* O_part, float* L_part, float* Z, float* L, void* Z_bf16,
+                                uint32_t* counters, void* workspace, size_t workspace_bytes,
+                                flare_stream_t stream);
+
+/*
  * flare_decode -- the local decode of [FLARE++] (FLARE and FLARE++ forward
  * paragraphs): every token attends over the M replicated latents,
  *     Y[b,h,n,:] = sum_m softmax_m(scale * Xq[b,h,n,:].Klat[b,h,m,:]) Z[b,h,m,:]

@@ -9,6 +9,7 @@ library is missing or no GPU is present, the calls raise.
 Shapes (see the header for the contract):
   encode:     Q [H,M,D] or [B,H,M,D]; K, V [B,H,N,D]  ->  O_part [R,B,H,M,D], L_part [R,B,H,M]
   lse_merge:  O_part, L_part                          ->  Z [.., M, D], L [.., M] (+ bf16 Z)
+  encode_merge: encode then lse_merge in one call     ->  O_part, L_part, Z, L (+ bf16 Z)
   decode:     Xq [B,H,N,D], Klat [H,M,D] or [B,H,M,D], Z [B,H,M,D] -> Y [B,H,N,D]
   encode_bwd: + Z, L, dZ                              ->  dQ [B,H,M,D], dK, dV [B,H,N,D]
 """
@@ -20,7 +21,7 @@ from typing import Dict, Optional, Sequence, Tuple
 
 import torch  # noqa: F401  (loaded first so the library binds to torch's HIP runtime)
 
-__all__ = ["FlareError", "encode", "lse_merge", "decode", "encode_bwd", "decode_bwd", "flare_forward",
+__all__ = ["FlareError", "encode", "lse_merge", "encode_merge", "decode", "encode_bwd", "decode_bwd", "flare_forward",
            "flarepp_forward", "flarepp_backward", "encode_workspace_size", "encode_bwd_workspace_size",
            "decode_bwd_workspace_size", "library_path", "scale_for", "ACCUMULATE_DQ", "ACCUMULATE_DK"]
 
@@ -61,6 +62,9 @@ def _load():
     lib.flare_encode.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp,
                                  vp, sz, vp]
     lib.flare_encode.restype = i32
+    lib.flare_encode_merge.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp,
+                                       vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.flare_encode_merge.restype = i32
     lib.lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.lse_merge.restype = i32
     lib.flare_decode.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp]
@@ -210,6 +214,74 @@ def encode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, offsets: Sequence[
         _check(lib.flare_encode(code, B, H, N, M, D, _ptr(Q), qbs, _ptr(K), _ptr(V), R, offs, _ptr(mask),
                                 float(scale), _ptr(O_part), _ptr(L_part), _ptr(ws), nbytes, _stream()))
     return O_part, L_part
+
+
+_cnt_cache: Dict[int, torch.Tensor] = {}
+
+
+def merge_counters(n: int, device) -> torch.Tensor:
+    """The per-device array of arrival counters encode_merge hands to the library
+    (zeroed once when allocated; every call leaves it zero)."""
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    t = _cnt_cache.get(key)
+    if t is None or t.numel() < n:
+        t = torch.zeros(max(n, 1024), dtype=torch.int32, device=device)
+        _cnt_cache[key] = t
+    return t
+
+
+def encode_merge(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, offsets: Sequence[int],
+                 mask: Optional[torch.Tensor] = None, scale: Optional[float] = None, want_bf16: bool = False,
+                 O_part: Optional[torch.Tensor] = None, L_part: Optional[torch.Tensor] = None,
+                 Z: Optional[torch.Tensor] = None, L: Optional[torch.Tensor] = None,
+                 Z_bf16: Optional[torch.Tensor] = None, counters: Optional[torch.Tensor] = None):
+    """encode then lse_merge in one C-ABI call (one launch on the matrix-core path):
+    -> (O_part, L_part, Z, L, Z_bf16 or None).  counters: int32 [>= B*H*(R+1)] zeros
+    (default: a per-device array kept by this module)."""
+    lib = _load()
+    _kv_check(K, V, Q)
+    B, H, N, D = K.shape
+    M, qbs = _q_layout(Q, B, H, D)
+    R = len(offsets) - 1
+    mask = _mask_check(mask, B, N, K.device)
+    if scale is None:
+        scale = scale_for(D)
+    dev = K.device
+    if O_part is None:
+        O_part = torch.empty((R, B, H, M, D), dtype=torch.float32, device=dev)
+    if L_part is None:
+        L_part = torch.empty((R, B, H, M), dtype=torch.float32, device=dev)
+    if Z is None:
+        Z = torch.empty((B, H, M, D), dtype=torch.float32, device=dev)
+    if L is None:
+        L = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+    if want_bf16 and Z_bf16 is None:
+        Z_bf16 = torch.empty((B, H, M, D), dtype=torch.bfloat16, device=dev)
+    if tuple(O_part.shape) != (R, B, H, M, D) or tuple(L_part.shape) != (R, B, H, M):
+        raise ValueError("O_part / L_part have the wrong shape")
+    if tuple(Z.shape) != (B, H, M, D) or tuple(L.shape) != (B, H, M):
+        raise ValueError("Z / L have the wrong shape")
+    if Z_bf16 is not None and (tuple(Z_bf16.shape) != (B, H, M, D) or Z_bf16.dtype != torch.bfloat16):
+        raise ValueError("Z_bf16 must be bfloat16 [B,H,M,D]")
+    for t, name in ((O_part, "O_part"), (L_part, "L_part"), (Z, "Z"), (L, "L")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+        _dev(t, name)
+    ncnt = B * H * (R + 1)
+    if counters is None:
+        counters = merge_counters(ncnt, dev)
+    if counters.dtype != torch.int32 or counters.numel() < ncnt:
+        raise ValueError("counters must be int32 with at least B*H*(R+1) entries")
+    _dev(counters, "counters")
+    offs = _offsets(offsets)
+    code = _dtype_code(K)
+    nbytes = int(lib.flare_encode_workspace_size(code, B, H, N, M, D, R, offs, int(mask is not None)))
+    ws = _workspace(nbytes, dev)
+    with torch.cuda.device(dev):
+        _check(lib.flare_encode_merge(code, B, H, N, M, D, _ptr(Q), qbs, _ptr(K), _ptr(V), R, offs, _ptr(mask),
+                                      float(scale), _ptr(O_part), _ptr(L_part), _ptr(Z), _ptr(L), _ptr(Z_bf16),
+                                      _ptr(counters), _ptr(ws), nbytes, _stream()))
+    return O_part, L_part, Z, L, Z_bf16
 
 
 def lse_merge(O_part: torch.Tensor, L_part: torch.Tensor, want_bf16: bool = False,
@@ -371,10 +443,15 @@ def decode_bwd(Xq, Klat, Z, scale, dY, token_mask=None, dXq=None, dKlat=None, dZ
     return dXq, dKlat, dZ
 
 
-def flare_forward(Q, K, V, offsets, mask=None, scale=None, token_mask=None):
-    """FLARE block mixer: Z = merge(encode(Q, K, V)); Y = decode(K, Q, Z)."""
-    O_part, L_part = encode(Q, K, V, offsets, mask, scale)
-    Z, L, _ = lse_merge(O_part, L_part)
+def flare_forward(Q, K, V, offsets, mask=None, scale=None, token_mask=None, fused=False):
+    """FLARE block mixer: Z = merge(encode(Q, K, V)); Y = decode(K, Q, Z).
+    fused=True makes the encode and the merge one call, flare_encode_merge (same
+    results; one launch, but slower than two on MI355X at the measured shapes)."""
+    if fused:
+        O_part, L_part, Z, L, _ = encode_merge(Q, K, V, offsets, mask, scale)
+    else:
+        O_part, L_part = encode(Q, K, V, offsets, mask, scale)
+        Z, L, _ = lse_merge(O_part, L_part)
     Y = decode(K, Q, Z, scale, token_mask)
     return {"O_part": O_part, "L_part": L_part, "Z": Z, "L": L, "Y": Y}
 
@@ -400,17 +477,25 @@ def flarepp_backward(fwd, Qt, Kt, Vt, K, V, offsets, dY, scale=None):
     return {"dQt": dQt, "dKt": dKt, "dVt": dVt, "dK": dK, "dV": dV, "dQX": dQX}
 
 
-def flarepp_forward(Qt, Kt, Vt, K, V, offsets, scale=None):
+def flarepp_forward(Qt, Kt, Vt, K, V, offsets, scale=None, fused=False):
     """FLARE++: Q(X) = merge(encode(Qt, Kt, Vt)); Z = merge(encode(Q(X), K, V)); Y = decode(K, Q(X), Z).
 
     The dynamic queries are consumed in the input dtype (the merge writes a
-    bfloat16 copy next to the float32 result for bfloat16 inputs).
+    bfloat16 copy next to the float32 result for bfloat16 inputs).  fused=True
+    makes each encode and its merge one call, flare_encode_merge (same results).
     """
-    O1, L1 = encode(Qt, Kt, Vt, offsets, None, scale)
-    QX, QX_L, QXb = lse_merge(O1, L1, want_bf16=(K.dtype == torch.bfloat16))
+    bf16 = K.dtype == torch.bfloat16
+    if fused:
+        O1, L1, QX, QX_L, QXb = encode_merge(Qt, Kt, Vt, offsets, None, scale, want_bf16=bf16)
+    else:
+        O1, L1 = encode(Qt, Kt, Vt, offsets, None, scale)
+        QX, QX_L, QXb = lse_merge(O1, L1, want_bf16=bf16)
     QXin = QXb if QXb is not None else QX
-    O2, L2 = encode(QXin, K, V, offsets, None, scale)
-    Z, L, _ = lse_merge(O2, L2)
+    if fused:
+        O2, L2, Z, L, _ = encode_merge(QXin, K, V, offsets, None, scale)
+    else:
+        O2, L2 = encode(QXin, K, V, offsets, None, scale)
+        Z, L, _ = lse_merge(O2, L2)
     Y = decode(K, QXin, Z, scale)
     return {"QX": QX, "QX_L": QX_L, "QX_in": QXin, "QX_O_part": O1, "QX_L_part": L1,
             "O_part": O2, "L_part": L2, "Z": Z, "L": L, "Y": Y}

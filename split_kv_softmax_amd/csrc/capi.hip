@@ -196,10 +196,42 @@ size_t flare_encode_workspace_size(flare_dtype dtype, int B, int H, int N, int M
   return plan_encode(dtype, B, H, N, M, D, R, offsets, masked != 0).ws_bytes;
 }
 
-flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
-                          int64_t q_batch_stride, const void* K, const void* V, int R,
-                          const int64_t* offsets, const uint8_t* mask, float scale, float* O_part,
-                          float* L_part, void* workspace, size_t workspace_bytes, flare_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Outputs of the merged form (flare_encode_merge); null: states only.
+struct MergeOut {
+  uint32_t* counters;
+  float* Z;
+  float* L;
+  void* Z_bf16;
+};
+
+flare_status merge_states(int R, int64_t rows, int D, const float* O_part, const float* L_part, float* Z, float* L,
+                          void* Z_bf16, hipStream_t s) {
+  FoldArgs f;
+  memset(&f, 0, sizeof(f));
+  f.in_O = O_part;
+  f.in_L = L_part;
+  f.out_O = Z;
+  f.out_L = L;
+  f.out_bf16 = static_cast<uint16_t*>(Z_bf16);
+  f.rows = rows;
+  f.D = D;
+  f.tab.ngroups = 1;
+  f.tab.in_begin[0] = 0;
+  f.tab.in_begin[1] = R;
+  f.tab.out_index[0] = 0;
+  hipError_t e = launch_fold(f, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return FLARE_OK;
+}
+
+flare_status encode_impl(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
+                         int64_t q_batch_stride, const void* K, const void* V, int R, const int64_t* offsets,
+                         const uint8_t* mask, float scale, float* O_part, float* L_part, void* workspace,
+                         size_t workspace_bytes, flare_stream_t stream, const MergeOut* mo) {
   flare_status st = check_common(dtype, B, H, N, M, D);
   if (st != FLARE_OK) return st;
   st = check_offsets(N, R, offsets);
@@ -217,6 +249,12 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, 
       return fail(FLARE_EINVAL, "Q, K, V and the Q batch stride must be 16-byte aligned");
   }
   if (!aligned16(O_part)) return fail(FLARE_EINVAL, "O_part must be 16-byte aligned");
+  if (mo) {
+    if (!mo->Z || !mo->L || !mo->counters) return fail(FLARE_EINVAL, "Z, L and counters must not be NULL");
+    if (!aligned16(mo->Z)) return fail(FLARE_EINVAL, "Z must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(mo->Z_bf16) & 7u) return fail(FLARE_EINVAL, "Z_bf16 must be 8-byte aligned");
+    if (reinterpret_cast<uintptr_t>(mo->counters) & 3u) return fail(FLARE_EINVAL, "counters must be 4-byte aligned");
+  }
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return fail(FLARE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
@@ -257,10 +295,23 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, 
     hipError_t e = launch_mask_words(mask, B, N, reinterpret_cast<uint64_t*>(ws), plan.mw_stride, s);
     if (e != hipSuccess) return hip_fail(e, "mask launch");
   }
-  (void)per;
+
+  // The merge runs inside the matrix-core encoder launch when that one launch
+  // holds every chunk (each (batch, head) then has nc workgroups in it).
+  const int nc = (int)plan.chunks.size();
+  const bool fused = mo && plan.kind == EncKind::Mfma && nc >= 1 && nc <= kMaxChunks && R <= kMaxFuseParts;
+  if (fused) {
+    a.fz.cnt = mo->counters;
+    int nonempty = 0;
+    for (int r = 0; r < R; ++r) nonempty += plan.first_chunk[r + 1] > plan.first_chunk[r];
+    a.fz.target = nonempty;
+    a.fz.Z = mo->Z;
+    a.fz.L = mo->L;
+    a.fz.Zb = static_cast<uint16_t*>(mo->Z_bf16);
+    for (int r = 0; r <= R; ++r) a.fz.pchunk[r] = (int16_t)plan.first_chunk[r];
+  }
 
   // encoder launches over groups of at most kMaxChunks consecutive chunks
-  const int nc = (int)plan.chunks.size();
   for (int c0 = 0; c0 < nc; c0 += kMaxChunks) {
     const int n = std::min(kMaxChunks, nc - c0);
     a.tab.nchunks = n;
@@ -284,6 +335,7 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, 
     }
     if (e != hipSuccess) return hip_fail(e, "encode launch");
   }
+  if (fused) return FLARE_OK;
 
   // fold split partitions and write the empty state of empty partitions
   FoldArgs f;
@@ -317,7 +369,30 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, 
   }
   hipError_t e = flush();
   if (e != hipSuccess) return hip_fail(e, "fold launch");
+  if (mo) return merge_states(R, (int64_t)per, D, O_part, L_part, mo->Z, mo->L, mo->Z_bf16, s);
   return FLARE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
+                          int64_t q_batch_stride, const void* K, const void* V, int R,
+                          const int64_t* offsets, const uint8_t* mask, float scale, float* O_part,
+                          float* L_part, void* workspace, size_t workspace_bytes, flare_stream_t stream) {
+  return encode_impl(dtype, B, H, N, M, D, Q, q_batch_stride, K, V, R, offsets, mask, scale, O_part, L_part,
+                     workspace, workspace_bytes, stream, nullptr);
+}
+
+flare_status flare_encode_merge(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
+                                int64_t q_batch_stride, const void* K, const void* V, int R,
+                                const int64_t* offsets, const uint8_t* mask, float scale, float* O_part,
+                                float* L_part, float* Z, float* L, void* Z_bf16, uint32_t* counters,
+                                void* workspace, size_t workspace_bytes, flare_stream_t stream) {
+  const MergeOut mo{counters, Z, L, Z_bf16};
+  return encode_impl(dtype, B, H, N, M, D, Q, q_batch_stride, K, V, R, offsets, mask, scale, O_part, L_part,
+                     workspace, workspace_bytes, stream, &mo);
 }
 
 flare_status lse_merge(int R, int64_t rows, int D, const float* O_part, const float* L_part, float* Z,
@@ -330,22 +405,7 @@ flare_status lse_merge(int R, int64_t rows, int D, const float* O_part, const fl
   if (!O_part || !L_part || !Z || !L) return fail(FLARE_EINVAL, "NULL pointer argument");
   if (!aligned16(O_part) || !aligned16(Z)) return fail(FLARE_EINVAL, "O_part and Z must be 16-byte aligned");
   if (Z_bf16 && (reinterpret_cast<uintptr_t>(Z_bf16) & 7u)) return fail(FLARE_EINVAL, "Z_bf16 must be 8-byte aligned");
-  FoldArgs f;
-  memset(&f, 0, sizeof(f));
-  f.in_O = O_part;
-  f.in_L = L_part;
-  f.out_O = Z;
-  f.out_L = L;
-  f.out_bf16 = static_cast<uint16_t*>(Z_bf16);
-  f.rows = rows;
-  f.D = D;
-  f.tab.ngroups = 1;
-  f.tab.in_begin[0] = 0;
-  f.tab.in_begin[1] = R;
-  f.tab.out_index[0] = 0;
-  hipError_t e = launch_fold(f, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
-  return FLARE_OK;
+  return merge_states(R, rows, D, O_part, L_part, Z, L, Z_bf16, static_cast<hipStream_t>(stream));
 }
 
 flare_status flare_decode(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Xq,

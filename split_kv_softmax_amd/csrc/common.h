@@ -210,4 +210,211 @@ __device__ __forceinline__ uint64_t mask_tile_bits(const_u64* mw, int t0) {
   return (lo >> sh) | (mw[w + 1] << (64 - sh));
 }
 
+// ---- merge of (m, l, acc) states ("Ring vs. Tree Attention": the online-
+// softmax merge; "FLARE++" appendix, eq. 23).  Natural-log units: a leaf
+// (O_r, L_r) enters as (L_r, 1, O_r), an empty one as (-inf, 0, 0).  Merging a
+// state with an empty one returns it bit for bit (factor exp(0) = 1 on its
+// side, exactly 0 on the empty side).  Shared by the tree merge kernel and the
+// fused encode + merge, so both give the same bits.
+struct MState {
+  float m, l;
+  f32x4_t acc;
+};
+
+__device__ __forceinline__ MState mstate_empty() { return MState{kNegInf, 0.f, f32x4_t{0.f, 0.f, 0.f, 0.f}}; }
+
+__device__ __forceinline__ MState mstate_leaf(float L, f32x4_t O) {
+  const bool e = L == kNegInf;
+  return MState{L, e ? 0.f : 1.f, e ? f32x4_t{0.f, 0.f, 0.f, 0.f} : O};
+}
+
+// The roundings of a merge are spelled out (one product, then a fused
+// multiply-add) and the compiler may not contract anything else, so that every
+// kernel that merges rounds alike whatever it can prove about the operands.
+__device__ __forceinline__ MState mstate_merge(const MState& x, const MState& y) {
+#pragma clang fp contract(off)
+  MState r;
+  r.m = fmaxf(x.m, y.m);
+  if (r.m == kNegInf) return mstate_empty();
+  const float fx = __expf(x.m - r.m);   // exactly 0 for an empty side
+  const float fy = __expf(y.m - r.m);
+  r.l = __builtin_fmaf(x.l, fx, y.l * fy);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r.acc[j] = __builtin_fmaf(x.acc[j], fx, y.acc[j] * fy);
+  return r;
+}
+
+// Normalised output of a merged state: O = acc / l (0 when empty), L = m + ln l (-inf when empty).
+__device__ __forceinline__ void mstate_finish(const MState& cur, f32x4_t& z, float& L) {
+#pragma clang fp contract(off)
+  const bool empty = !(cur.l > 0.f);
+  const float inv = empty ? 0.f : 1.f / cur.l;
+  z = cur.acc * inv;
+  if (empty) z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  L = empty ? kNegInf : cur.m + __logf(cur.l);
+}
+
+// Fold of states s0 .. s0+n-1 (n >= 0) of one row and one 4-column piece:
+// state s has log-normaliser in_L[s*rows + row] and output columns
+// in_O[s*sstride + off .. +4) (off = row*D + 4*piece).  Up to 16 states every
+// load is issued at once (indices past the end re-read the last state),
+// absent leaves are empty, and the rounds of the 16-leaf tree run on them
+// (fold_static, on the narrowest power-of-two width that holds n); merging
+// with an empty leaf returns the state unchanged, so this is the tree with
+// pass-through survivors.  Beyond 16 the leaves are visited in order
+// (16 loads at a time) keeping one partial state per tree level, a binary
+// counter: after leaf i the levels whose bit is set in i are merged into it
+// (left subtree first), and at the end the occupied levels are merged from the
+// lowest upwards, which is the round schedule with its pass-through
+// survivors.  i is the same for every thread, so the branches are uniform.
+// (The level walk is written out in each fold: behind a helper the level
+// array is no longer promoted to registers.)
+constexpr int kFoldBatch = 16;
+constexpr int kFoldLevels = 16;   // up to 65536 states
+
+// The rounds of the W-leaf tree over states s0 .. s0+n-1, 1 <= n <= W (W a
+// power of two), every load issued at once.  For n <= W/2 the upper half of
+// the leaves is empty and each merge with it returns the state unchanged, so
+// the narrowest W that holds n gives the result of any wider one.
+template <int W>
+__device__ __forceinline__ MState fold_static(const float* in_O, const float* in_L, int64_t s0, int n,
+                                              int64_t rows, int64_t row, int64_t off, int64_t sstride) {
+  MState t[W];
+  float Lb[W];
+  f32x4_t Ob[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    const int64_t s = s0 + (k < n ? k : n - 1);
+    Lb[k] = in_L[s * rows + row];
+    Ob[k] = *reinterpret_cast<const f32x4_t*>(in_O + s * sstride + off);
+  }
+#pragma unroll
+  for (int k = 0; k < W; ++k) t[k] = k < n ? mstate_leaf(Lb[k], Ob[k]) : mstate_empty();
+#pragma unroll
+  for (int w2 = 1; w2 < W; w2 *= 2)
+#pragma unroll
+    for (int i = 0; i < W; i += 2 * w2) t[i] = mstate_merge(t[i], t[i + w2]);
+  return t[0];
+}
+
+__device__ __forceinline__ MState fold_states(const float* in_O, const float* in_L, int64_t s0, int n,
+                                              int64_t rows, int64_t row, int64_t off, int64_t sstride) {
+  if (n == 0) return mstate_empty();
+  if (n == 1) return fold_static<1>(in_O, in_L, s0, n, rows, row, off, sstride);
+  if (n == 2) return fold_static<2>(in_O, in_L, s0, n, rows, row, off, sstride);
+  if (n <= 4) return fold_static<4>(in_O, in_L, s0, n, rows, row, off, sstride);
+  if (n <= 8) return fold_static<8>(in_O, in_L, s0, n, rows, row, off, sstride);
+  if (n <= kFoldBatch) return fold_static<kFoldBatch>(in_O, in_L, s0, n, rows, row, off, sstride);
+  MState lv[kFoldLevels];
+  for (int i0 = 0; i0 < n; i0 += kFoldBatch) {
+    float Lb[kFoldBatch];
+    f32x4_t Ob[kFoldBatch];
+#pragma unroll
+    for (int k = 0; k < kFoldBatch; ++k) {
+      const int64_t s = s0 + (i0 + k < n ? i0 + k : n - 1);
+      Lb[k] = in_L[s * rows + row];
+      Ob[k] = *reinterpret_cast<const f32x4_t*>(in_O + s * sstride + off);
+    }
+#pragma unroll
+    for (int k = 0; k < kFoldBatch; ++k) {
+      const int i = i0 + k;
+      if (i < n) {
+        MState leaf = mstate_leaf(Lb[k], Ob[k]);
+        bool carry = true;
+#pragma unroll
+        for (int lvl = 0; lvl < kFoldLevels; ++lvl) {
+          if (carry) {
+            if ((i >> lvl) & 1) {
+              leaf = mstate_merge(lv[lvl], leaf);
+            } else {
+              lv[lvl] = leaf;
+              carry = false;
+            }
+          }
+        }
+      }
+    }
+  }
+  MState cur = mstate_empty();
+  bool have = false;
+#pragma unroll
+  for (int lvl = 0; lvl < kFoldLevels; ++lvl) {
+    if ((n >> lvl) & 1) {
+      cur = have ? mstate_merge(lv[lvl], cur) : lv[lvl];
+      have = true;
+    }
+  }
+  return cur;
+}
+
+// The same fold with few registers, for n <= 256 states: the binary counter
+// over the leaves, four loads at a time.  Up to 16 states it counts exactly 16
+// leaves (the absent ones empty), which builds the complete 16-leaf tree of
+// fold_states merge by merge (left subtree first in every merge); beyond 16 it
+// counts the n leaves as fold_states does.  The results are therefore
+// identical.
+__device__ __forceinline__ MState fold_states_lean(const float* in_O, const float* in_L, int64_t s0, int n,
+                                                   int64_t rows, int64_t row, int64_t off, int64_t sstride) {
+  constexpr int kLv = 9;   // 256 leaves
+  if (n == 0) return mstate_empty();
+  MState lv[kLv];
+  const int total = n <= kFoldBatch ? kFoldBatch : n;
+  for (int i0 = 0; i0 < total; i0 += 4) {
+    float Lb[4];
+    f32x4_t Ob[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t s = s0 + (i0 + k < n ? i0 + k : n - 1);
+      Lb[k] = in_L[s * rows + row];
+      Ob[k] = *reinterpret_cast<const f32x4_t*>(in_O + s * sstride + off);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = i0 + k;
+      if (i < total) {
+        MState leaf = i < n ? mstate_leaf(Lb[k], Ob[k]) : mstate_empty();
+        bool carry = true;
+#pragma unroll
+        for (int lvl = 0; lvl < kLv; ++lvl) {
+          if (carry) {
+            if ((i >> lvl) & 1) {
+              leaf = mstate_merge(lv[lvl], leaf);
+            } else {
+              lv[lvl] = leaf;
+              carry = false;
+            }
+          }
+        }
+      }
+    }
+  }
+  MState cur = mstate_empty();
+  bool have = false;
+#pragma unroll
+  for (int lvl = 0; lvl < kLv; ++lvl) {
+    if ((total >> lvl) & 1) {
+      cur = have ? mstate_merge(lv[lvl], cur) : lv[lvl];
+      have = true;
+    }
+  }
+  return cur;
+}
+
+// Store a folded state as output state oi: normalised columns (and their
+// bfloat16 copy when out_bf16 is set), and the log-normaliser from the thread
+// that holds the row's first piece.
+__device__ __forceinline__ void store_state(const MState& cur, float* out_O, float* out_L, uint16_t* out_bf16,
+                                            int64_t oi, int64_t rows, int64_t row, int64_t off, int64_t sstride,
+                                            int D) {
+  f32x4_t z;
+  float Lz;
+  mstate_finish(cur, z, Lz);
+  *reinterpret_cast<f32x4_t*>(out_O + oi * sstride + off) = z;
+  if (off % D == 0) out_L[oi * rows + row] = Lz;
+  if (out_bf16) {
+    const u32x2_t wv = {pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+    *reinterpret_cast<u32x2_t*>(out_bf16 + oi * sstride + off) = wv;
+  }
+}
+
 }  // namespace flare

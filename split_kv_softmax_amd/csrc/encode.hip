@@ -92,6 +92,94 @@ __device__ __forceinline__ void finish_chunk(uint8_t* smem, const EncodeArgs& a,
   if (hh == 0) Lb[m] = empty ? kNegInf : (m_run * a.scale + __logf(l_tot));
 }
 
+// Fused merge (see FuseTable).  Publication: every wave waits until its own
+// stores have reached the L2 of its XCD, the workgroup meets at a barrier, and
+// one thread issues the device-scope release (a write-back of that L2, so the
+// stores reach memory that every XCD reads) before it counts; the workgroup
+// whose count completes a total issues the device-scope acquire (dropping
+// stale cached lines) before it reads what the others stored.  One release
+// per count and acquires only in the completing workgroups: a full fence in
+// every thread would write back and invalidate the L2 under the workgroups
+// still streaming.  Returns whether this workgroup completed the count.
+// sflag: one int of LDS that no thread reads or writes any more.
+__device__ __forceinline__ bool publish_and_count(uint32_t* cnt, uint32_t target, int* sflag) {
+  wait_vm<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool last = atomicAdd(cnt, 1u) + 1u == target;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *sflag = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *sflag != 0;
+  __syncthreads();   // every thread has read the flag before it can be reused
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+// Merge tail of the workgroup that stored the state of chunk c of (b, h).  A
+// chunk of a partition split over several chunks counts on that partition's
+// counter; the workgroup that completes it folds the partition's chunk states
+// into O_part / L_part (on its own CU, so the partitions of a slice fold in
+// parallel) and then counts on the slice's counter, as a chunk that is a whole
+// partition does at once.  The workgroup that completes the slice writes the
+// empty state of the partitions without a token and merges the R partition
+// states into Z / L.  Every fold takes the merge kernels' merges in their
+// order, so the results equal those of the separate fold and merge launches
+// bit for bit: fold_states itself up to 16 states (all loads of a piece in
+// flight at once), fold_states_lean beyond (the same merges with fewer
+// registers; at most 256 chunks and 256 partitions).
+__device__ __forceinline__ void merge_tail(const EncodeArgs& a, int b, int h, int c, int* sflag) {
+  if (a.fz.cnt == nullptr) return;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int D = a.D, D4 = D >> 2;
+  const int64_t rows = (int64_t)a.B * a.H * a.M;
+  const int64_t sstride = rows * D;
+  const int64_t p0 = bh * a.M * D4, p1 = p0 + (int64_t)a.M * D4;   // (row, 4-column piece) of (b, h)
+  const int slot = a.tab.slot[c];
+  if (slot >= 0) {
+    // the partition r holding chunk c: the last r with pchunk[r] <= c
+    int r = 0;
+    for (int lo = 0, hi = a.R - 1; lo <= hi;) {
+      const int mid = (lo + hi) >> 1;
+      if (a.fz.pchunk[mid] <= c) { r = mid; lo = mid + 1; } else { hi = mid - 1; }
+    }
+    const int c0 = a.fz.pchunk[r], n = a.fz.pchunk[r + 1] - c0;
+    uint32_t* pcnt = a.fz.cnt + (int64_t)a.B * a.H + bh * a.R + r;
+    if (!publish_and_count(pcnt, (uint32_t)n, sflag)) return;
+    const int s0 = a.tab.slot[c0];
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+      const int64_t row = p / D4, off = 4 * p;
+      const MState st = n <= kFoldBatch ? fold_states(a.ws_O, a.ws_L, s0, n, rows, row, off, sstride)
+                                        : fold_states_lean(a.ws_O, a.ws_L, s0, n, rows, row, off, sstride);
+      store_state(st, a.O_part, a.L_part, nullptr, r, rows, row, off, sstride, D);
+    }
+    if (threadIdx.x == 0) *pcnt = 0;
+  }
+  if (!publish_and_count(a.fz.cnt + bh, (uint32_t)a.fz.target, sflag)) return;
+  // partitions without a token: the empty state (0, -inf)
+  for (int r = 0; r < a.R; ++r) {
+    if (a.fz.pchunk[r + 1] != a.fz.pchunk[r]) continue;
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+      const int64_t row = p / D4, off = 4 * p;
+      store_state(mstate_empty(), a.O_part, a.L_part, nullptr, r, rows, row, off, sstride, D);
+    }
+  }
+  // ... read back below by other threads of this workgroup (same CU):
+  // complete the stores, then meet
+  wait_vm<0>();
+  __syncthreads();
+  // the R partition states -> Z, L
+  for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+    const int64_t row = p / D4, off = 4 * p;
+    const MState st = a.R <= kFoldBatch ? fold_states(a.O_part, a.L_part, 0, a.R, rows, row, off, sstride)
+                                        : fold_states_lean(a.O_part, a.L_part, 0, a.R, rows, row, off, sstride);
+    store_state(st, a.fz.Z, a.fz.L, a.fz.Zb, 0, rows, row, off, sstride, D);
+  }
+  if (threadIdx.x == 0) a.fz.cnt[bh] = 0;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 matrix-core encoder.  One workgroup = one (batch, head, chunk) and all
 // M = 32*NW latent rows, so each K/V byte is read from HBM exactly once.
@@ -426,6 +514,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
 
   float l_tot = RS ? lacc[0] : l_run + __shfl_xor(l_run, 32, 64);
   finish_chunk<D, NW, G>(smem, a, grp, wave, lane, o, m_run, l_tot, b, h, c);
+  merge_tail(a, b, h, c, reinterpret_cast<int*>(smem));
 }
 
 // ---------------------------------------------------------------------------
@@ -762,6 +851,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   }
 
   finish_chunk<D, NW, G>(smem, a, grp, wave, lane, o, m_run, lsum, b, h, c);
+  merge_tail(a, b, h, c, reinterpret_cast<int*>(smem));
 }
 
 bool encode_mfma_supported(int M, int D) {
@@ -1099,21 +1189,10 @@ __device__ __forceinline__ float ldv<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float ldv<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
+// One latent row m of (b, h) over chunk c, on one wave.
 template <typename TIn>
-__global__ __launch_bounds__(256) void encode_generic_kernel(const EncodeArgs a) {
+__device__ __forceinline__ void encode_generic_row(const EncodeArgs& a, int b, int h, int c, int m, int lane) {
   constexpr int MAXDL = 4;  // D <= 256
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nch = a.tab.nchunks;
-  const int mgroups = (a.M + 3) / 4;
-  int bid = blockIdx.x;
-  const int c = bid % nch;
-  bid /= nch;
-  const int mg = bid % mgroups;
-  bid /= mgroups;
-  const int h = bid % a.H;
-  const int b = bid / a.H;
-  const int m = 4 * mg + wave;
-  if (m >= a.M) return;
   const int D = a.D;
   const int t_begin = a.tab.bnd[c], t_end = a.tab.bnd[c + 1];
   const int64_t bh = (int64_t)b * a.H + h;
@@ -1179,6 +1258,22 @@ __global__ __launch_bounds__(256) void encode_generic_kernel(const EncodeArgs a)
     if (d < D) Ob[d] = acc[j] * inv;
   }
   if (lane == 0) *Lb = empty ? kNegInf : (m_run * a.scale + __logf(l_run));
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void encode_generic_kernel(const EncodeArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nch = a.tab.nchunks;
+  const int mgroups = (a.M + 3) / 4;
+  int bid = blockIdx.x;
+  const int c = bid % nch;
+  bid /= nch;
+  const int mg = bid % mgroups;
+  bid /= mgroups;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int m = 4 * mg + wave;
+  if (m < a.M) encode_generic_row<TIn>(a, b, h, c, m, lane);
 }
 
 hipError_t launch_encode_generic(const EncodeArgs& a, bool bf16, hipStream_t s) {

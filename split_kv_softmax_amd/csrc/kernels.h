@@ -19,6 +19,27 @@ struct ChunkTable {
   int16_t slot[kMaxChunks];
 };
 
+// Fused merge of an encoder launch.  Partition r owns chunks [pchunk[r],
+// pchunk[r+1]) of the chunk table.  A workgroup whose chunk is a whole
+// partition adds one to the slice counter cnt[b*H + h] once its state is
+// stored; one whose partition is split adds one to the partition counter
+// cnt[B*H + (b*H + h)*R + r], and the workgroup that completes that count
+// folds the partition's chunk states into O_part / L_part and then adds one
+// to the slice counter.  The workgroup that brings the slice counter to
+// `target` (the nonempty partitions) writes the empty state of empty
+// partitions and merges the R partition states into Z / L (and the bfloat16
+// copy Zb when set).  Each completing workgroup puts its counter back to 0.
+// cnt == null: no merge.
+constexpr int kMaxFuseParts = 256;
+struct FuseTable {
+  uint32_t* cnt;   // [B*H*(R+1)], 0 on entry
+  int target;
+  float* Z;        // [B,H,M,D]
+  float* L;        // [B,H,M]
+  uint16_t* Zb;    // nullable [B,H,M,D]
+  int16_t pchunk[kMaxFuseParts + 1];
+};
+
 struct EncodeArgs {
   const void* Q;
   const void* K;
@@ -36,6 +57,7 @@ struct EncodeArgs {
   float scale_log2;   // s * log2(e)
   ChunkTable tab;
   const int32_t* order;   // launch order of the (b, h, chunk) blocks, heaviest first, or null
+  FuseTable fz;
 };
 
 // Group g folds input states [in_begin[g], in_begin[g+1]) of `in` into output

@@ -35,6 +35,8 @@ def lib():
     L.flare_encode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64, i32]
     L.flare_encode_workspace_size.restype = sz
     L.lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp, vp]
+    L.flare_encode_merge.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp,
+                                     vp, vp, vp, vp, sz, vp]
     L.flare_decode.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, f32, vp, vp]
     L.flare_encode_bwd.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp,
                                    vp, vp, vp, vp, i32, vp, sz, vp]
@@ -55,7 +57,7 @@ def offs(*v):
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"flare_encode", "lse_merge", "flare_decode", "flare_encode_bwd"} <= set(names)
+    assert {"flare_encode", "flare_encode_merge", "lse_merge", "flare_decode", "flare_encode_bwd"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert b"gfx950" in lib.flare_version()
@@ -128,3 +130,24 @@ def test_decode_backward_validates(lib):
     assert lib.flare_decode_bwd(1, 1, 2, 1000, 64, 64, FAKE, FAKE, 0, FAKE, None, 0.1, FAKE, FAKE, FAKE, FAKE,
                                 None, FAKE, n - 1, None) == EWS
     assert lib.flare_decode_bwd_workspace_size(1, 1, 2, 1000, 300, 64, 0) == 0     # invalid shape -> 0
+
+
+def _encm(lib, o, Z=FAKE, L=FAKE, Zb=None, cnt=FAKE, N=1024, ws=None, nbytes=0):
+    return lib.flare_encode_merge(1, 1, 1, N, 64, 64, FAKE, 0, FAKE, FAKE, len(o) - 1, o, None, 0.125, FAKE, FAKE,
+                                  Z, L, Zb, cnt, ws, nbytes, None)
+
+
+def test_encode_merge_validates(lib):
+    """The merged call checks what flare_encode checks, plus its merge outputs and counters."""
+    assert _encm(lib, offs(0, 600, 500, 1024)) == EINVAL            # offsets as flare_encode
+    assert b"disjoint" in lib.flare_last_error()
+    assert _encm(lib, offs(0, 1024), Z=None) == EINVAL
+    assert _encm(lib, offs(0, 1024), L=None) == EINVAL
+    assert _encm(lib, offs(0, 1024), cnt=None) == EINVAL
+    assert b"counters" in lib.flare_last_error()
+    assert _encm(lib, offs(0, 1024), Z=ctypes.c_void_p(0x7f0000000008)) == EINVAL      # Z 16-byte aligned
+    assert _encm(lib, offs(0, 1024), Zb=ctypes.c_void_p(0x7f0000000004)) == EINVAL     # Z_bf16 8-byte aligned
+    assert _encm(lib, offs(0, 1024), cnt=ctypes.c_void_p(0x7f0000000002)) == EINVAL    # counters 4-byte aligned
+    o = offs(0, 40000, 80000)
+    n = lib.flare_encode_workspace_size(1, 1, 1, 80000, 64, 64, 2, o, 0)
+    assert n > 0 and _encm(lib, o, N=80000, ws=FAKE, nbytes=n - 1) == EWS               # same workspace as encode
