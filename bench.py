@@ -1,7 +1,7 @@
 """Throughput of the split-KV / FLARE softmax hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cpu-seconds S]
-                    [--backward] [--fused] [--graph]
+                    [--backward] [--shared] [--fused] [--graph]
 
 A step is one pass of the whole path over one batch of synthetic input that
 already sits in HBM.  For the default workload (FLARE++, B=1, H=16, N=262144,
@@ -106,11 +106,14 @@ class FlareppStep(Step):
     """The FLARE++ forward chain with preallocated outputs; fused: each encoder
     and its merge as one call (flare_encode_merge)."""
 
-    def __init__(self, w: W.Workload, x, fused=False):
+    def __init__(self, w: W.Workload, x, fused=False, shared=False):
         self.w, self.x = w, x
+        self.shared = shared
         B, H, N, M, D, R = w.B, w.H, w.N, w.M, w.D, w.R
         dev = x["K"].device
         f32 = dict(dtype=torch.float32, device=dev)
+        # shared projections: the query-synthesis encoder reads K and V themselves
+        Kt, Vt = (x["K"], x["V"]) if shared else (x["Kt"], x["Vt"])
         self.O1 = torch.empty((R, B, H, M, D), **f32)
         self.L1 = torch.empty((R, B, H, M), **f32)
         self.QX = torch.empty((B, H, M, D), **f32)
@@ -124,14 +127,14 @@ class FlareppStep(Step):
         dec = ("decode", lambda: fl.decode(x["K"], self.QXb, self.Z, w.scale, None, self.Y))
         if fused:
             self._phases([
-                ("encode_merge1", lambda: fl.encode_merge(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, True,
+                ("encode_merge1", lambda: fl.encode_merge(x["Qt"], Kt, Vt, w.offsets, None, w.scale, True,
                                                           self.O1, self.L1, self.QX, self.QXL, self.QXb)),
                 ("encode_merge2", lambda: fl.encode_merge(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, False,
                                                           self.O2, self.L2, self.Z, self.L)),
                 dec])
         else:
             self._phases([
-                ("encode1", lambda: fl.encode(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.O1, self.L1)),
+                ("encode1", lambda: fl.encode(x["Qt"], Kt, Vt, w.offsets, None, w.scale, self.O1, self.L1)),
                 ("merge1", lambda: fl.lse_merge(self.O1, self.L1, Z=self.QX, L=self.QXL, Z_bf16=self.QXb)),
                 ("encode2", lambda: fl.encode(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, self.O2, self.L2)),
                 ("merge2", lambda: fl.lse_merge(self.O2, self.L2, Z=self.Z, L=self.L)),
@@ -195,7 +198,7 @@ def _host(t, b, h):
     return t[h:h + 1].cpu() if t.dim() == 3 else t[b:b + 1, h:h + 1].cpu()
 
 
-def cpu_baseline(w: W.Workload, x, budget_s: float):
+def cpu_baseline(w: W.Workload, x, budget_s: float, shared: bool = False):
     """Time the float64 oracle on whole (batch, head) slices of the same inputs, full N each,
     until about ``budget_s`` seconds of CPU work are done; tokens/s = sliced tokens / wall."""
     from oracle import flare_ref as ref
@@ -206,7 +209,8 @@ def cpu_baseline(w: W.Workload, x, budget_s: float):
         mk = x["mask"][b:b + 1].cpu() if "mask" in x else None
         t0 = time.perf_counter()
         if w.kind == "flarepp":
-            ref.flarepp_ref(xs["Qt"], xs["Kt"], xs["Vt"], xs["K"], xs["V"], w.offsets, w.scale)
+            kt, vt = (xs["K"], xs["V"]) if shared else (xs["Kt"], xs["Vt"])
+            ref.flarepp_ref(xs["Qt"], kt, vt, xs["K"], xs["V"], w.offsets, w.scale)
         elif w.kind == "flare":
             e = ref.encode_ref(xs["Q"], xs["K"], xs["V"], w.offsets, None, w.scale)
             ref.decode_ref(xs["K"], xs["Q"], e["Z"], w.scale)
@@ -234,10 +238,13 @@ def roofline_of(w: W.Workload, x, step, ph):
     rows = w.B * w.H * w.N
     if w.kind == "flarepp" and "encode2_bwd" in ph:
         # physical-value encoder backward: K, V read, dV written, dK read and written (it adds into the
-        # decoder's key gradient); query-synthesis encoder backward: Kt, Vt read, dKt, dVt written
+        # decoder's key gradient); query-synthesis encoder backward: Kt, Vt read, dKt, dVt written, or
+        # with shared projections K, V read and dK, dV read and written (it adds into both)
         ms = 0.5 * (ph["encode2_bwd"] + ph["encode1_bwd"])
-        return ms, (5 + 4) * rows * row // 2, ("flare_encode_bwd call (row term, key/value-gradient kernel with "
-                                                "fused query gradient, reduce); both encoder backwards averaged")
+        enc1_rows = 6 if getattr(step, "shared", False) else 4
+        return ms, (5 + enc1_rows) * rows * row // 2, ("flare_encode_bwd call (row term, key/value-gradient kernel "
+                                                       "with fused query gradient, reduce); both encoder backwards "
+                                                       "averaged")
     if w.kind == "flarepp" and "encode_merge1" in ph:
         ms = 0.5 * (ph["encode_merge1"] + ph["encode_merge2"])
         return ms, 2 * rows * row, ("encode_ilv_kernel with the merge inside (flare_encode_merge, one launch; "
@@ -280,8 +287,8 @@ class FlareppTrainStep(FlareppStep):
     """FLARE++ forward chain followed by its backward chain (decoder, physical-value
     encoder, query-synthesis encoder) with preallocated gradients."""
 
-    def __init__(self, w: W.Workload, x, fused=False):
-        super().__init__(w, x, fused)
+    def __init__(self, w: W.Workload, x, fused=False, shared=False):
+        super().__init__(w, x, fused, shared)
         dev = x["K"].device
         B, H, M, D = w.B, w.H, w.M, w.D
         f32 = dict(dtype=torch.float32, device=dev)
@@ -301,8 +308,11 @@ class FlareppTrainStep(FlareppStep):
             ("encode2_bwd", lambda: fl.encode_bwd(self.QXb, x["K"], x["V"], w.offsets, None, w.scale, self.Z, self.L,
                                                   self.dZ2c, dQ=self.dQX, dK=self.dK, dV=self.dV, dQ_cast=self.dQXc,
                                                   flags=fl.ACCUMULATE_DQ | fl.ACCUMULATE_DK)),
-            ("encode1_bwd", lambda: fl.encode_bwd(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.QX,
-                                                  self.QXL, self.dQXc, dQ=self.dQt, dK=self.dKt, dV=self.dVt))])
+            ("encode1_bwd", (lambda: fl.encode_bwd(x["Qt"], x["K"], x["V"], w.offsets, None, w.scale, self.QX,
+                                                   self.QXL, self.dQXc, dQ=self.dQt, dK=self.dK, dV=self.dV,
+                                                   flags=fl.ACCUMULATE_DK | fl.ACCUMULATE_DV)) if shared else
+             (lambda: fl.encode_bwd(x["Qt"], x["Kt"], x["Vt"], w.offsets, None, w.scale, self.QX,
+                                    self.QXL, self.dQXc, dQ=self.dQt, dK=self.dKt, dV=self.dVt)))])
 
 
 STEPS = {"flarepp": FlareppStep, "flare": FlareStep, "splitkv": EncodeMergeStep, "encode": EncodeMergeStep,
@@ -329,6 +339,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and replay it for the warm-up and timed steps "
                          "(the per-phase pass stays eager)")
+    ap.add_argument("--shared", action="store_true",
+                    help="FLARE++ only: the shared-projection variant (the query-synthesis encoder reads K and V; "
+                         "with --backward its key and value gradients add into dK and dV)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device 3 times "
                          "(the plain copy that scales the HBM byte counters)")
@@ -346,7 +359,13 @@ def main():
     if args.backward and w.kind != "flarepp":
         print("--backward is defined for the FLARE++ workload only", file=sys.stderr)
         sys.exit(2)
-    step = FlareppTrainStep(w, x, args.fused) if args.backward else STEPS[w.kind](w, x, args.fused)
+    if args.shared and w.kind != "flarepp":
+        print("--shared is defined for the FLARE++ workload only", file=sys.stderr)
+        sys.exit(2)
+    if w.kind == "flarepp":
+        step = (FlareppTrainStep if args.backward else FlareppStep)(w, x, args.fused, args.shared)
+    else:
+        step = STEPS[w.kind](w, x, args.fused)
     run = lambda: step(timed_phases=False)  # noqa: E731
     if args.graph:
         # one eager step on a side stream sizes the library's cached workspace
@@ -388,11 +407,12 @@ def main():
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     tokens = w.B * w.N * w.H
     kvb = 2 if w.dtype == "bf16" else 4
-    is_main = w.name == W.FLAREPP.name and not args.backward
+    is_main = w.name == W.FLAREPP.name and not args.backward and not args.shared
 
     line = {
         "metric": "FLARE encode+decode tokens/sec (B*N*H) at N=256K; % of HBM/MFMA roofline" if is_main
-        else ("FLARE++ forward+backward tokens/sec (B*N*H)" if args.backward else f"{w.kind} tokens/sec (B*N*H)"),
+        else (("FLARE++ forward+backward tokens/sec (B*N*H)" if args.backward else f"{w.kind} tokens/sec (B*N*H)")
+              + (", shared projections" if args.shared else "")),
         "value": tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -407,6 +427,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "M": w.M, "D": w.D, "R": w.R,
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU",
                    "encode_merge": "one call" if args.fused else "two calls",
+                   **({"projections": "shared"} if args.shared else {}),
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if is_main else None,
@@ -424,7 +445,7 @@ def main():
         line["config"]["valid_fraction"] = float(x["mask"].float().mean().item())
     line["copy_reference"] = copy_reference()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, args.shared)
     print(json.dumps(line), flush=True)
     if args.calibrate_copy:
         del x, step

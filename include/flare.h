@@ -179,7 +179,8 @@ size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, i
  *     dQ[m,:] = scale sum_n dS[m,n] K[n,:]  summed over all partitions
  * dQ: [B,H,M,D] float, one slice per batch even when Q is replicated (the sum
  * over the batch is the caller's).  dK, dV: [B,H,N,D] in dtype; rows of masked
- * tokens are written as 0.  Rows with L = -inf get zero gradients.
+ * tokens are written as 0 (kept as they were when accumulating).  Rows with L = -inf
+ * get zero gradients.
  * dQ_cast (nullable): dQ also written in dtype (the dZ of the encoder that produced Q, in
  * the FLARE++ chain).  flags: FLARE_BWD_ACCUMULATE_* below, or 0.
  * Offsets are validated as in flare_encode; workspace must hold
@@ -197,9 +198,14 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
 
 /* flags of flare_encode_bwd (bitwise or).  The FLARE++ backward paragraph adds the
  * decoder's contributions to the encoder's: with these the encoder backward adds into
- * gradients that a preceding flare_decode_bwd wrote. */
+ * gradients that a preceding flare_decode_bwd (or flare_encode_bwd) wrote.  With the
+ * projections of the query-synthesis encoder tied to K and V (the shared-projection
+ * variant of [FLARE++], paragraph on the cost of the extra projections), that encoder's
+ * key and value gradients add into those of the physical-value encoder.  Accumulating
+ * calls leave the rows of masked tokens as they were. */
 #define FLARE_BWD_ACCUMULATE_DQ 1   /* dQ += (instead of dQ =) */
-#define FLARE_BWD_ACCUMULATE_DK 2   /* dK += (instead of dK =); dV is always written */
+#define FLARE_BWD_ACCUMULATE_DK 2   /* dK += (instead of dK =) */
+#define FLARE_BWD_ACCUMULATE_DV 4   /* dV += (instead of dV =) */
 
 /* Bytes of device workspace flare_decode_bwd needs (masked != 0 when a token mask
  * will be passed). */

@@ -401,6 +401,18 @@ def decode_bwd_ref(Xq, Klat, Z, scale: float, dY, token_mask=None,
     return out
 
 
+def flarepp_shared_bwd_ref(Qt, K, V, offsets, scale: float, dY, round_qx_bf16: bool = False,
+                           slices: Optional[List[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
+    """Gradients of <dY, Y> for the shared-projection variant of FLARE++ ("FLARE++",
+    paragraph on the cost of the two extra projections: the query-synthesis
+    encoder's keys and values tied to K and V).  K and V then enter all three
+    attention calls, so their gradients are the sums of the three calls'
+    contributions: dK = dK_dec + dK_enc2 + dK_enc1, dV = dV_enc2 + dV_enc1."""
+    g = flarepp_bwd_ref(Qt, K, V, K, V, offsets, scale, dY, round_qx_bf16=round_qx_bf16, slices=slices)
+    return {"dQt": g["dQt"], "dK": g["dK"] + g["dKt"], "dV": g["dV"] + g["dVt"], "dQX": g["dQX"],
+            "forward": g["forward"]}
+
+
 def flarepp_bwd_ref(Qt, Kt, Vt, K, V, offsets, scale: float, dY, round_qx_bf16: bool = False,
                     slices: Optional[List[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
     """Gradients of <dY, Y> for the FLARE++ chain of flarepp_ref.

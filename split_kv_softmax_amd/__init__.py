@@ -23,9 +23,10 @@ import torch  # noqa: F401  (loaded first so the library binds to torch's HIP ru
 
 __all__ = ["FlareError", "encode", "lse_merge", "encode_merge", "decode", "encode_bwd", "decode_bwd", "flare_forward",
            "flarepp_forward", "flarepp_backward", "encode_workspace_size", "encode_bwd_workspace_size",
-           "decode_bwd_workspace_size", "library_path", "scale_for", "ACCUMULATE_DQ", "ACCUMULATE_DK"]
+           "decode_bwd_workspace_size", "library_path", "scale_for", "ACCUMULATE_DQ", "ACCUMULATE_DK",
+           "ACCUMULATE_DV", "encode_merge", "merge_counters"]
 
-ACCUMULATE_DQ, ACCUMULATE_DK = 1, 2   # flags of encode_bwd (FLARE_BWD_ACCUMULATE_*)
+ACCUMULATE_DQ, ACCUMULATE_DK, ACCUMULATE_DV = 1, 2, 4   # flags of encode_bwd (FLARE_BWD_ACCUMULATE_*)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libflare.so")
@@ -354,8 +355,9 @@ def encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dQ=None, dK=None, dV=Non
                flags: int = 0):
     """Encoder gradients with the global statistics -> (dQ [B,H,M,D] f32, dK, dV).
 
-    ``flags`` (ACCUMULATE_DQ / ACCUMULATE_DK) add into the given dQ / dK instead of
-    overwriting them; ``dQ_cast`` (a [B,H,M,D] tensor in the input dtype) also receives dQ.
+    ``flags`` (ACCUMULATE_DQ / ACCUMULATE_DK / ACCUMULATE_DV) add into the given dQ / dK / dV
+    instead of overwriting them; ``dQ_cast`` (a [B,H,M,D] tensor in the input dtype) also
+    receives dQ.
     """
     lib = _load()
     _kv_check(K, V, Q)
@@ -466,14 +468,22 @@ def flarepp_backward(fwd, Qt, Kt, Vt, K, V, offsets, dY, scale=None):
     encoder backward with its own (Q(X), L) and that dQ(X) -> dQt, dKt, dVt.
     Q(X) enters the second encoder and the decoder rounded to the input dtype; its
     gradient passes the rounding unchanged.
+
+    Shared projections (Kt is K and Vt is V): the query-synthesis encoder's key and
+    value gradients add into dK and dV, and dKt, dVt are those same tensors.
     """
     QXin = fwd["QX_in"]
+    shared = Kt is K and Vt is V
     dZc = torch.empty_like(fwd["Z"], dtype=K.dtype)
     dK, dQX, _ = decode_bwd(K, QXin, fwd["Z"], scale, dY, dZ_cast=dZc)
     dQXc = torch.empty_like(dQX, dtype=K.dtype)
     _, dK, dV = encode_bwd(QXin, K, V, offsets, None, scale, fwd["Z"], fwd["L"], dZc, dQ=dQX, dK=dK,
                            dQ_cast=dQXc, flags=ACCUMULATE_DQ | ACCUMULATE_DK)
-    dQt, dKt, dVt = encode_bwd(Qt, Kt, Vt, offsets, None, scale, fwd["QX"], fwd["QX_L"], dQXc)
+    if shared:
+        dQt, dKt, dVt = encode_bwd(Qt, K, V, offsets, None, scale, fwd["QX"], fwd["QX_L"], dQXc, dK=dK, dV=dV,
+                                   flags=ACCUMULATE_DK | ACCUMULATE_DV)
+    else:
+        dQt, dKt, dVt = encode_bwd(Qt, Kt, Vt, offsets, None, scale, fwd["QX"], fwd["QX_L"], dQXc)
     return {"dQt": dQt, "dKt": dKt, "dVt": dVt, "dK": dK, "dV": dV, "dQX": dQX}
 
 
@@ -483,6 +493,7 @@ def flarepp_forward(Qt, Kt, Vt, K, V, offsets, scale=None, fused=False):
     The dynamic queries are consumed in the input dtype (the merge writes a
     bfloat16 copy next to the float32 result for bfloat16 inputs).  fused=True
     makes each encode and its merge one call, flare_encode_merge (same results).
+    The shared-projection variant passes K and V as Kt and Vt.
     """
     bf16 = K.dtype == torch.bfloat16
     if fused:

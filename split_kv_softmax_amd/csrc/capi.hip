@@ -561,7 +561,8 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   if (st != FLARE_OK) return st;
   if (!std::isfinite(scale)) return fail(FLARE_EINVAL, "scale must be finite");
   if (q_batch_stride < 0) return fail(FLARE_EINVAL, "q_batch_stride must be >= 0");
-  if (flags & ~(FLARE_BWD_ACCUMULATE_DQ | FLARE_BWD_ACCUMULATE_DK)) return fail(FLARE_EINVAL, "unknown flags");
+  if (flags & ~(FLARE_BWD_ACCUMULATE_DQ | FLARE_BWD_ACCUMULATE_DK | FLARE_BWD_ACCUMULATE_DV))
+    return fail(FLARE_EINVAL, "unknown flags");
   if ((int64_t)B * H == 0) return FLARE_OK;
   if ((int64_t)M > 0 && (!Q || !Z || !L || !dZ || !dQ)) return fail(FLARE_EINVAL, "NULL pointer argument");
   if (N > 0 && (!K || !V || !dK || !dV)) return fail(FLARE_EINVAL, "NULL pointer argument");
@@ -603,6 +604,7 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   a.dQ_cast = dQ_cast;
   a.accumulate_dq = (flags & FLARE_BWD_ACCUMULATE_DQ) != 0;
   a.accumulate_dk = (flags & FLARE_BWD_ACCUMULATE_DK) != 0;
+  a.accumulate_dv = (flags & FLARE_BWD_ACCUMULATE_DV) != 0;
   const bool bf16 = dtype == FLARE_BF16;
   hipError_t e = launch_bwd_rowdot(dZ, bf16, Z, (int64_t)B * H * M, D, reinterpret_cast<float*>(ws), s);
   if (e != hipSuccess) return hip_fail(e, "backward row-term launch");

@@ -92,12 +92,16 @@ __global__ __launch_bounds__(256) void bwd_kv_generic_kernel(const BwdArgs a) {
       }
     }
   }
+  // an accumulating call adds exactly the gradient a writing call stores (the
+  // product is rounded before the add, never contracted into it)
 #pragma unroll
   for (int j = 0; j < MAXDL; ++j) {
     const int d = lane + 64 * j;
     if (d < D) {
-      stg_(dv + d, av[j]);
-      stg_(dk + d, a.scale * ak[j] + (a.accumulate_dk ? ldg_(dk + d) : 0.f));
+#pragma clang fp contract(off)
+      const float gk = a.scale * ak[j];
+      stg_(dv + d, a.accumulate_dv ? av[j] + ldg_(dv + d) : av[j]);
+      stg_(dk + d, a.accumulate_dk ? gk + ldg_(dk + d) : gk);
     }
   }
 }
@@ -151,7 +155,9 @@ __global__ __launch_bounds__(256) void bwd_q_generic_kernel(const BwdArgs a) {
   for (int j = 0; j < MAXDL; ++j) {
     const int d = lane + 64 * j;
     if (d < D) {
-      const float r = a.scale * acc[j] + (a.accumulate_dq ? a.dQ[row * D + d] : 0.f);
+#pragma clang fp contract(off)
+      const float g = a.scale * acc[j];   // rounded before an accumulating add, as when written
+      const float r = a.accumulate_dq ? g + a.dQ[row * D + d] : g;
       a.dQ[row * D + d] = r;
       if (a.dQ_cast) stg_(static_cast<TIn*>(a.dQ_cast) + row * D + d, r);
     }
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swap_bits2(int x) { return ((x & 1) << 1) | (x >> 1); }
 
-template <int D, int M, int NW, int S, bool DQ, bool ACC>
+template <int D, int M, int NW, int S, bool DQ, int ACC>
 __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   constexpr int TILE = 64;
   constexpr int ROWB = 2 * D;          // bytes of one K/V/gradient row
@@ -539,11 +545,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
     const int nrows = t_end - t0 < TILE ? t_end - t0 : TILE;
     const bool whole = nrows == TILE;
     const int64_t tb = (int64_t)t0 * D;
-    // the tile's gradient rows (bytes past the chunk are dropped); with ACC an
-    // empty tile leaves dK as it is (a zero-length range drops every store)
+    // the tile's gradient rows (bytes past the chunk are dropped); an empty tile
+    // leaves an accumulated gradient as it is (a zero-length range drops every store)
     const __amdgpu_buffer_rsrc_t kout =
-        __builtin_amdgcn_make_buffer_rsrc(dKg + tb, 0, (ACC && !bits) ? 0 : nrows * ROWB, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vout = __builtin_amdgcn_make_buffer_rsrc(dVg + tb, 0, nrows * ROWB, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(dKg + tb, 0, ((ACC & 1) && !bits) ? 0 : nrows * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vout =
+        __builtin_amdgcn_make_buffer_rsrc(dVg + tb, 0, ((ACC & 2) && !bits) ? 0 : nrows * ROWB, 0x00020000);
     if (!bits) {
       // no valid token: zero gradient rows, nothing loaded
 #pragma unroll
@@ -636,18 +643,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
         }
       }
       barrier_lds();
-      // ACC: dK += this gradient (another product already wrote its share); the
-      // old rows are read here so the loads overlap phase B.  A separate
-      // instantiation, so that the kernel without them has no register-tracked
-      // load in its loop (before reusing such registers the compiler waits for
-      // every outstanding load, the ring's included).
-      u32x4_t prev[ACC ? CPT / 2 : 1];
-      if constexpr (ACC) {
+      // ACC bit 0: dK += this gradient, bit 1: dV += (another product already
+      // wrote its share); the old rows are read here so the loads overlap phase
+      // B.  Separate instantiations, so that the kernel without them has no
+      // register-tracked load in its loop (before reusing such registers the
+      // compiler waits for every outstanding load, the ring's included).
+      constexpr int NPK = (ACC & 1) ? CPT / 2 : 0, NPV = (ACC & 2) ? CPT / 2 : 0;
+      u32x4_t prev[NPK + NPV > 0 ? NPK + NPV : 1];
 #pragma unroll
-        for (int k = 0; k < CPT / 2; ++k) {   // rows past the chunk read row 0 (in range, unused)
-          const int rk = r0 + RSTEP * k;
-          prev[k] = ld16(dKg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0);
-        }
+      for (int k = 0; k < NPK; ++k) {   // rows past the chunk read row 0 (in range, unused)
+        const int rk = r0 + RSTEP * k;
+        prev[k] = ld16(dKg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0);
+      }
+#pragma unroll
+      for (int k = 0; k < NPV; ++k) {
+        const int rk = r0 + RSTEP * k;
+        prev[NPK + k] = ld16(dVg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0);
       }
       // ---- phase B: this wave's output blocks, staged into the tile's K/V slot ----
       {
@@ -722,22 +733,21 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       // ---- whole rows out: dK from the K slot, dV from the V slot; each thread
       // owns CPT fixed 16-byte chunks (the first half in dK) ----
       {
-        if constexpr (ACC) {
-          // consume the old rows on every path here, so that the compiler's wait for
-          // them sits in this block and no load is left pending into the next tile
+        // consume the old rows on every path here, so that the compiler's wait for
+        // them sits in this block and no load is left pending into the next tile
 #pragma unroll
-          for (int k = 0; k < CPT / 2; ++k) asm volatile("" ::"v"(prev[k]));
-        }
+        for (int k = 0; k < NPK + NPV; ++k) asm volatile("" ::"v"(prev[k]));
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
           // read and add on every row (the staging holds all 64), store only rows in the chunk
           const bool isv = i >= CPT / 2;
           const int k = i % (CPT / 2);
           u32x4_t v = ld16((isv ? vst : kst) + lds0 + RSTEP * ROWB * k);
-          if (ACC && !isv) {
+          if (((ACC & 1) && !isv) || ((ACC & 2) && isv)) {
+            const u32x4_t& pv = prev[isv ? NPK + k : k];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(prev[k][e]), bf16hi(v[e]) + bf16hi(prev[k][e]));
+              v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(pv[e]), bf16hi(v[e]) + bf16hi(pv[e]));
           }
           __builtin_amdgcn_raw_buffer_store_b128(v, isv ? vout : kout, 2 * (off0 + RSTEP * D * k), 0, kCachePolicyNT);
         }
@@ -799,10 +809,12 @@ hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s) {
 template <int D, int M, int NW, int S, bool DQ>
 static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
-  if (a.accumulate_dk)
-    hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
-  else
-    hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ, false>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a);
+  switch ((a.accumulate_dk ? 1 : 0) | (a.accumulate_dv ? 2 : 0)) {
+    case 0: hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ, 0>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ, 1>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ, 2>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a); break;
+    default: hipLaunchKernelGGL((bwd_kv_mfma_kernel<D, M, NW, S, DQ, 3>), dim3((unsigned)grid), dim3(64 * NW), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

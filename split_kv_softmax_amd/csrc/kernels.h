@@ -109,7 +109,8 @@ struct BwdArgs {
   float* ws_dq;                 // [chunks,B,H,M,D] partial query gradients (matrix-core path)
   void* dQ_cast;                // [B,H,M,D] dQ also in the input dtype, or null
   int accumulate_dq;            // dQ += instead of dQ =
-  int accumulate_dk;            // dK += instead of dK =  (dV is always written)
+  int accumulate_dk;            // dK += instead of dK =
+  int accumulate_dv;            // dV += instead of dV =
   int64_t q_bstride;
   int B, H, N, M, D;
   float scale;

@@ -115,3 +115,62 @@ def test_flarepp_backward_chain_small():
     compare_bf16(g["dQX"], r["dQX"], "dQX")
     for k in ("dQt", "dKt", "dVt", "dK", "dV"):
         compare_bf16(g[k], r[k], k)
+
+
+@pytest.mark.parametrize("M,D,masked", [(128, 64, False), (64, 64, True), (256, 128, True), (16, 32, False)])
+def test_encoder_backward_accumulate_dv(M, D, masked):
+    """ACCUMULATE_DK | ACCUMULATE_DV add the gradient to what dK and dV hold (bf16 sums of
+    the same bf16 gradient, so bit for bit); rows of masked tokens keep their old values."""
+    B, H, N = 2, 2, 2600
+    offsets = [0, 900, 900, 2000, 2600]
+    dt = torch.bfloat16 if D >= 64 else torch.float32
+    Q = W.normal((H, M, D), 1410 + M, W.T_Q, D ** -0.5, dt, DEV)
+    K = W.normal((B, H, N, D), 1410 + M, W.T_K, 1.0, dt, DEV)
+    V = W.normal((B, H, N, D), 1410 + M, W.T_V, 1.0, dt, DEV)
+    dZ = W.normal((B, H, M, D), 1410 + M, W.T_DZ, 1.0, dt, DEV)
+    mask = None
+    if masked:
+        g = np.random.default_rng(M + D)
+        m = (g.random((B, N)) > 0.3).astype(np.uint8)
+        m[:, 0] = 1
+        mask = torch.from_numpy(m).to(DEV)
+    scale = fl.scale_for(D)
+    O, Lp = fl.encode(Q, K, V, offsets, mask, scale)
+    Z, L, _ = fl.lse_merge(O, Lp)
+    _, dK0, dV0 = fl.encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ)
+    prevK = torch.randn_like(dK0.float()).to(dt)
+    prevV = torch.randn_like(dV0.float()).to(dt)
+    dK, dV = prevK.clone(), prevV.clone()
+    fl.encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dK=dK, dV=dV, flags=fl.ACCUMULATE_DK | fl.ACCUMULATE_DV)
+    torch.cuda.synchronize()
+    assert torch.equal(dK, (prevK.float() + dK0.float()).to(dt))
+    assert torch.equal(dV, (prevV.float() + dV0.float()).to(dt))
+    if masked:
+        inv = (mask == 0)[:, None, :, None].expand_as(dK)
+        assert torch.equal(dK[inv], prevK[inv]) and torch.equal(dV[inv], prevV[inv])
+    # dV alone
+    dV2 = prevV.clone()
+    _, dK2, _ = fl.encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dV=dV2, flags=fl.ACCUMULATE_DV)
+    torch.cuda.synchronize()
+    assert torch.equal(dV2, dV) and torch.equal(dK2, dK0)
+
+
+def test_flarepp_shared_projection_chain_small():
+    """Shared projections (query-synthesis keys and values tied to K and V): forward and the
+    three-call backward against the oracle's shared variant."""
+    w = W.shrink(W.FLAREPP, 4000, R=4, H=2, ragged=True)
+    x = w.make(DEV)
+    dY = W.normal((1, 2, 4000, 64), 1510, W.T_DZ, 1.0, torch.bfloat16, DEV)
+    K, V = x["K"], x["V"]
+    fwd = fl.flarepp_forward(x["Qt"], K, V, K, V, w.offsets, w.scale)
+    g = fl.flarepp_backward(fwd, x["Qt"], K, V, K, V, w.offsets, dY, w.scale)
+    torch.cuda.synchronize()
+    rf = ref.flarepp_ref(x["Qt"], K, V, K, V, w.offsets, w.scale)
+    compare_bf16(fwd["Z"], rf["Z"], "Z")
+    compare_bf16(fwd["Y"], rf["Y"], "Y")
+    r = ref.flarepp_shared_bwd_ref(x["Qt"], K, V, w.offsets, w.scale, dY, round_qx_bf16=True)
+    compare_bf16(g["dQX"], r["dQX"], "dQX")
+    for k in ("dQt", "dK", "dV"):
+        compare_bf16(g[k], r[k], k)
+    assert g["dKt"] is g["dK"] and g["dVt"] is g["dV"]
+

@@ -466,3 +466,23 @@ def test_flarepp_backward_matches_autograd_through_sdpa_chain():
     (Y * torch.from_numpy(dY)).sum().backward()
     for name, t in (("dQt", tq), ("dKt", tkt), ("dVt", tvt), ("dK", tk), ("dV", tv)):
         np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+
+
+def test_flarepp_shared_projection_backward_matches_autograd():
+    """Shared projections: one K and one V feed the query-synthesis encoder, the
+    physical-value encoder and the decoder; autograd sums the three uses itself."""
+    rng = np.random.default_rng(25)
+    B, H, N, M, D = 1, 2, 40, 4, 8
+    Qt = rng.standard_normal((H, M, D))
+    K, V, dY = (rng.standard_normal((B, H, N, D)) for _ in range(3))
+    s = 1 / math.sqrt(D)
+    g = ref.flarepp_shared_bwd_ref(Qt, K, V, [0, 9, 9, 25, 40], s, dY)
+    tq = torch.tensor(np.broadcast_to(Qt, (B, H, M, D)).copy(), requires_grad=True)
+    tk, tv = (torch.tensor(a, requires_grad=True) for a in (K, V))
+    QX = F.scaled_dot_product_attention(tq, tk, tv, scale=s)
+    Z = F.scaled_dot_product_attention(QX, tk, tv, scale=s)
+    Y = F.scaled_dot_product_attention(tk, QX, Z, scale=s)
+    (Y * torch.from_numpy(dY)).sum().backward()
+    for name, t in (("dQt", tq), ("dK", tk), ("dV", tv)):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+
