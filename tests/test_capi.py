@@ -115,8 +115,11 @@ def test_backward_validates_offsets(lib):
                                 FAKE, FAKE, FAKE, FAKE, None, 0, None, 0, None) == EINVAL
     # unknown flags are rejected before anything else runs
     assert lib.flare_encode_bwd(1, 1, 1, 100, 64, 64, FAKE, 0, FAKE, FAKE, 2, offs(0, 50, 100), None, 0.1, FAKE,
-                                FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, None, 0, None) == EINVAL
+                                FAKE, FAKE, FAKE, FAKE, FAKE, None, 8, None, 0, None) == EINVAL
     assert b"flags" in lib.flare_last_error()
+    # the three accumulate flags pass that check (and stop at the missing workspace)
+    assert lib.flare_encode_bwd(1, 1, 1, 100, 64, 64, FAKE, 0, FAKE, FAKE, 2, offs(0, 50, 100), None, 0.1, FAKE,
+                                FAKE, FAKE, FAKE, FAKE, FAKE, None, 7, None, 0, None) == EWS
 
 
 def test_decode_backward_validates(lib):
