@@ -62,8 +62,8 @@ flare_status check_offsets(int N, int R, const int64_t* off) {
 // ------------------------------------------------------------ work planning
 enum class EncKind { Mfma, Q1, Generic };
 
-EncKind encode_kind(flare_dtype dt, int M, int D) {
-  if (dt == FLARE_BF16 && encode_mfma_supported(M, D)) return EncKind::Mfma;
+EncKind encode_kind(flare_dtype dt, int M, int D, bool masked) {
+  if (dt == FLARE_BF16 && (encode_mfma_supported(M, D) || encode_ilv_used(M, D, masked))) return EncKind::Mfma;
   if (dt == FLARE_BF16 && encode_q1_supported(M, D)) return EncKind::Q1;
   return EncKind::Generic;
 }
@@ -133,7 +133,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 EncodePlan plan_encode(flare_dtype dt, int B, int H, int N, int M, int D, int R, const int64_t* off, bool masked) {
   EncodePlan p;
-  p.kind = encode_kind(dt, M, D);
+  p.kind = encode_kind(dt, M, D, masked);
   int64_t max_part = 0;
   for (int r = 0; r < R; ++r) max_part = std::max<int64_t>(max_part, off[r + 1] - off[r]);
   const int len = chunk_len_for(p.kind, B, H, R, M, D, max_part, masked);

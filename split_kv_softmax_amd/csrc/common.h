@@ -143,9 +143,13 @@ __device__ __forceinline__ void wait_vm() {
 //    (128-byte rows) or on all 16 rows (256-byte rows);
 //  * transposing reads (4 consecutive rows x 4 consecutive chunks per 32
 //    lanes): the 4 rows land in disjoint aligned groups of 4 chunks.
-// D = 64 also serves any other buffer with 128-byte rows.
+// D = 64 also serves any other buffer with 128-byte rows.  D = 16 (32-byte
+// rows of two chunks): rows 8..15 of every 16 swap their chunks, so the 16
+// row reads of a lane group cover the 64 banks once, and 4 consecutive rows
+// (transposing reads) are 128 contiguous bytes.
 template <int D>
 __device__ __forceinline__ int kv_swz(int r) {
+  if constexpr (D == 16) return (r >> 3) & 1;
   return D == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
 }
 
@@ -184,12 +188,13 @@ __device__ __forceinline__ void wait_vm_le(int n) {
 // stronger: loads complete in issue order.
 template <int UNIT, int KMAX>
 __device__ __forceinline__ void wait_units(int k) {
-  static_assert(KMAX <= 8, "table covers k <= 8");
+  static_assert(KMAX <= 16, "table covers k <= 16");
 #define FL_WU(K)                                                   \
   if constexpr (K <= KMAX) {                                       \
     if (k == K) { wait_vm<(UNIT * K < 64 ? UNIT * K : 63)>(); return; } \
   }
   FL_WU(1) FL_WU(2) FL_WU(3) FL_WU(4) FL_WU(5) FL_WU(6) FL_WU(7) FL_WU(8)
+  FL_WU(9) FL_WU(10) FL_WU(11) FL_WU(12) FL_WU(13) FL_WU(14) FL_WU(15) FL_WU(16)
 #undef FL_WU
   wait_vm<0>();
 }

@@ -19,19 +19,29 @@ namespace flare {
 // direct loads into a per-wave ring of S blocks: waves never wait for each
 // other, and S-1 blocks of a wave are in flight while it computes one.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int row_swz(int D, int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+__device__ __forceinline__ int row_swz(int D, int r) {
+  // 16-byte chunk swizzle of token row r: 128-byte rows (D=64) and 256-byte
+  // rows (D=128) permute their chunks; 32-byte rows (D=16) swap their two
+  // chunks on rows 8..15 of every 16, so 16 rows read by 16 lanes cover the 64
+  // banks once
+  return D == 64 ? ((r >> 1) & 7) : D == 16 ? ((r >> 3) & 1) : (r & 15);
+}
 
 template <int NI, int ST, int S>
 __device__ __forceinline__ void wait_block(int later_blocks, int later_stores) {
   // vector-memory ops issued after block j's loads: later_blocks more blocks of
   // NI loads and later_stores blocks of ST stores
+  static_assert(NI * (S - 2 > 0 ? S - 2 : 0) + ST * (S - 1) < 64, "vmcnt range");
+  if constexpr (S > 3) {
+    // deeper rings (1 KB blocks): the general threshold wait
+    wait_vm_le<NI * (S - 2) + ST * (S - 1)>(NI * later_blocks + ST * later_stores);
+    return;
+  }
 #define FL_W(B, T)                                  \
   if (later_blocks == B && later_stores == T) {     \
     wait_vm<(NI * B + ST * T) < 64 ? (NI * B + ST * T) : 63>(); \
     return;                                         \
   }
-  static_assert(S <= 3, "wait table covers S <= 3");
-  static_assert(NI * (S - 2 > 0 ? S - 2 : 0) + ST * (S - 1) < 64, "vmcnt range");
   FL_W(0, 0) FL_W(0, 1) FL_W(0, 2) FL_W(1, 0) FL_W(1, 1) FL_W(1, 2)
 #undef FL_W
   wait_vm<0>();
@@ -41,7 +51,10 @@ template <int D, int MB, int NWV, int S>
 __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs a) {
   constexpr int M = 32 * MB;
   constexpr int KS = D / 16;   // k-steps of the score product
-  constexpr int DB = D / 32;   // 32-row blocks of Y^T
+  // 32-row blocks of Y^T; at head dim 16 one block whose rows 16..31 are
+  // products of repeated head dims, never stored
+  constexpr int DB = D >= 32 ? D / 32 : 1;
+  constexpr int NG = D >= 32 ? 2 : 1;   // 8-dim register groups of a block that hold head dims
   constexpr int MS = M / 16;   // k-steps of the value product
   constexpr int KLD = D + 8;
   constexpr int ZLD = M + 8;
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       for (int db = 0; db < DB; ++db) {
         // Z^T rows permuted so that register group g of lane half hh holds the 8
         // consecutive head dims 32*db + 16*g + 8*hh .. +7
-        const uint16_t* zrow = &Zt[(32 * db + swap23(l32)) * ZLD + 8 * hh];
+        const uint16_t* zrow = &Zt[(32 * db + (D >= 32 ? swap23(l32) : swap23(l32) & 15)) * ZLD + 8 * hh];
         y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)), pk,
                              y[db]);
       }
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         u32x4_t w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -295,18 +308,19 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
 
 bool decode_mfma_supported(int M, int D) {
   // register budget: the M scores and D outputs of 32 tokens per wave
-  if (D == 64) return M == 32 || M == 64 || M == 128 || M == 256;
+  if (D == 64 || D == 16) return M == 32 || M == 64 || M == 128 || M == 256;
   if (D == 128) return M == 32 || M == 64 || M == 128;
   return false;
 }
 
 // waves per workgroup of the matrix-core decode (tokens_per_block is a multiple of 32 * this)
-int decode_waves(int D) { return D == 64 ? 8 : 4; }
+int decode_waves(int D) { return D == 128 ? 4 : 8; }
 
 template <int D, int MB>
 static hipError_t launch_dec_t(const DecodeArgs& a, hipStream_t s) {
-  constexpr int NWV = D == 64 ? 8 : 4;
-  constexpr int S = (D == 64 && MB <= 4) ? 3 : 2;   // LDS: ring + staged latents within 160 KB
+  constexpr int NWV = D == 128 ? 4 : 8;
+  // LDS: ring + staged latents within 160 KB; 1 KB blocks at head dim 16 take a deeper ring
+  constexpr int S = D == 16 ? 6 : (D == 64 && MB <= 4) ? 3 : 2;
   const int64_t nblk = (a.N + a.tokens_per_block - 1) / a.tokens_per_block;
   const int64_t grid = nblk * a.H * a.B;
   hipLaunchKernelGGL((decode_mfma_kernel<D, MB, NWV, S>), dim3((unsigned)grid), dim3(64 * NWV), 0, s, a);
@@ -321,6 +335,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
       case 64: return launch_dec_t<64, 2>(a, s);
       case 128: return launch_dec_t<64, 4>(a, s);
       case 256: return launch_dec_t<64, 8>(a, s);
+    }
+  } else if (a.D == 16) {
+    switch (a.M) {
+      case 32: return launch_dec_t<16, 1>(a, s);
+      case 64: return launch_dec_t<16, 2>(a, s);
+      case 128: return launch_dec_t<16, 4>(a, s);
+      case 256: return launch_dec_t<16, 8>(a, s);
     }
   } else if (a.D == 128) {
     switch (a.M) {

@@ -25,9 +25,10 @@ namespace flare {
 // a workspace slot of a split partition).
 template <int D, int NW, int G>
 __device__ __forceinline__ void finish_chunk(uint8_t* smem, const EncodeArgs& a, int grp, int wave, int lane,
-                                             f32x16_t (&o)[D / 32], float m_run, float l_tot, int b, int h,
-                                             int c) {
-  constexpr int DB = D / 32;
+                                             f32x16_t (&o)[D >= 32 ? D / 32 : 1], float m_run, float l_tot, int b,
+                                             int h, int c) {
+  constexpr int DB = D >= 32 ? D / 32 : 1;
+  constexpr int NQ = D >= 32 ? 4 : 2;   // 4-row groups of a block that hold head dims
   const int l32 = lane & 31, hh = lane >> 5;
   const float c2 = a.scale_log2;
   if constexpr (G > 1) {
@@ -85,7 +86,7 @@ __device__ __forceinline__ void finish_chunk(uint8_t* smem, const EncodeArgs& a,
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       f32x4_t v = {o[db][4 * q] * inv, o[db][4 * q + 1] * inv, o[db][4 * q + 2] * inv, o[db][4 * q + 3] * inv};
       *reinterpret_cast<f32x4_t*>(Ob + (int64_t)m * D + 32 * db + 8 * q + 4 * hh) = v;
     }
@@ -542,20 +543,25 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   constexpr int NB = TILE / 32;            // 32-token blocks of the score product
   constexpr int NK = TILE / 16;            // 16-token k-steps of the value product
   static_assert(TILE == 32 || TILE == 64, "tile of 32 or 64 tokens");
+  static_assert(D == 16 || D == 64, "head dim 16 or 64");
   constexpr int ROWB = 2 * D;              // bytes per row
   constexpr int TB = TILE * ROWB;          // bytes of a K (or V) tile
   constexpr int RING = 2 * S * TB;         // S K slots, then S V slots
   constexpr int NI = TB / 1024;            // 1 KB direct loads per tile and tensor
-  constexpr int NJ = NI / NW;              // ... issued by each wave
+  // ... issued by each wave; a tile of fewer loads than waves (head dim 16)
+  // is loaded by its first NI waves, and the others' waits pass at once
+  constexpr int NJ = NI >= NW ? NI / NW : 1;
   constexpr int KS = D / 16;               // k-steps of the score product
-  constexpr int DB = D / 32;               // 32-row blocks of O^T
-  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  // 32-row blocks of O^T; at head dim 16 one block whose rows 16..31 are
+  // products of repeated head dims, never stored
+  constexpr int DB = D >= 32 ? D / 32 : 1;
+  static_assert(NI >= 1 && (NI % NW == 0 || NI < NW), "loads must split evenly over the waves");
   static_assert(S >= 4 && 2 * NJ * (S - 1) < 64, "ring depth / vmcnt range");
   static_assert(S * TB <= 65536, "slot offsets within a K or V ring are immediate LDS offsets");
-  static_assert(G == 1 || (G * NW * 32 * 64 + 2 * G * NW * 64) * 4 <= G * RING,
-                "the combine buffer reuses the rings");
+  constexpr int COMBINE = G == 1 ? 0 : (G * NW * 32 * 64 + 2 * G * NW * 64) * 4;   // finish_chunk's buffer
+  constexpr int SMEM = G * RING > COMBINE ? G * RING : COMBINE;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[G * RING];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -610,6 +616,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   }
   // K (is_v false) or V rows of local tile u into ring slot `slot`
   auto issue = [&](int u, int slot, bool is_v) {
+    if (NI < NW && wave >= NI) return;   // (wave-uniform)
     const int t0 = t_begin + (grp + G * u) * TILE;
     const int nrows = t_end - t0;
     const uint16_t* base = (is_v ? Vg : Kg) + (int64_t)t0 * D;
@@ -633,7 +640,8 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int n0 = 8 * (lg >> 1) + 4 * q + (li >> 2);
-        const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+        // head dim 16: the lanes of operand rows 16..31 read dims 0..15 again
+        const int d0 = 32 * db + (D >= 32 ? 16 * (lg & 1) : 0) + 4 * (li & 3);
         vaddr[db][q] = ring_lds + S * TB + n0 * ROWB + (((d0 >> 3) ^ kv_swz<D>(n0)) * 16) + (d0 & 7) * 2;
       }
   }
@@ -911,7 +919,7 @@ static hipError_t launch_d64(const EncodeArgs& a, hipStream_t s, bool pipe) {
 bool encode_ilv_used(int M, int D, bool masked) {
   const char* e = getenv("FLARE_ENCODE_ILV");
   if (e && atoi(e) == 0) return false;
-  return D == 64 && (M == 128 || M == 64) && !masked;
+  return (D == 64 || D == 16) && (M == 128 || M == 64) && !masked;
 }
 
 static bool encode_ilv_selected(const EncodeArgs& a) { return encode_ilv_used(a.M, a.D, a.mask_words != nullptr); }
@@ -919,10 +927,17 @@ static bool encode_ilv_selected(const EncodeArgs& a) { return encode_ilv_used(a.
 hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
   if (encode_ilv_selected(a)) {
     const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
-    if (a.M == 128)
+    if (a.D == 16) {
+      // 2 KB tiles: deeper rings keep as many bytes in flight per CU
+      if (a.M == 128)
+        hipLaunchKernelGGL((encode_ilv_kernel<16, 4, 8, 2, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((encode_ilv_kernel<16, 2, 8, 4, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    } else if (a.M == 128) {
       hipLaunchKernelGGL((encode_ilv_kernel<64, 4, 4, 2, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
-    else
+    } else {
       hipLaunchKernelGGL((encode_ilv_kernel<64, 2, 4, 4, 32>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    }
     return hipGetLastError();
   }
   if (a.D == 64) {

@@ -65,9 +65,11 @@ def test_fp32_small_encoder_workload():
     _check_encode(w, x, fp32=True)
 
 
-@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64), (64, 128), (128, 128), (256, 128)])
+@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64), (64, 128), (128, 128), (256, 128),
+                                 (64, 16), (128, 16)])
 @pytest.mark.parametrize("masked", [False, True])
 def test_bf16_encoder_matrix_core(M, D, masked):
+    # head dim 16: the pipelined encoder without a mask, the vector path with one
     w, x = _enc_case(M, D, N=2500, R=5, masked=masked)
     _check_encode(w, x)
 
@@ -148,7 +150,8 @@ def test_fp32_generic_larger():
 
 
 # ------------------------------------------------------------------- decode
-@pytest.mark.parametrize("M,D", [(64, 64), (128, 64), (64, 128), (256, 128)])
+@pytest.mark.parametrize("M,D", [(64, 64), (128, 64), (64, 128), (256, 128), (32, 16), (64, 16), (128, 16),
+                                 (256, 16)])
 def test_decode_matrix_core(M, D):
     B, H, N = 2, 2, 1000
     Xq = W.normal((B, H, N, D), 600 + M, W.T_K, 1.0, torch.bfloat16, DEV)
@@ -209,6 +212,36 @@ def test_flarepp_small():
     compare_bf16(out["Y"], r["Y"], "Y")
 
 
+def test_flarepp_head_dim_16_small():
+    """The FLARE++ chain at head dim 16 (the pages' C = 128, H = 8 backbone), ragged partitions."""
+    w = W.shrink(W.FLAREPP_D16, 6000, R=5, H=3, ragged=True)
+    x = w.make(DEV)
+    out = fl.flarepp_forward(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale)
+    torch.cuda.synchronize()
+    r = ref.flarepp_ref(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale)
+    compare_bf16(out["QX"], r["QX"], "QX")
+    compare_bf16(out["Z"], r["Z"], "Z")
+    compare_L(out["L"], r["L"], "L")
+    compare_bf16(out["Y"], r["Y"], "Y")
+
+
+def test_encoder_head_dim_16_split_partitions_and_one_call():
+    """Head dim 16 with partitions cut into chunks (few slices), and the one-call form bit for bit."""
+    w = W.shrink(W.FLAREPP_D16, 40000, R=2, H=1, ragged=True)
+    x = w.make(DEV)
+    O, Lp, Z, L, Zb = fl.encode_merge(x["Qt"], x["K"], x["V"], w.offsets, None, w.scale, True)
+    O2, Lp2 = fl.encode(x["Qt"], x["K"], x["V"], w.offsets, None, w.scale)
+    Z2, L2, Zb2 = fl.lse_merge(O2, Lp2, want_bf16=True)
+    torch.cuda.synchronize()
+    for a, b, n in ((O, O2, "O_part"), (Lp, Lp2, "L_part"), (Z, Z2, "Z"), (L, L2, "L"), (Zb, Zb2, "Z_bf16")):
+        assert torch.equal(a, b), n
+    e = ref.encode_ref(x["Qt"], x["K"], x["V"], w.offsets, None, w.scale)
+    compare_bf16(O, e["O_part"], "O_part")
+    compare_L(Lp, e["L_part"], "L_part")
+    compare_bf16(Z, e["Z"], "Z")
+    compare_L(L, e["L"], "L")
+
+
 # ------------------------------------------------------- exactness properties
 def test_empty_and_fully_masked_partitions_are_exact():
     w, x = _enc_case(64, 64, N=1200, R=5, masked=True)
@@ -263,7 +296,7 @@ def _spike_inputs(B, H, N, M, D, spikes, device=DEV):
     return (Q.to(torch.bfloat16).to(device), K.to(torch.bfloat16).to(device), V.to(torch.bfloat16).to(device))
 
 
-@pytest.mark.parametrize("M,D", [(64, 64), (128, 64), (256, 128), (1, 128)])
+@pytest.mark.parametrize("M,D", [(64, 64), (128, 64), (256, 128), (1, 128), (64, 16), (128, 16)])
 def test_spike_index_handling_is_bit_exact(M, D):
     B, H = 2, 3
     offs = [0, 300, 500, 500, 924, 1024, 1500]

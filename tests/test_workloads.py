@@ -27,7 +27,7 @@ def test_masked_recipe_has_empty_partition_and_no_empty_batch():
 
 
 def test_workload_shapes_and_offsets():
-    for w in W.ALL:
+    for w in W.ALL + W.EXTRA:
         assert w.offsets[0] == 0 and w.offsets[-1] == w.N
         assert all(a <= b for a, b in zip(w.offsets, w.offsets[1:]))
     s = W.shrink(W.FLAREPP, 3000, R=5, ragged=True)

@@ -190,7 +190,17 @@ MASKED_FWD_BWD = _w(
     masked=True, mask_slot=16384)
 
 ALL = [FLARE_ENCODE_F32_SMALL, FLARE_BLOCK, FLAREPP, SPLITKV_Q1, MASKED_FWD_BWD]
-BY_NAME = {w.name: w for w in ALL}
+
+# Beyond the five: the FLARE++ chain at the head dim of the pages' step-time
+# sweep (a C = 128 backbone with H = 8 heads, so D = 16), at its largest token
+# count (about 10^6, here 2^20) and the latent count of the FLARE++ workload
+# above (the sweep's own M is not stated).
+FLAREPP_D16 = _w(
+    name="flarepp_fwd_bf16_B1_H8_N1048576_M128_D16_R16", wid=6, kind="flarepp", dtype="bf16",
+    B=1, H=8, N=1048576, M=128, D=16, offsets=equal_offsets(1048576, 16), q_std=0.25,
+    q_per_batch=False)
+EXTRA = [FLAREPP_D16]
+BY_NAME = {w.name: w for w in ALL + EXTRA}
 
 
 def shrink(w: Workload, N: int, R: Optional[int] = None, B: Optional[int] = None,
