@@ -928,11 +928,12 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
   if (encode_ilv_selected(a)) {
     const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
     if (a.D == 16) {
-      // 2 KB tiles: deeper rings keep as many bytes in flight per CU
+      // 2 KB tiles; the loop is instruction-bound, and a 4-stage ring measured
+      // faster than 6 or 8 stages (fewer wait cases per round)
       if (a.M == 128)
-        hipLaunchKernelGGL((encode_ilv_kernel<16, 4, 8, 2, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((encode_ilv_kernel<16, 4, 4, 2, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
       else
-        hipLaunchKernelGGL((encode_ilv_kernel<16, 2, 8, 4, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((encode_ilv_kernel<16, 2, 4, 4, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
     } else if (a.M == 128) {
       hipLaunchKernelGGL((encode_ilv_kernel<64, 4, 4, 2, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
     } else {

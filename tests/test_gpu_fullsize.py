@@ -1,4 +1,4 @@
-"""Parity at the five workloads' full sizes, in the launch configuration the benchmark times.
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark times.
 
 The whole path runs on the GPU at full size.  The float64 oracle then
 recomputes a sample of (batch, head) slices one by one from the very same
@@ -99,6 +99,33 @@ def test_full_flarepp_chain_as_benchmarked():
     for h in (0, 11):
         xs = {k: v[:, h:h + 1].cpu() if v.dim() == 4 else v[h:h + 1].cpu() for k, v in x.items()}
         r = ref.flarepp_ref(xs["Qt"], xs["Kt"], xs["Vt"], xs["K"], xs["V"], w.offsets, w.scale)
+        compare_bf16(step.QX[:, h:h + 1], r["QX"], f"QX[h={h}]")
+        compare_bf16(step.O2[:, :, h:h + 1], r["O_part"], f"O_part[h={h}]")
+        compare_L(step.L2[:, :, h:h + 1], r["L_part"], f"L_part[h={h}]")
+        compare_bf16(step.Z[:, h:h + 1], r["Z"], f"Z[h={h}]")
+        compare_L(step.L[:, h:h + 1], r["L"], f"L[h={h}]")
+        compare_bf16(step.Y[:, h:h + 1], r["Y"], f"Y[h={h}]")
+
+
+@pytest.mark.parametrize("fused,shared", [(False, False), (True, True)])
+def test_full_flarepp_head_dim_16(fused, shared):
+    """FLARE++ at head dim 16 (B=1, H=8, N=2^20, M=128, R=16) through the benchmark's step, also with
+    the one-call encoder + merge and the shared projections; two heads against the oracle."""
+    sys.path.insert(0, ROOT)
+    import bench
+    w = W.FLAREPP_D16
+    _say(f"case {w.name} fused={fused} shared={shared}")
+    x = w.make(DEV)
+    step = bench.FlareppStep(w, x, fused, shared)
+    step(timed_phases=False)
+    torch.cuda.synchronize()
+    for name in ("O1", "L1", "QX", "QXL", "O2", "L2", "Z", "L", "Y"):
+        _finite(getattr(step, name), name)
+    assert torch.equal(step.QXb, step.QX.to(torch.bfloat16))
+    for h in (0, 5):
+        xs = {k: v[:, h:h + 1].cpu() if v.dim() == 4 else v[h:h + 1].cpu() for k, v in x.items()}
+        kt, vt = (xs["K"], xs["V"]) if shared else (xs["Kt"], xs["Vt"])
+        r = ref.flarepp_ref(xs["Qt"], kt, vt, xs["K"], xs["V"], w.offsets, w.scale)
         compare_bf16(step.QX[:, h:h + 1], r["QX"], f"QX[h={h}]")
         compare_bf16(step.O2[:, :, h:h + 1], r["O_part"], f"O_part[h={h}]")
         compare_L(step.L2[:, :, h:h + 1], r["L_part"], f"L_part[h={h}]")
