@@ -156,3 +156,41 @@ def test_flarepp_forward_graph_replays_match_eager(fused):
         torch.cuda.synchronize()
         assert torch.equal(other["Y"], expect["Y"])
     assert int(fl.merge_counters(1, torch.device(DEV)).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_flarepp_training_step_graph_replays_match_eager(shared):
+    """Forward and the three-call backward captured in one graph: every replay equals the eager step."""
+    w = W.shrink(W.FLAREPP, 12000, R=4, H=2, ragged=True)
+    x = w.make(DEV)
+    Kt, Vt = (x["K"], x["V"]) if shared else (x["Kt"], x["Vt"])
+    dY = W.normal((1, 2, 12000, 64), 1520, W.T_DZ, 1.0, torch.bfloat16, DEV)
+
+    def step():
+        fwd = fl.flarepp_forward(x["Qt"], Kt, Vt, x["K"], x["V"], w.offsets, w.scale)
+        g = fl.flarepp_backward(fwd, x["Qt"], Kt, Vt, x["K"], x["V"], w.offsets, dY, w.scale)
+        return fwd["Y"], g
+
+    keys = ("dQt", "dKt", "dVt", "dK", "dV", "dQX")
+    Y0, g0 = step()                      # sizes the cached workspaces outside the capture
+    torch.cuda.synchronize()
+    expect = {k: g0[k].clone() for k in keys}
+    expect["Y"] = Y0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        Y, g = step()
+    out = dict(g)
+    out["Y"] = Y
+    for rep in range(3):
+        for k in expect:
+            out[k].zero_()               # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in expect:
+            assert torch.equal(out[k], expect[k]), f"replay {rep}: {k} differs from the eager step"
