@@ -196,7 +196,10 @@ hipError_t launch_decode_bwd_generic(const DecBwdArgs& a, bool bf16, hipStream_t
 // dXq rows leave through the consumed ring slot as whole rows; each token's
 // log2-normaliser and delta go to the workspace for the latent side.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int tok_swz(int D, int r) { return D == 64 ? ((r >> 1) & 7) : (r & 15); }
+// 16-byte chunk swizzle of token row r (32-byte rows at D=16 swap their chunks on rows 8..15 of every 16)
+__device__ __forceinline__ int tok_swz(int D, int r) {
+  return D == 64 ? ((r >> 1) & 7) : D == 16 ? ((r >> 3) & 1) : (r & 15);
+}
 
 template <int NI, int ST, int S>
 __device__ __forceinline__ void wait_blk(int later_blocks, int later_stores) {
@@ -220,7 +223,10 @@ template <int D, int MB, int NWV, int S>
 __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArgs a) {
   constexpr int M = 32 * MB;
   constexpr int KS = D / 16;   // k-steps over the head dim
-  constexpr int DB = D / 32;   // 32-row blocks of dXq^T
+  // 32-row blocks of dXq^T; at head dim 16 one block whose rows 16..31 are
+  // products of repeated head dims, never stored
+  constexpr int DB = D >= 32 ? D / 32 : 1;
+  constexpr int NG = D >= 32 ? 2 : 1;   // 8-dim register groups of a block that hold head dims
   constexpr int MS = M / 16;   // k-steps over the latents
   constexpr int BLK = 32;
   constexpr int ROWB = 2 * D;
@@ -311,7 +317,8 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int row = 8 * (lg >> 1) + 4 * q + (li >> 2);
-      const int col = 32 * db + 16 * (lg & 1) + 4 * swap_bits2(li & 3);
+      // head dim 16: the lanes of operand rows 16..31 read dims 0..15 again
+      const int col = 32 * db + (D >= 32 ? 16 * (lg & 1) : 0) + 4 * swap_bits2(li & 3);
       toff[q][db] = lat(row, col >> 3) + (col & 7) * 2;
     }
   for (int j0 = 0; j0 < nb; j0 += S)
@@ -437,7 +444,7 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < NG; ++g) {
         u32x4_t w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -485,11 +492,17 @@ __global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs
   constexpr int TB = TILE * ROWB;
   constexpr int STAGE = 2 * TB + 1024;       // Xq tile, dY tile, statistics (512 B used)
   constexpr int NI = TB / 1024;
+  // 1 KB loads per wave and tensor; a tile of fewer loads than waves (head dim
+  // 16) is loaded by its first NI waves
+  constexpr int NJ = NI >= NW ? NI / NW : 1;
   constexpr int KS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int OPS = 2 * NI / NW + 1;       // loads per wave and tile (the statistics share one)
+  // 32-row blocks of the products' outputs; at head dim 16 one block whose
+  // rows 16..31 are products of repeated head dims, never stored
+  constexpr int DB = D >= 32 ? D / 32 : 1;
+  constexpr int NQ = D >= 32 ? 4 : 2;        // 4-row groups of a block that hold head dims
+  constexpr int OPS = 2 * NJ + 1;            // loads per loading wave and tile (the statistics share one)
   constexpr int SPW = 32 / NW;               // 16-byte statistics pieces per wave
-  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  static_assert(NI % NW == 0 || NI < NW, "loads must split evenly over the waves");
   static_assert(OPS * (S - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
 
@@ -539,12 +552,14 @@ __global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs
     if (mw) bits &= mask_tile_bits(mw, t0);
     return bits;
   };
+  const bool loads = NI >= NW || wave < NI;   // (wave-uniform)
   auto issue = [&](int u) {
     const int t0 = t_begin + u * TILE;
     const int nrows = t_end - t0;
     const uint32_t kst = lds_addr(smem) + (u % S) * STAGE;
 #pragma unroll
-    for (int j = 0; j < NI / NW; ++j) {
+    for (int j = 0; j < NJ; ++j) {
+      if (!loads) break;
       const int ii = wave + NW * j;
       const int byte = ii * 1024 + lane * 16;
       const int r = byte / ROWB, pc = (byte % ROWB) / 16;
@@ -582,7 +597,11 @@ __global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs
     int later = 0;
 #pragma unroll
     for (int k = 1; k < S - 1; ++k) later += ring[k] != 0ull;
-    wait_tiles<OPS, S>(later);
+    // a wave that loads no tile rows issues the statistics piece alone
+    if (loads)
+      wait_tiles<OPS, S>(later);
+    else
+      wait_tiles<1, S>(later);
     barrier_lds();
     ring[S - 1] = tile_bits(t + S - 1);
     if (ring[S - 1]) issue(t + S - 1);
@@ -655,7 +674,8 @@ __global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs
       // dZ^T += dY^T A^T and dKlat^T += Xq^T dT^T through transposing reads of the tiles
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+        // head dim 16: the lanes of operand rows 16..31 read dims 0..15 again
+        const int d0 = 32 * db + (D >= 32 ? 16 * (lg & 1) : 0) + 4 * (li & 3);
         const int chl = d0 >> 3, half = (d0 & 7) * 2;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -682,7 +702,7 @@ __global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int64_t off = (int64_t)m * D + 32 * db + 8 * q + 4 * hh;
       *reinterpret_cast<f32x4_t*>(W + off) = f32x4_t{accz[db][4 * q], accz[db][4 * q + 1], accz[db][4 * q + 2],
                                                      accz[db][4 * q + 3]};
@@ -710,16 +730,17 @@ __global__ __launch_bounds__(256) void dbwd_reduce_kernel(const float* __restric
 }
 
 bool decode_bwd_mfma_supported(int M, int D) {
-  return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128);
+  return (D == 16 || D == 64 || D == 128) && (M == 32 || M == 64 || M == 128);
 }
 
 // token-side waves per workgroup: at D=64 eight waves with 2-stage rings fill the
-// LDS (128 KB of rings, up to 32 KB of latents), two waves per SIMD
-int decode_bwd_waves(int D) { return D == 64 ? 8 : 2; }
+// LDS (128 KB of rings, up to 32 KB of latents), two waves per SIMD; D=16 the same
+// with quarter-size rings
+int decode_bwd_waves(int D) { return D == 128 ? 2 : 8; }
 
 template <int D, int MB>
 static hipError_t launch_dbwd_t(const DecBwdArgs& a, hipStream_t s) {
-  constexpr int NWV = D == 64 ? 8 : 2;
+  constexpr int NWV = D == 128 ? 2 : 8;
   constexpr int S = 2;
   const int64_t nblk = (a.N + a.tokens_per_block - 1) / a.tokens_per_block;
   hipLaunchKernelGGL((dbwd_tok_mfma_kernel<D, MB, NWV, S>), dim3((unsigned)(nblk * a.H * a.B)), dim3(64 * NWV), 0,
@@ -740,6 +761,12 @@ hipError_t launch_decode_bwd_mfma(const DecBwdArgs& a, hipStream_t s) {
       case 32: return launch_dbwd_t<64, 1>(a, s);
       case 64: return launch_dbwd_t<64, 2>(a, s);
       case 128: return launch_dbwd_t<64, 4>(a, s);
+    }
+  } else if (a.D == 16) {
+    switch (a.M) {
+      case 32: return launch_dbwd_t<16, 1>(a, s);
+      case 64: return launch_dbwd_t<16, 2>(a, s);
+      case 128: return launch_dbwd_t<16, 4>(a, s);
     }
   } else if (a.D == 128) {
     switch (a.M) {

@@ -61,7 +61,8 @@ def test_decode_backward_fp32():
     _check_decode(Xq, Kl, Z, dY, tm, 32 ** -0.5, fp32=True)
 
 
-@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (32, 128), (64, 128), (128, 128), (256, 64)])
+@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (32, 128), (64, 128), (128, 128), (256, 64),
+                                 (32, 16), (64, 16), (128, 16)])
 def test_decode_backward_bf16(M, D):
     Xq, Kl, Z, dY, tm = _decode_case(M, D, 2100)
     _check_decode(Xq, Kl, Z, dY, tm, float(np.float32(1) / np.sqrt(np.float32(D))), with_cast=True)
@@ -70,6 +71,11 @@ def test_decode_backward_bf16(M, D):
 def test_decode_backward_unmasked_per_batch_latents_ragged_tail():
     Xq, Kl, Z, dY, _ = _decode_case(128, 64, 4999, B=1, H=3, masked=False, per_batch=True)
     _check_decode(Xq, Kl, Z, dY, None, 0.125)
+
+
+def test_decode_backward_head_dim_16_unmasked_ragged_tail():
+    Xq, Kl, Z, dY, _ = _decode_case(128, 16, 4999, B=1, H=3, masked=False, per_batch=True)
+    _check_decode(Xq, Kl, Z, dY, None, 0.25)
 
 
 def test_decode_backward_is_deterministic():
