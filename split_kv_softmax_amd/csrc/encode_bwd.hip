@@ -390,9 +390,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   constexpr int NI = TB / 1024;
   constexpr int KS = D / 16;           // contraction steps over the head dim
   constexpr int KM = M / 16;           // contraction steps over the latents
-  constexpr int DB = D / 32;
+  // 32-row head-dim blocks; at head dim 16 one block whose rows 16..31 are
+  // products of repeated head dims, never stored
+  constexpr int DB = D >= 32 ? D / 32 : 1;
+  constexpr int NG = D >= 32 ? 2 : 1;  // 8-dim register groups of a block that hold head dims
   constexpr int MW = M / 32;           // waves with latent rows in phase A
-  constexpr int OPS = 2 * NI / NW;
+  // loads per wave and tile; a 2 KB tile (head dim 16) is one 1 KB piece of K
+  // or of V per wave, waves 0..NI-1 taking K and NI..2NI-1 taking V
+  constexpr bool SPLIT = NI < NW;
+  static_assert(!SPLIT || NW == 2 * NI, "one load per wave");
+  constexpr int OPS = SPLIT ? 1 : 2 * NI / NW;
   constexpr int PDS = M * TILE * 2;    // one bf16 [M][64] buffer
   constexpr int RING = S * STAGE;
   constexpr int LDS_MAIN = RING + 2 * PDS;
@@ -402,9 +409,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   constexpr int NDW = DB >= WPT ? DB / WPT : 1;
   constexpr int NNB = DB >= WPT ? 2 : 2 * DB / WPT;
   constexpr int CPT = 2 * TILE * CPR / (64 * NW);   // copy-out chunks per thread
-  static_assert(CPT % 2 == 0 && CPT * 64 * NW == 2 * TILE * CPR, "copy-out split");
+  // CPT even: each thread owns CPT/2 chunks of dK and as many of dV; CPT = 1
+  // (head dim 16): threads 0..TILE*CPR-1 own one chunk of dK, the others one of dV
+  static_assert((CPT % 2 == 0 || CPT == 1) && CPT * 64 * NW == 2 * TILE * CPR, "copy-out split");
   static_assert((S - 2) * OPS + (S - 1) * CPT < 64, "vmcnt range");
-  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  static_assert(NI % NW == 0 || SPLIT, "loads must split evenly over the waves");
   static_assert(MW <= NW && NW % 2 == 0 && WPT <= 2 * DB, "wave layout");
   static_assert(OPS * (S - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
@@ -465,7 +474,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
-          const int col = 32 * (db0 + j) + 16 * (lg & 1) + 4 * swap_bits2(li & 3);
+          // head dim 16: the lanes of operand rows 16..31 read dims 0..15 again
+          const int col = 32 * (db0 + j) + (D >= 32 ? 16 * (lg & 1) : 0) + 4 * swap_bits2(li & 3);
           part[q] = __builtin_bit_cast(
               u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(src + row * ROWB + col * 2)));
         }
@@ -493,6 +503,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
     const int t0 = t_begin + u * TILE;
     const int nrows = t_end - t0;
     const uint32_t kst = lds_addr(smem) + (u % S) * STAGE;
+    if constexpr (SPLIT) {
+      const int ii = wave % NI;
+      const bool isv = wave >= NI;   // (wave-uniform)
+      const int byte = ii * 1024 + lane * 16;
+      const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+      const int ch = pc ^ kv_swz<D>(r);
+      const int rr = r < nrows ? r : 0;
+      const int64_t off = (int64_t)(t0 + rr) * D + 8 * ch;
+      dma16((isv ? Vg : Kg) + off, kst + (isv ? TB : 0) + ii * 1024);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NI / NW; ++j) {
       const int ii = wave + NW * j;
@@ -506,7 +527,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
     }
   };
   // staged gradient rows: 16-byte chunk ch of row n sits at ch ^ out_swz(n)
-  auto out_swz = [](int n) { return D == 64 ? kv_swz<64>(n) : (n & 15); };
+  auto out_swz = [](int n) { return D == 64 ? kv_swz<64>(n) : D == 16 ? kv_swz<16>(n) : (n & 15); };
 
   f32x16_t dq[DQ ? DB : 1];
 #pragma unroll
@@ -522,8 +543,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   // copy-out chunks of this thread: chunk i is 16-byte column ch0 of row r0 + RSTEP*(i % (CPT/2)) of
   // dK (first half) or dV; RSTEP keeps the staging swizzle of r0
   constexpr int RSTEP = 64 * NW / CPR;
-  static_assert(RSTEP % 16 == 0, "copy-out rows share one swizzle");
-  const int r0 = tid / CPR, ch0 = tid % CPR;
+  static_assert(CPT == 1 || RSTEP % 16 == 0, "copy-out rows share one swizzle");
+  const int fo = CPT == 1 ? tid % (TILE * CPR) : tid;   // chunk within its tensor
+  const bool ov = CPT == 1 && tid >= TILE * CPR;        // CPT = 1: this thread's chunk is of dV
+  const int r0 = fo / CPR, ch0 = fo % CPR;
   const int lds0 = r0 * ROWB + (ch0 ^ out_swz(r0)) * 16;
   const int off0 = r0 * D + 8 * ch0;
   const int swk = kv_swz<D>(swap23(l32));   // rows 32*b2 + swap23(l32)
@@ -555,8 +578,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       // no valid token: zero gradient rows, nothing loaded
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const bool isv = i >= CPT / 2;
-        const int k = i % (CPT / 2);
+        const bool isv = CPT == 1 ? ov : i >= CPT / 2;
+        const int k = CPT == 1 ? 0 : i % (CPT / 2 > 0 ? CPT / 2 : 1);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0, 0, 0, 0}, isv ? vout : kout, 2 * (off0 + RSTEP * D * k), 0,
                                                kCachePolicyNT);
       }
@@ -623,7 +646,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
             // dQ^T += K^T dS^T over this block's 32 tokens
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-              const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+              const int d0 = 32 * db + (D >= 32 ? 16 * (lg & 1) : 0) + 4 * (li & 3);
               const int chl = d0 >> 3, half = (d0 & 7) * 2;
 #pragma unroll
               for (int g = 0; g < 2; ++g) {
@@ -648,15 +671,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       // B.  Separate instantiations, so that the kernel without them has no
       // register-tracked load in its loop (before reusing such registers the
       // compiler waits for every outstanding load, the ring's included).
-      constexpr int NPK = (ACC & 1) ? CPT / 2 : 0, NPV = (ACC & 2) ? CPT / 2 : 0;
+      constexpr int HALF = CPT == 1 ? 1 : CPT / 2;   // chunks per tensor of a thread (CPT = 1: of one tensor)
+      constexpr int NPK = (ACC & 1) ? HALF : 0, NPV = (ACC & 2) ? HALF : 0;
       u32x4_t prev[NPK + NPV > 0 ? NPK + NPV : 1];
 #pragma unroll
       for (int k = 0; k < NPK; ++k) {   // rows past the chunk read row 0 (in range, unused)
+        if (CPT == 1 && ov) break;
         const int rk = r0 + RSTEP * k;
         prev[k] = ld16(dKg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0);
       }
 #pragma unroll
       for (int k = 0; k < NPV; ++k) {
+        if (CPT == 1 && !ov) break;
         const int rk = r0 + RSTEP * k;
         prev[NPK + k] = ld16(dVg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0);
       }
@@ -683,7 +709,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < NDW; ++j)
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
+            for (int g = 0; g < NG; ++g) {
               const f32x16_t& v = acc[j];
               const u32x4_t w = {pack_bf16x2(v[8 * g + 0], v[8 * g + 1]), pack_bf16x2(v[8 * g + 2], v[8 * g + 3]),
                                  pack_bf16x2(v[8 * g + 4], v[8 * g + 5]), pack_bf16x2(v[8 * g + 6], v[8 * g + 7])};
@@ -740,8 +766,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
           // read and add on every row (the staging holds all 64), store only rows in the chunk
-          const bool isv = i >= CPT / 2;
-          const int k = i % (CPT / 2);
+          const bool isv = CPT == 1 ? ov : i >= CPT / 2;
+          const int k = CPT == 1 ? 0 : i % (CPT / 2 > 0 ? CPT / 2 : 1);
           u32x4_t v = ld16((isv ? vst : kst) + lds0 + RSTEP * ROWB * k);
           if (((ACC & 1) && !isv) || ((ACC & 2) && isv)) {
             const u32x4_t& pv = prev[isv ? NPK + k : k];
@@ -762,7 +788,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2 * NG; ++q) {
           f32x4_t v = {dq[db][4 * q], dq[db][4 * q + 1], dq[db][4 * q + 2], dq[db][4 * q + 3]};
           *reinterpret_cast<f32x4_t*>(W + (int64_t)m * D + 32 * db + 8 * q + 4 * hh) = v;
         }
@@ -789,6 +815,7 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restr
 }
 
 bool bwd_mfma_supported(int M, int D) {
+  if (D == 16) return M == 32 || M == 64 || M == 128;
   return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128 || M == 256);
 }
 
@@ -820,7 +847,13 @@ static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t s) {
 
 template <bool DQ>
 static hipError_t launch_kv_dq(const BwdArgs& a, hipStream_t s) {
-  if (a.D == 64) {
+  if (a.D == 16) {
+    switch (a.M) {
+      case 32: return launch_kv_t<16, 32, 4, 3, DQ>(a, s);
+      case 64: return launch_kv_t<16, 64, 4, 3, DQ>(a, s);
+      case 128: return launch_kv_t<16, 128, 4, 3, DQ>(a, s);
+    }
+  } else if (a.D == 64) {
     switch (a.M) {
       case 32: return launch_kv_t<64, 32, 4, 3, DQ>(a, s);
       case 64: return launch_kv_t<64, 64, 4, 3, DQ>(a, s);
@@ -844,7 +877,7 @@ bool bwd_kv_fuses_dq(int M, int D) { return !(M == 256 && D == 128); }
 
 // D=64 with M<=128: 4 waves of <=248 VGPRs and <=80 KB of LDS, so two per CU;
 // the other shapes need more than half the LDS or all 256 VGPRs per lane
-int bwd_kv_blocks_per_cu(int M, int D) { return D == 64 && M <= 128 ? 2 : 1; }
+int bwd_kv_blocks_per_cu(int M, int D) { return (D == 64 || D == 16) && M <= 128 ? 2 : 1; }
 
 hipError_t launch_bwd_kv_mfma(const BwdArgs& a, bool with_dq, hipStream_t s) {
   return with_dq ? launch_kv_dq<true>(a, s) : launch_kv_dq<false>(a, s);

@@ -52,7 +52,7 @@ def _check(w, x, Z, L, dQ, dK, dV, fp32=False):
 
 # every matrix-core shape: fused (one pass) and split (separate query-gradient pass)
 @pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64),
-                                 (32, 128), (64, 128), (128, 128), (256, 128)])
+                                 (32, 128), (64, 128), (128, 128), (256, 128), (32, 16), (64, 16), (128, 16)])
 def test_backward_masked_bf16(M, D):
     w, x = _masked_case(M, D, N=2048, R=4)
     _check(w, x, *_run(w, x))
@@ -92,6 +92,18 @@ def test_backward_unmasked_ragged_bf16():
     K = W.normal((1, 2, 3000, 64), 950, W.T_K, 1.0, torch.bfloat16, DEV)
     V = W.normal((1, 2, 3000, 64), 950, W.T_V, 1.0, torch.bfloat16, DEV)
     dZ = W.normal((1, 2, 128, 64), 950, W.T_DZ, 1.0, torch.bfloat16, DEV)
+    x = {"Q": Q, "K": K, "V": V, "dZ": dZ}
+    _check(base, x, *_run(base, x))
+
+
+@pytest.mark.parametrize("M", [64, 128])
+def test_backward_head_dim_16_unmasked_ragged(M):
+    """Head dim 16 without a mask, ragged partitions and a tail that is not a whole tile."""
+    base = W.shrink(W.FLAREPP_D16, 3333, R=5, H=2, ragged=True)
+    Q = W.normal((2, M, 16), 955 + M, W.T_Q, 0.25, torch.bfloat16, DEV)
+    K = W.normal((1, 2, 3333, 16), 955 + M, W.T_K, 1.0, torch.bfloat16, DEV)
+    V = W.normal((1, 2, 3333, 16), 955 + M, W.T_V, 1.0, torch.bfloat16, DEV)
+    dZ = W.normal((1, 2, M, 16), 955 + M, W.T_DZ, 1.0, torch.bfloat16, DEV)
     x = {"Q": Q, "K": K, "V": V, "dZ": dZ}
     _check(base, x, *_run(base, x))
 

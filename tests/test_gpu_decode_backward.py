@@ -180,3 +180,25 @@ def test_flarepp_shared_projection_chain_small():
         compare_bf16(g[k], r[k], k)
     assert g["dKt"] is g["dK"] and g["dVt"] is g["dV"]
 
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_flarepp_backward_chain_head_dim_16(shared):
+    """The three-call chain at head dim 16 (the pages' C = 128, H = 8 backbone), separate or shared projections."""
+    w = W.shrink(W.FLAREPP_D16, 5000, R=4, H=2, ragged=True)
+    x = w.make(DEV)
+    dY = W.normal((1, 2, 5000, 16), 1530, W.T_DZ, 1.0, torch.bfloat16, DEV)
+    Kt, Vt = (x["K"], x["V"]) if shared else (x["Kt"], x["Vt"])
+    fwd = fl.flarepp_forward(x["Qt"], Kt, Vt, x["K"], x["V"], w.offsets, w.scale)
+    g = fl.flarepp_backward(fwd, x["Qt"], Kt, Vt, x["K"], x["V"], w.offsets, dY, w.scale)
+    torch.cuda.synchronize()
+    if shared:
+        r = ref.flarepp_shared_bwd_ref(x["Qt"], x["K"], x["V"], w.offsets, w.scale, dY, round_qx_bf16=True)
+        names = ("dQt", "dK", "dV")
+    else:
+        r = ref.flarepp_bwd_ref(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale, dY,
+                                round_qx_bf16=True)
+        names = ("dQt", "dKt", "dVt", "dK", "dV")
+    compare_bf16(g["dQX"], r["dQX"], "dQX")
+    for k in names:
+        compare_bf16(g[k], r[k], k)
+
