@@ -40,8 +40,10 @@
  *  - The library holds no state between calls: the statistics saved by one
  *    encoder invocation are the caller's to keep [FLARE++ backward paragraph].
  *  - Supported shapes: D % 4 == 0 and 4 <= D <= 256, M >= 1; matrix-core paths
- *    for bfloat16 with D in {64,128} and M a multiple of 32 up to 256, a vector
- *    path for M = 1, and a general vector path for everything else.
+ *    for bfloat16 with D in {64,128} and M a multiple of 32 up to 256 (and D = 16:
+ *    the encoder without a mask at M in {64,128}, the decode at M up to 256, both
+ *    backwards at M in {32,64,128}), a vector path for M = 1, and a general vector
+ *    path for everything else.
  */
 #ifndef FLARE_H
 #define FLARE_H
@@ -185,7 +187,8 @@ size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, i
  * the FLARE++ chain).  flags: FLARE_BWD_ACCUMULATE_* below, or 0.
  * Offsets are validated as in flare_encode; workspace must hold
  * flare_encode_bwd_workspace_size() bytes, 16-byte aligned.  For bf16 with
- * D in {64,128} and M in {32,64,128,256} the matrix-core path runs; it needs
+ * D in {64,128} and M in {32,64,128,256}, or D = 16 and M in {32,64,128}, the
+ * matrix-core path runs; it needs
  * Q, K, V, dZ, dQ, dK, dV 16-byte aligned (else FLARE_EINVAL) and sums dQ over
  * token chunks in a fixed order, so results are bitwise reproducible.
  */
@@ -227,7 +230,7 @@ size_t flare_decode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, i
  * (their Y is 0): dXq rows written as 0, no contribution to dKlat or dZ.
  * All pointers are device pointers owned by the caller; workspace must hold
  * flare_decode_bwd_workspace_size() bytes, 16-byte aligned.  Shapes as flare_decode
- * (M <= 256).  For bf16 with D in {64,128} and M in {32,64,128} the matrix-core path runs;
+ * (M <= 256).  For bf16 with D in {16,64,128} and M in {32,64,128} the matrix-core path runs;
  * it needs every tensor 16-byte aligned (else FLARE_EINVAL) and sums the latent gradients
  * over token chunks in a fixed order (bitwise reproducible).
  */
