@@ -209,3 +209,25 @@ def test_full_flarepp_backward_chain():
         compare_bf16(g["dQX"][:, h:h + 1], r["dQX"], f"dQX[h={h}]")
         for k in ("dQt", "dKt", "dVt", "dK", "dV"):
             compare_bf16(g[k][:, h:h + 1], r[k], f"{k}[h={h}]")
+
+
+def test_full_flarepp_backward_chain_head_dim_16():
+    """FLARE++ backward chain at head dim 16 (B=1, H=8, N=2^20, M=128, R=16), every output finite, one
+    head recomputed by the oracle as executed (Q(X) rounded to bf16)."""
+    w = W.FLAREPP_D16
+    _say(f"case {w.name} backward")
+    x = w.make(DEV)
+    dY = W.normal((w.B, w.H, w.N, w.D), w.wid, W.T_DZ, 1.0, torch.bfloat16, DEV)
+    fwd = fl.flarepp_forward(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale)
+    g = fl.flarepp_backward(fwd, x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, dY, w.scale)
+    torch.cuda.synchronize()
+    for k, t in g.items():
+        _finite(t, k)
+    h = 6
+    xs = {k: v[:, h:h + 1].cpu() if v.dim() == 4 else v[h:h + 1].cpu() for k, v in x.items()}
+    r = ref.flarepp_bwd_ref(xs["Qt"], xs["Kt"], xs["Vt"], xs["K"], xs["V"], w.offsets, w.scale,
+                            dY[:, h:h + 1].cpu(), round_qx_bf16=True)
+    compare_bf16(g["dQX"][:, h:h + 1], r["dQX"], f"dQX[h={h}]")
+    for k in ("dQt", "dKt", "dVt", "dK", "dV"):
+        compare_bf16(g[k][:, h:h + 1], r[k], f"{k}[h={h}]")
+
