@@ -41,7 +41,7 @@
  *    encoder invocation are the caller's to keep [FLARE++ backward paragraph].
  *  - Supported shapes: D % 4 == 0 and 4 <= D <= 256, M >= 1; matrix-core paths
  *    for bfloat16 with D in {64,128} and M a multiple of 32 up to 256 (and D = 16:
- *    the encoder without a mask at M in {64,128}, the decode at M up to 256, both
+ *    the encoder at M in {32,64,128,256}, the decode at M up to 256, both
  *    backwards at M in {32,64,128}), a vector path for M = 1, and a general vector
  *    path for everything else.
  */

@@ -205,9 +205,15 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
   constexpr int STAGE = 2 * TB;
   constexpr int NI = TB / 1024;            // 1 KB direct loads per tile and tensor
   constexpr int KS = D / 16;               // k-steps of the score product
-  constexpr int DB = D / 32;               // 32-row blocks of O^T
-  constexpr int OPS = 2 * NI / NW;         // loads this wave issues per tile
-  static_assert(NI % NW == 0, "loads must split evenly over the waves");
+  // 32-row blocks of O^T; at head dim 16 one block whose rows 16..31 are
+  // products of repeated head dims, never stored
+  constexpr int DB = D >= 32 ? D / 32 : 1;
+  // a tile of fewer 1 KB loads than waves (head dim 16) is loaded by its first
+  // NI waves; the others' waits pass at once
+  constexpr int NJ = NI >= NW ? NI / NW : 1;
+  constexpr int OPS = 2 * NJ;              // loads a loading wave issues per tile
+  static_assert(D == 16 || D == 64 || D == 128, "head dim 16, 64 or 128");
+  static_assert(NI >= 1 && (NI % NW == 0 || NI < NW), "loads must split evenly over the waves");
   static_assert(OPS * (S - 2) < 64, "vmcnt range");
   // G token groups of NW waves each: group g takes tiles g, g+G, g+2G, ...
   // of the chunk into its own LDS ring; their states are combined at the end.
@@ -262,7 +268,6 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
   // this lane's 16-byte piece of each of its loads: byte offset within a full
   // tile, and within row 0 (rows past the chunk re-read row 0: in bounds,
   // never used as valid)
-  constexpr int NJ = NI / NW;
   uint32_t voff[NJ], voff0[NJ];
   int vrow[NJ];
 #pragma unroll
@@ -278,6 +283,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
   // K rows of local tile u go to K slot u % S, V rows to V slot u % S (the
   // second half of the stage).  Rows past the chunk re-read row 0.
   auto issue_half = [&](int u, int slot, bool is_v) {
+    if (NI < NW && wave >= NI) return;   // (wave-uniform)
     const int t0 = t_begin + (grp + G * u) * TILE;
     const int nrows = t_end - t0;
     const uint16_t* base = (is_v ? Vg : Kg) + (int64_t)t0 * D;
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
   const int swk = kv_swz<D>(swap23(l32));             // rows 32*b2 + swap23(l32)
   // K operands are read in groups of KG k-steps for both 32-token blocks before
   // the products that use them, so the LDS latency is paid once per group
-  constexpr int KG = D == 64 ? 4 : 2;
+  constexpr int KG = D == 64 ? 4 : (D == 128 ? 2 : 1);
   auto scores = [&](const uint8_t* kst, f32x16_t* sc) {
     sc[0] = f32x16_t{};
     sc[1] = f32x16_t{};
@@ -484,7 +490,8 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
             for (int kk = 0; kk < VK; ++kk)
 #pragma unroll
               for (int db = 0; db < DB; ++db) {
-                const int d0 = 32 * db + 16 * (lg & 1) + 4 * (li & 3);
+                // head dim 16: the lanes of operand rows 16..31 read dims 0..15 again
+                const int d0 = 32 * db + (D >= 32 ? 16 * (lg & 1) : 0) + 4 * (li & 3);
                 const int chl = d0 >> 3, half = (d0 & 7) * 2;
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
@@ -863,7 +870,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
 }
 
 bool encode_mfma_supported(int M, int D) {
-  return (D == 64 || D == 128) && (M == 32 || M == 64 || M == 128 || M == 256);
+  return (D == 16 || D == 64 || D == 128) && (M == 32 || M == 64 || M == 128 || M == 256);
 }
 
 template <int D, int NW, int S, int G, int L = 0, bool RS = true>
@@ -901,6 +908,7 @@ int encode_mfma_per_cu(int M, int D, bool masked) {
   // workgroups of the chosen variant that fit on one CU (LDS and registers)
   if (encode_ilv_used(M, D, masked)) return 1;
   if (D == 64) return encode_mfma_groups(M, D) > 1 ? 1 : (encode_mfma_stages(M, D) == 3 ? 3 : 2);
+  if (D == 16) return M >= 256 ? 2 : (M == 128 ? 4 : 8);   // 16 KB rings, up to 16 waves of <=128 VGPRs
   return M >= 128 ? 1 : 2;
 }
 
@@ -962,6 +970,14 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
           default: return s3 ? launch_d64<4, 3, 1>(a, s, pipe) : launch_d64<4, 4, 1>(a, s, pipe);
         }
       case 256: return s3 ? launch_d64<8, 3, 1>(a, s, pipe) : launch_d64<8, 4, 1>(a, s, pipe);
+    }
+  } else if (a.D == 16) {
+    // padding masks at head dim 16 (the pipelined encoder takes the rest): 2 KB tiles, 4-stage rings
+    switch (a.M) {
+      case 32: return launch_mfma_t<16, 1, 4, 1>(a, s);
+      case 64: return launch_mfma_t<16, 2, 4, 1>(a, s);
+      case 128: return launch_mfma_t<16, 4, 4, 1>(a, s);
+      case 256: return launch_mfma_t<16, 8, 4, 1>(a, s);
     }
   } else if (a.D == 128) {
     switch (a.M) {

@@ -66,10 +66,10 @@ def test_fp32_small_encoder_workload():
 
 
 @pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64), (64, 128), (128, 128), (256, 128),
-                                 (64, 16), (128, 16)])
+                                 (32, 16), (64, 16), (128, 16), (256, 16)])
 @pytest.mark.parametrize("masked", [False, True])
 def test_bf16_encoder_matrix_core(M, D, masked):
-    # head dim 16: the pipelined encoder without a mask, the vector path with one
+    # head dim 16 at 64 or 128 latent rows without a mask takes the pipelined encoder
     w, x = _enc_case(M, D, N=2500, R=5, masked=masked)
     _check_encode(w, x)
 
@@ -93,11 +93,12 @@ def test_bf16_encoder_split_partitions():
 
 
 @pytest.mark.parametrize("masked", [False, True])
-def test_bf16_encoder_partitions_shorter_than_a_tile_per_group(masked):
+@pytest.mark.parametrize("D", [64, 16])
+def test_bf16_encoder_partitions_shorter_than_a_tile_per_group(masked, D):
     """Partitions of 1, 63, 64, 65, 127, 128, 129 and 0 tokens: fewer 64-token
     tiles than the encoder's token groups, partial last tiles, an empty one."""
     offs = [0, 1, 64, 128, 193, 320, 448, 577, 577, 800]
-    w, x = _enc_case(128, 64, N=offs[-1], R=len(offs) - 1, masked=masked)
+    w, x = _enc_case(128, D, N=offs[-1], R=len(offs) - 1, masked=masked)
     w = w.with_(offsets=offs)
     if masked:
         x["mask"][:, 1:64] = 1          # keep the 63-token partition fully valid

@@ -63,6 +63,9 @@ CASES = {
     # partitions split over several chunks next to a direct one and an empty one
     "split_partitions": dict(M=128, D=64, offsets=[0, 0, 30000, 30100, 40000], B=2, H=2),
     "split_partitions_masked": dict(M=64, D=128, offsets=[0, 20000, 20000, 20050, 26000], B=1, H=2, masked=True),
+    # head dim 16: the general matrix-core encoder with a padding mask, and at 256 latent rows
+    "mfma_M128_D16_masked": dict(M=128, D=16, offsets=[0, 700, 700, 1900, 2500, 4033], B=2, H=3, masked=True),
+    "mfma_M256_D16_split": dict(M=256, D=16, offsets=[0, 20000, 20000, 20050, 26000], B=1, H=2),
     # two launches: single-query vector path, float32 vector path
     "q1_fallback": dict(M=1, D=128, offsets=[0, 5000, 5000, 9000], B=2, H=4),
     "f32_fallback": dict(M=16, D=32, offsets=[0, 300, 500, 924, 1024], B=1, H=1, dtype=torch.float32),
