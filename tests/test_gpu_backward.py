@@ -154,7 +154,7 @@ def test_backward_is_deterministic():
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("M,D", [(128, 64), (256, 128)])
+@pytest.mark.parametrize("M,D", [(128, 64), (256, 128), (128, 16)])
 def test_heavy_first_launch_order_changes_no_bit(M, D, monkeypatch):
     """Masked inputs launch their chunks heaviest first; each chunk writes its own
     state and partial, so the forward states and all gradients are the same bits
