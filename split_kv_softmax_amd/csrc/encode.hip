@@ -1210,9 +1210,9 @@ hipError_t launch_encode_q1(const EncodeArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // General vector encoder (float32 inputs, or bf16 shapes without a matrix-core
-// variant).  One wave per (batch, head, chunk, latent row); a 64-token tile
-// gives one score per lane, then lanes switch to head dimensions to
-// accumulate the weighted values.  All arithmetic is float32.
+// variant).  One wave per (batch, head, chunk, latent row); a token tile gives
+// one score per lane, then lanes switch to head dimensions to accumulate the
+// weighted values.  All arithmetic is float32.
 // ---------------------------------------------------------------------------
 template <typename TIn>
 __device__ __forceinline__ float ldv(const TIn* p);
@@ -1221,32 +1221,67 @@ __device__ __forceinline__ float ldv<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float ldv<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-// One latent row m of (b, h) over chunk c, on one wave.
+// The workgroup's four waves take latent rows 4g .. 4g+3 of (b, h) over chunk
+// c.  Token tiles of TT rows (64 up to head dim 64, then 64*64/D) are staged
+// in LDS as float32 with rows padded to D+1 words (a lane reading its own row
+// hits its own bank), once for all four rows.  Per tile: one score per lane
+// (lane = token), the tile's maximum and weights, then lanes switch to head
+// dimensions to accumulate the weighted values in token order.
+constexpr int kGenTileWords = 2 * 64 * 65;   // K and V tiles: 2 * TT * (D+1) <= 8320 for D <= 256
 template <typename TIn>
-__device__ __forceinline__ void encode_generic_row(const EncodeArgs& a, int b, int h, int c, int m, int lane) {
+__global__ __launch_bounds__(256) void encode_generic_kernel(const EncodeArgs a) {
   constexpr int MAXDL = 4;  // D <= 256
+  __shared__ float sm[kGenTileWords + 4 * 256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nch = a.tab.nchunks;
+  const int mgroups = (a.M + 3) / 4;
+  int bid = blockIdx.x;
+  const int c = bid % nch;
+  bid /= nch;
+  const int mg = bid % mgroups;
+  bid /= mgroups;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int m = 4 * mg + wave;
+  const bool active = m < a.M;   // (wave-uniform) a row past M only helps stage the tiles
   const int D = a.D;
+  const int DP = D + 1;
+  const int TT = D <= 64 ? 64 : (D <= 128 ? 32 : 16);
+  float* kt = sm;
+  float* vt = sm + TT * DP;
+  float* qs = sm + kGenTileWords + wave * 256;
   const int t_begin = a.tab.bnd[c], t_end = a.tab.bnd[c + 1];
   const int64_t bh = (int64_t)b * a.H + h;
   const TIn* Kg = static_cast<const TIn*>(a.K) + bh * (int64_t)a.N * D;
   const TIn* Vg = static_cast<const TIn*>(a.V) + bh * (int64_t)a.N * D;
-  const TIn* Qr = static_cast<const TIn*>(a.Q) + (int64_t)b * a.q_bstride + ((int64_t)h * a.M + m) * D;
   const uint8_t* mk = a.mask ? a.mask + (int64_t)b * a.N : nullptr;
   const float c2 = a.scale_log2;
+  if (active) {
+    const TIn* Qr = static_cast<const TIn*>(a.Q) + (int64_t)b * a.q_bstride + ((int64_t)h * a.M + m) * D;
+    for (int d = lane; d < D; d += 64) qs[d] = ldv(Qr + d);
+  }
 
   float m_run = kNegInf, l_run = 0.f, acc[MAXDL];
 #pragma unroll
   for (int j = 0; j < MAXDL; ++j) acc[j] = 0.f;
 
-  for (int t0 = t_begin; t0 < t_end; t0 += 64) {
-    const int t = t0 + lane;
-    bool ok = t < t_end;
-    if (ok && mk) ok = mk[t] != 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += TT) {
+    const int n = t_end - t0 < TT ? t_end - t0 : TT;
+    __syncthreads();   // every wave is done with the previous tile
+    for (int f = threadIdx.x; f < n * D; f += 256) {
+      const int r = f / D, d = f - r * D;
+      kt[r * DP + d] = ldv(Kg + (int64_t)t0 * D + f);
+      vt[r * DP + d] = ldv(Vg + (int64_t)t0 * D + f);
+    }
+    __syncthreads();
+    if (!active) continue;
+    bool ok = lane < n;
+    if (ok && mk) ok = mk[t0 + lane] != 0;
     float sdot = kNegInf;
     if (ok) {
-      const TIn* kr = Kg + (int64_t)t * D;
+      const float* kr = kt + lane * DP;
       float d = 0.f;
-      for (int i = 0; i < D; ++i) d = __builtin_fmaf(ldv(Qr + i), ldv(kr + i), d);
+      for (int i = 0; i < D; ++i) d = __builtin_fmaf(qs[i], kr[i], d);
       sdot = d;
     }
     const uint64_t okmask = __ballot(ok);
@@ -1259,18 +1294,19 @@ __device__ __forceinline__ void encode_generic_row(const EncodeArgs& a, int b, i
     l_run = l_run * alpha + wave_sum(p);
 #pragma unroll
     for (int j = 0; j < MAXDL; ++j) acc[j] *= alpha;
-    for (int i = 0; i < 64; ++i) {
+    for (int i = 0; i < n; ++i) {
       const float pi = __shfl(p, i, 64);
       if (!((okmask >> i) & 1ull)) continue;
-      const TIn* vr = Vg + (int64_t)(t0 + i) * D;
+      const float* vr = vt + i * DP;
 #pragma unroll
       for (int j = 0; j < MAXDL; ++j) {
         const int d = lane + 64 * j;
-        if (d < D) acc[j] = __builtin_fmaf(pi, ldv(vr + d), acc[j]);
+        if (d < D) acc[j] = __builtin_fmaf(pi, vr[d], acc[j]);
       }
     }
     m_run = m_new;
   }
+  if (!active) return;
   const int slot = a.tab.slot[c];
   float* Ob;
   float* Lb;
@@ -1290,22 +1326,6 @@ __device__ __forceinline__ void encode_generic_row(const EncodeArgs& a, int b, i
     if (d < D) Ob[d] = acc[j] * inv;
   }
   if (lane == 0) *Lb = empty ? kNegInf : (m_run * a.scale + __logf(l_run));
-}
-
-template <typename TIn>
-__global__ __launch_bounds__(256) void encode_generic_kernel(const EncodeArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nch = a.tab.nchunks;
-  const int mgroups = (a.M + 3) / 4;
-  int bid = blockIdx.x;
-  const int c = bid % nch;
-  bid /= nch;
-  const int mg = bid % mgroups;
-  bid /= mgroups;
-  const int h = bid % a.H;
-  const int b = bid / a.H;
-  const int m = 4 * mg + wave;
-  if (m < a.M) encode_generic_row<TIn>(a, b, h, c, m, lane);
 }
 
 hipError_t launch_encode_generic(const EncodeArgs& a, bool bf16, hipStream_t s) {
