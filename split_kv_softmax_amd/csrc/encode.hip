@@ -1268,10 +1268,12 @@ __global__ __launch_bounds__(256) void encode_generic_kernel(const EncodeArgs a)
   for (int t0 = t_begin; t0 < t_end; t0 += TT) {
     const int n = t_end - t0 < TT ? t_end - t0 : TT;
     __syncthreads();   // every wave is done with the previous tile
+    // padded tokens get zero value rows (their weights are 0 and a padded row
+    // may hold NaN), so the value loop below needs no per-token branch
     for (int f = threadIdx.x; f < n * D; f += 256) {
       const int r = f / D, d = f - r * D;
       kt[r * DP + d] = ldv(Kg + (int64_t)t0 * D + f);
-      vt[r * DP + d] = ldv(Vg + (int64_t)t0 * D + f);
+      vt[r * DP + d] = (!mk || mk[t0 + r] != 0) ? ldv(Vg + (int64_t)t0 * D + f) : 0.f;
     }
     __syncthreads();
     if (!active) continue;
@@ -1281,10 +1283,15 @@ __global__ __launch_bounds__(256) void encode_generic_kernel(const EncodeArgs a)
     if (ok) {
       const float* kr = kt + lane * DP;
       float d = 0.f;
-      for (int i = 0; i < D; ++i) d = __builtin_fmaf(qs[i], kr[i], d);
+      for (int i = 0; i < D; i += 4) {   // D % 4 == 0
+        const float k0 = kr[i], k1 = kr[i + 1], k2 = kr[i + 2], k3 = kr[i + 3];
+        d = __builtin_fmaf(qs[i], k0, d);
+        d = __builtin_fmaf(qs[i + 1], k1, d);
+        d = __builtin_fmaf(qs[i + 2], k2, d);
+        d = __builtin_fmaf(qs[i + 3], k3, d);
+      }
       sdot = d;
     }
-    const uint64_t okmask = __ballot(ok);
     const float mx = wave_max(sdot);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
@@ -1294,14 +1301,27 @@ __global__ __launch_bounds__(256) void encode_generic_kernel(const EncodeArgs a)
     l_run = l_run * alpha + wave_sum(p);
 #pragma unroll
     for (int j = 0; j < MAXDL; ++j) acc[j] *= alpha;
-    for (int i = 0; i < n; ++i) {
+    // tokens in order, four per step so that their reads are issued together
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+      float pi[4], vv[4][MAXDL];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        pi[k] = __shfl(p, i + k, 64);
+#pragma unroll
+        for (int j = 0; j < MAXDL; ++j) vv[k][j] = lane + 64 * j < D ? vt[(i + k) * DP + lane + 64 * j] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int j = 0; j < MAXDL; ++j) acc[j] = __builtin_fmaf(pi[k], vv[k][j], acc[j]);
+    }
+    for (; i < n; ++i) {
       const float pi = __shfl(p, i, 64);
-      if (!((okmask >> i) & 1ull)) continue;
-      const float* vr = vt + i * DP;
 #pragma unroll
       for (int j = 0; j < MAXDL; ++j) {
         const int d = lane + 64 * j;
-        if (d < D) acc[j] = __builtin_fmaf(pi, vr[d], acc[j]);
+        if (d < D) acc[j] = __builtin_fmaf(pi, vt[i * DP + d], acc[j]);
       }
     }
     m_run = m_new;
