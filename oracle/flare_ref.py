@@ -266,6 +266,17 @@ def decode_ref(Xq, Klat, Z, scale: float, token_mask=None,
     return Y
 
 
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """x rounded to bfloat16 (to float32, then to nearest even bfloat16) and widened back.
+
+    The kernels hold Q(X) in float32 and round that to bfloat16; the detour
+    through float32 reproduces that.  NaN stays NaN (it marks a (batch, head)
+    slice that was not computed when only some slices are)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
 def flarepp_ref(Qt, Kt, Vt, K, V, offsets, scale: float, round_qx_bf16: bool = False,
                 slices: Optional[List[Tuple[int, int]]] = None) -> Dict[str, np.ndarray]:
     """FLARE++ forward: Q(X) = Enc(Qt, Kt, Vt); Z = Enc(Q(X), K, V); Y = Dec(K, Q(X), Z).
@@ -276,11 +287,7 @@ def flarepp_ref(Qt, Kt, Vt, K, V, offsets, scale: float, round_qx_bf16: bool = F
     """
     e1 = encode_ref(Qt, Kt, Vt, offsets, None, scale, slices=slices)
     QX = e1["Z"]
-    QXu = QX
-    if round_qx_bf16:
-        import torch
-        QXu = torch.from_numpy(np.nan_to_num(QX)).to(torch.float32).to(torch.bfloat16).to(
-            torch.float64).numpy()
+    QXu = bf16_round(QX) if round_qx_bf16 else QX
     e2 = encode_ref(QXu, K, V, offsets, None, scale, slices=slices)
     Y = decode_ref(K, QXu, e2["Z"], scale, slices=slices)
     return {"QX": QX, "QX_L": e1["L"], "QX_O_part": e1["O_part"], "QX_L_part": e1["L_part"],
@@ -427,11 +434,7 @@ def flarepp_bwd_ref(Qt, Kt, Vt, K, V, offsets, scale: float, dY, round_qx_bf16: 
     """
     f = flarepp_ref(Qt, Kt, Vt, K, V, offsets, scale, round_qx_bf16=round_qx_bf16, slices=slices)
     QX = f["QX"]
-    QXu = QX
-    if round_qx_bf16:
-        import torch
-        QXu = torch.from_numpy(np.nan_to_num(QX)).to(torch.float32).to(torch.bfloat16).to(
-            torch.float64).numpy()
+    QXu = bf16_round(QX) if round_qx_bf16 else QX
     d = decode_bwd_ref(K, QXu, f["Z"], scale, dY, slices=slices)
     g2 = encode_bwd_ref(QXu, K, V, None, scale, f["Z"], f["L"], d["dZ"], slices=slices)
     dQX = d["dKlat"] + g2["dQ"]

@@ -486,3 +486,48 @@ def test_flarepp_shared_projection_backward_matches_autograd():
     for name, t in (("dQt", tq), ("dK", tk), ("dV", tv)):
         np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
 
+
+
+def _bf16_straight_through(t):
+    """t rounded to bfloat16 in the forward pass, the identity in the backward pass."""
+    return t + (t.detach().float().bfloat16().double() - t.detach())
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_flarepp_as_executed_chain_matches_autograd_with_bf16_queries(shared):
+    """The "as executed" chain (Q(X) consumed as bfloat16 by the physical-value encoder and
+    the decoder, its gradient passed through the rounding unchanged) against fp64 autograd
+    through the SDPA chain with a straight-through rounding of Q(X).  The query-synthesis
+    encoder's backward must use its own unrounded output; a rounded copy in the wrong
+    place (encoder 1's saved Z, or one call rounded and the other not) moves the result by
+    ~1e-3 relative, far outside the 1e-9 bound."""
+    rng = np.random.default_rng(26 + shared)
+    B, H, N, M, D = 1, 2, 56, 4, 8
+    Qt = rng.standard_normal((H, M, D)) * 2
+    Kt, Vt, K, V, dY = (rng.standard_normal((B, H, N, D)) for _ in range(5))
+    if shared:
+        Kt, Vt = K, V
+    s = 1 / math.sqrt(D)
+    offs = [0, 11, 11, 40, 56]
+    f = ref.flarepp_ref(Qt, Kt, Vt, K, V, offs, s, round_qx_bf16=True)
+    g = (ref.flarepp_shared_bwd_ref(Qt, K, V, offs, s, dY, round_qx_bf16=True) if shared else
+         ref.flarepp_bwd_ref(Qt, Kt, Vt, K, V, offs, s, dY, round_qx_bf16=True))
+    g_plain = (ref.flarepp_shared_bwd_ref(Qt, K, V, offs, s, dY) if shared else
+               ref.flarepp_bwd_ref(Qt, Kt, Vt, K, V, offs, s, dY))
+    tq = torch.tensor(np.broadcast_to(Qt, (B, H, M, D)).copy(), requires_grad=True)
+    tk, tv = (torch.tensor(a, requires_grad=True) for a in (K, V))
+    tkt, tvt = (tk, tv) if shared else (torch.tensor(a, requires_grad=True) for a in (Kt, Vt))
+    QX = F.scaled_dot_product_attention(tq, tkt, tvt, scale=s)
+    QXr = _bf16_straight_through(QX)
+    Z = F.scaled_dot_product_attention(QXr, tk, tv, scale=s)
+    Y = F.scaled_dot_product_attention(tk, QXr, Z, scale=s)
+    (Y * torch.from_numpy(dY)).sum().backward()
+    np.testing.assert_allclose(f["QX"], QX.detach().numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(f["Z"], Z.detach().numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(f["Y"], Y.detach().numpy(), rtol=1e-11, atol=1e-13)
+    names = (("dQt", tq), ("dK", tk), ("dV", tv)) if shared else \
+        (("dQt", tq), ("dKt", tkt), ("dVt", tvt), ("dK", tk), ("dV", tv))
+    for name, t in names:
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-9, atol=1e-11, err_msg=name)
+        # the rounding is visible: the plain chain differs well beyond the bound above
+        assert np.abs(g_plain[name] - g[name]).max() > 1e-6, name
