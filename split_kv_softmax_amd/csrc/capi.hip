@@ -86,16 +86,6 @@ struct EncodePlan {
   size_t ws_bytes = 0;
 };
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  return atoi(v);
-}
-
-// Masked inputs launch their blocks heaviest first (valid-token count per
-// chunk); FLARE_HEAVY_FIRST=0 keeps the plain block order.
-bool heavy_first_enabled() { return env_int("FLARE_HEAVY_FIRST", 1) != 0; }
-
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 // Chunk length for a partition of n tokens.
@@ -108,8 +98,7 @@ int chunk_len_for(EncKind kind, int B, int H, int R, int M, int D, int64_t max_p
       // percent of the K/V bytes (state bytes / K,V bytes = 2M / chunk_len).
       const int64_t base = (int64_t)B * H * R;
       const int64_t target = 256 * (int64_t)encode_mfma_per_cu(M, D, masked);
-      int split = env_int("FLARE_ENCODE_SPLIT", 0);
-      if (split <= 0) split = (int)std::max<int64_t>(1, (target + base - 1) / base);
+      const int split = (int)std::max<int64_t>(1, (target + base - 1) / base);
       int len = round_up((int)((max_part + split - 1) / split), 64);
       const int min_len = std::max(1024, 32 * M);
       if (split > 1 && len < min_len) len = min_len;
@@ -322,7 +311,7 @@ flare_status encode_impl(flare_dtype dtype, int B, int H, int N, int M, int D, c
     a.tab.bnd[n] = plan.chunks[c0 + n - 1].hi;
     hipError_t e;
     a.order = nullptr;
-    if (plan.order_bytes && heavy_first_enabled() && (int64_t)B * n <= kMaxOrderItems) {
+    if (plan.order_bytes && (int64_t)B * n <= kMaxOrderItems) {
       int32_t* order = reinterpret_cast<int32_t*>(ws + plan.ws_bytes - plan.order_bytes);
       e = launch_heavy_first(a.mask_words, a.mask_words_stride, a.tab, B, H, order, s);
       if (e != hipSuccess) return hip_fail(e, "launch-order launch");
@@ -480,8 +469,6 @@ BwdPlan plan_bwd(flare_dtype dt, int B, int H, int N, int M, int D, bool masked)
     int64_t per = std::max<int64_t>(1, (slots + bh - 1) / bh);
     int64_t len = ((N + per - 1) / per + 63) / 64 * 64;
     len = std::max<int64_t>(len, 1024);
-    const int forced = env_int("FLARE_BWD_CHUNK", 0);
-    if (forced >= 64) len = (forced + 63) / 64 * 64;
     while ((N + len - 1) / len > kMaxChunks) len *= 2;
     for (int64_t t = 0; t < N; t += len) p.bnd.push_back((int32_t)t);
     p.bnd.push_back(N);
@@ -624,7 +611,7 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   a.tab.nchunks = nc;
   for (int i = 0; i <= nc; ++i) a.tab.bnd[i] = plan.bnd[i];
   for (int i = 0; i < nc; ++i) a.tab.slot[i] = (int16_t)i;
-  if (plan.order_bytes && heavy_first_enabled()) {
+  if (plan.order_bytes) {
     int32_t* order = reinterpret_cast<int32_t*>(ws + plan.c_bytes + plan.mw_bytes + plan.dq_bytes);
     e = launch_heavy_first(a.mask_words, a.mask_words_stride, a.tab, B, H, order, s);
     if (e != hipSuccess) return hip_fail(e, "launch-order launch");
@@ -637,7 +624,7 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
     e = launch_bwd_dq_mfma(a, s);
     if (e != hipSuccess) return hip_fail(e, "query-gradient launch");
   }
-  e = launch_bwd_kv_mfma(a, fuse, s);
+  e = launch_bwd_kv_mfma(a, s);
   if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
   // the fused kernel's partials already carry s (it contracts s dS); the query-gradient kernel's do not
   e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, fuse ? 1.f : scale, dQ, a.accumulate_dq != 0,

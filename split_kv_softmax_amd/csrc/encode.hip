@@ -197,7 +197,7 @@ __device__ __forceinline__ void merge_tail(const EncodeArgs& a, int b, int h, in
 // tile.  Rows are stored unpadded with their 16-byte chunks XOR-swizzled by
 // row so that the operand reads of a wave spread over the LDS banks.
 // ---------------------------------------------------------------------------
-template <int D, int NW, int S, int G, int L, bool RS>
+template <int D, int NW, int S, int G>
 __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeArgs a) {
   constexpr int TILE = 64;
   constexpr int ROWB = 2 * D;              // bytes per row
@@ -299,33 +299,23 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16_t{};
   float m_run = kNegInf;   // reference maximum (raw dot products) of row 32w + l32
-  // running row sum of the weights.  RS: on the matrix cores, ones x P^T puts
-  // the row's sum of the bf16-rounded weights in every register of both lane
-  // halves; else on the vector ALUs, each lane half summing its own tokens'
-  // float32 weights.
+  // running row sum of the weights, on the matrix cores: ones x P^T puts the
+  // row's sum of the bf16-rounded weights in every register of both lane halves
   f32x16_t lacc = f32x16_t{};
-  float l_run = 0.f;
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const float c2 = a.scale_log2;
 
-  // With lead L = 1 the loop is software-pipelined: round u computes the
-  // scores of tile u+1 on the matrix cores while the vector ALUs turn the
-  // scores of tile u into weights, then adds tile u's weighted values.  Round
-  // u needs K(u+L) and V(u): that pair is "batch u", so the K ring runs L
-  // tiles ahead of the V ring.  (L = 0: scores and weights of a tile in the
-  // same round, for shapes whose registers cannot hold two score tiles.)
-  // vb[k] = validity bits of local tile u + k (k = 0..S-1+L); nb[k] = number
-  // of this wave's loads in batch u + k (0, NJ or 2 NJ).
-  uint64_t vb[S + L];
+  // Round u needs K(u) and V(u) ("batch u"); scores, weights and values of a
+  // tile in the same round.  vb[k] = validity bits of local tile u + k
+  // (k = 0..S-1); nb[k] = number of this wave's loads in batch u + k (0 or 2 NJ).
+  uint64_t vb[S];
 #pragma unroll
-  for (int k = 0; k < S + L; ++k) vb[k] = tile_bits(grp, k);
+  for (int k = 0; k < S; ++k) vb[k] = tile_bits(grp, k);
   int nb[S];
-  if (L == 1 && vb[0]) issue_half(0, 0, false);        // K(0) alone, before batch 0
 #pragma unroll
   for (int k = 0; k < S - 1; ++k) {
     nb[k] = 0;
-    if (vb[k + L]) { issue_half(k + L, (k + L) % S, false); nb[k] += NJ; }
-    if (vb[k]) { issue_half(k, k % S, true); nb[k] += NJ; }
+    if (vb[k]) { issue_half(k, k % S, false); issue_half(k, k % S, true); nb[k] += 2 * NJ; }
   }
   nb[S - 1] = 0;
   // the scores of tile 0
@@ -355,16 +345,6 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * KG, 0);
     }
   };
-  f32x16_t scn[2];                                     // scores of the next tile (L = 1)
-  if constexpr (L == 1) {
-    int pend = 0;
-#pragma unroll
-    for (int k = 0; k < S - 1; ++k) pend += nb[k];
-    wait_units<NJ, 2 * (S - 1)>(pend / NJ);
-    barrier_lds();
-    if (vb[0]) scores(myring, scn);
-  }
-
   const int lg = lane >> 4, li = lane & 15;
   // S rounds per trip so that each round's ring slots are compile-time constants
   for (int u0 = 0; u0 < nrounds; u0 += S) {
@@ -372,18 +352,20 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
     for (int st = 0; st < S; ++st) {
       const int u = u0 + st;
       if (u < nrounds) {
-        // batch u = {K(u+L), V(u)} complete for this wave; batches u+1 .. u+S-2 may be in flight
+        // batch u = {K(u), V(u)} complete for this wave; batches u+1 .. u+S-2 may be in flight
         int pend = 0;
 #pragma unroll
         for (int k = 1; k < S - 1; ++k) pend += nb[k];
         wait_units<NJ, 2 * (S - 2)>(pend / NJ);
         barrier_lds();
-        // every wave is past round u-1: K slot (u-1+L) % S (held K(u-1+L)) and
-        // V slot (u-1) % S (held V(u-1)) are free for batch u+S-1
-        vb[S - 1 + L] = tile_bits(grp, u + S - 1 + L);
+        // every wave is past round u-1: stage (u-1) % S is free for batch u+S-1
+        vb[S - 1] = tile_bits(grp, u + S - 1);
         nb[S - 1] = 0;
-        if (vb[S - 1 + L]) { issue_half(u + S - 1 + L, (st + S - 1 + L) % S, false); nb[S - 1] += NJ; }
-        if (vb[S - 1]) { issue_half(u + S - 1, (st + S - 1) % S, true); nb[S - 1] += NJ; }
+        if (vb[S - 1]) {
+          issue_half(u + S - 1, (st + S - 1) % S, false);
+          issue_half(u + S - 1, (st + S - 1) % S, true);
+          nb[S - 1] += 2 * NJ;
+        }
         const uint64_t bits = vb[0];
         bool partial = false;     // is any group's tile of this round partially valid?
 #pragma unroll
@@ -403,20 +385,8 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
           barrier_lds();
         }
         f32x16_t sc[2];
-        // K slot of the next tile (L = 1): its scores are computed in the same
-        // straight-line block as this tile's weights, so the matrix-core work
-        // interleaves with the vector work.  When the next tile has no valid
-        // token the slot holds stale rows; those scores are never used.
-        const uint8_t* knext = myring + ((st + 1) % S) * STAGE;
-        if constexpr (L == 1) {
-          sc[0] = scn[0];
-          sc[1] = scn[1];
-        } else {
-          if (bits) scores(myring + st * STAGE, sc);
-        }
-        if (!bits) {
-          if constexpr (L == 1) scores(knext, scn);
-        } else {
+        if (bits) {
+          scores(myring + st * STAGE, sc);
           // register r of lane half hh in block b2 holds token 32*b2 + 16*(r/8) + 8*hh + r%8
           if (bits != ~0ull) {
             const uint64_t lb = bits >> (8 * hh);
@@ -449,14 +419,12 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
           if (__ballot(grow)) {
             const float m_new = grow ? mx : m_run;
             const float alpha = grow ? fast_exp2((m_run - m_new) * c2) : 1.f;   // 0 when m_run = -inf
-            if constexpr (RS) lacc *= alpha;
-            else l_run *= alpha;
+            lacc *= alpha;
 #pragma unroll
             for (int i = 0; i < DB; ++i) o[i] *= alpha;
             m_run = m_new;
           }
           const float nmc = -((m_run == kNegInf) ? 0.f : m_run) * c2;
-          if constexpr (L == 1) scores(knext, scn);
           // weights, rounded to bf16 for the value product
           bf16x8_t pk[4];
 #pragma unroll
@@ -469,14 +437,9 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
               const u32x4_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                  pack_bf16x2(p[6], p[7])};
               pk[2 * b2 + g] = __builtin_bit_cast(bf16x8_t, w);
-              if constexpr (!RS) {
-                l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-              }
             }
-          if constexpr (RS) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) lacc = mfma32x32x16(ones, pk[ks], lacc);
-          }
+          for (int ks = 0; ks < 4; ++ks) lacc = mfma32x32x16(ones, pk[ks], lacc);
           // ---- O^T += V^T P^T ; k-step ks covers tokens 16ks .. 16ks+15.
           // Transposing reads: in each 16-lane group lane i points at token row
           // (i/4) of a 4-token block and 4 head dims starting at 4*(i%4); it gets
@@ -513,14 +476,14 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
           }
         }
 #pragma unroll
-        for (int k = 0; k < S - 1 + L; ++k) vb[k] = vb[k + 1];
+        for (int k = 0; k < S - 1; ++k) vb[k] = vb[k + 1];
 #pragma unroll
         for (int k = 0; k < S - 1; ++k) nb[k] = nb[k + 1];
       }
     }
   }
 
-  float l_tot = RS ? lacc[0] : l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = lacc[0];
   finish_chunk<D, NW, G>(smem, a, grp, wave, lane, o, m_run, l_tot, b, h, c);
   merge_tail(a, b, h, c, reinterpret_cast<int*>(smem));
 }
@@ -873,60 +836,33 @@ bool encode_mfma_supported(int M, int D) {
   return (D == 16 || D == 64 || D == 128) && (M == 32 || M == 64 || M == 128 || M == 256);
 }
 
-template <int D, int NW, int S, int G, int L = 0, bool RS = true>
+template <int D, int NW, int S, int G>
 static hipError_t launch_mfma_t(const EncodeArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
-  hipLaunchKernelGGL((encode_mfma_kernel<D, NW, S, G, L, RS>), dim3((unsigned)grid), dim3(64 * NW * G), 0, s, a);
+  hipLaunchKernelGGL((encode_mfma_kernel<D, NW, S, G>), dim3((unsigned)grid), dim3(64 * NW * G), 0, s, a);
   return hipGetLastError();
 }
 
-int encode_mfma_groups(int M, int D) {
-  // Token groups per workgroup: at head dim 64 and 128 latent rows three
-  // 4-wave groups (12 waves, three 48-KB rings) fill a CU as one workgroup,
-  // so a partition needs no split and no fold.
-  const char* e = getenv("FLARE_ENCODE_GROUPS");
-  if (e && atoi(e) >= 1 && atoi(e) <= 3 && D == 64 && (M == 128 || M == 64)) return atoi(e);
-  return (D == 64 && M == 128) ? 3 : 1;
-}
-
-int encode_mfma_stages(int M, int D) {
-  // LDS ring: D=64 stages are 16 KB, D=128 stages 32 KB.  Within 160 KB per
-  // CU: three groups of three stages, two groups of up to five, or one ring
-  // of three or four stages per workgroup.
-  const char* e = getenv("FLARE_ENCODE_STAGES");
-  const int g = encode_mfma_groups(M, D);
-  if (D == 64 && e) {
-    const int v = atoi(e);
-    if (g == 1 && (v == 3 || v == 4)) return v;
-    if (g == 2 && (v == 3 || v == 4 || v == 5)) return v;
-  }
-  if (D == 64) return g == 2 ? 4 : 3;
-  return (M >= 128) ? 4 : 3;
-}
-
+// Matrix-core encoder variants, fixed at build time.  Head dim 64: one
+// workgroup of 3-stage rings (16 KB stages) per 32*NW latent rows; at 128
+// latent rows (padding masks: the pipelined encoder takes the unmasked case)
+// three 4-wave token groups (12 waves, three 48 KB rings) fill a CU as one
+// workgroup, so a partition needs no split and no fold.  Head dim 128: 32 KB
+// stages, four of them from 128 latent rows on.  Head dim 16: 2 KB tiles,
+// 4-stage rings.
 int encode_mfma_per_cu(int M, int D, bool masked) {
   // workgroups of the chosen variant that fit on one CU (LDS and registers)
   if (encode_ilv_used(M, D, masked)) return 1;
-  if (D == 64) return encode_mfma_groups(M, D) > 1 ? 1 : (encode_mfma_stages(M, D) == 3 ? 3 : 2);
+  if (D == 64) return M == 128 ? 1 : 3;
   if (D == 16) return M >= 256 ? 2 : (M == 128 ? 4 : 8);   // 16 KB rings, up to 16 waves of <=128 VGPRs
   return M >= 128 ? 1 : 2;
 }
 
-// Software-pipelined variant (scores of the next tile during this tile's
-// weights) for head dim 64: a tuning option, chosen with FLARE_ENCODE_PIPE.
-template <int NW, int S, int G, bool RS = true>
-static hipError_t launch_d64(const EncodeArgs& a, hipStream_t s, bool pipe) {
-  return pipe ? launch_mfma_t<64, NW, S, G, 1, RS>(a, s) : launch_mfma_t<64, NW, S, G, 0>(a, s);
-}
-
 // The two-tile pipelined encoder serves bf16 inputs without a padding mask at
-// head dim 64: 128 latent rows as two 4-wave groups with 64-token tiles, 64
-// rows as four 2-wave groups with 32-token tiles (8 waves and 128 KB of
-// four-stage rings either way, one workgroup per CU); FLARE_ENCODE_ILV=0
-// selects encode_mfma_kernel instead (for comparison).
+// head dims 64 and 16: 128 latent rows as two 4-wave groups with 64-token
+// tiles, 64 rows as four 2-wave groups (32-token tiles at head dim 64) --
+// 8 waves and four-stage rings either way, one workgroup per CU.
 bool encode_ilv_used(int M, int D, bool masked) {
-  const char* e = getenv("FLARE_ENCODE_ILV");
-  if (e && atoi(e) == 0) return false;
   return (D == 64 || D == 16) && (M == 128 || M == 64) && !masked;
 }
 
@@ -950,29 +886,14 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.D == 64) {
-    const bool s3 = encode_mfma_stages(a.M, a.D) == 3;
-    const bool pipe = getenv("FLARE_ENCODE_PIPE") != nullptr;
     switch (a.M) {
-      case 32: return s3 ? launch_d64<1, 3, 1>(a, s, pipe) : launch_d64<1, 4, 1>(a, s, pipe);
-      case 64:
-        if (encode_mfma_groups(a.M, a.D) == 3) return launch_d64<2, 3, 3>(a, s, pipe);
-        return s3 ? launch_d64<2, 3, 1>(a, s, pipe) : launch_d64<2, 4, 1>(a, s, pipe);
-      case 128:
-        switch (encode_mfma_groups(a.M, a.D)) {
-          case 3:   // registers: two score tiles only with the row sum on the vector ALUs
-            return launch_d64<4, 3, 3, false>(a, s, pipe);
-          case 2:
-            switch (encode_mfma_stages(a.M, a.D)) {
-              case 5: return launch_d64<4, 5, 2>(a, s, pipe);
-              case 4: return launch_d64<4, 4, 2>(a, s, pipe);
-              default: return launch_d64<4, 3, 2>(a, s, pipe);
-            }
-          default: return s3 ? launch_d64<4, 3, 1>(a, s, pipe) : launch_d64<4, 4, 1>(a, s, pipe);
-        }
-      case 256: return s3 ? launch_d64<8, 3, 1>(a, s, pipe) : launch_d64<8, 4, 1>(a, s, pipe);
+      case 32: return launch_mfma_t<64, 1, 3, 1>(a, s);
+      case 64: return launch_mfma_t<64, 2, 3, 1>(a, s);
+      case 128: return launch_mfma_t<64, 4, 3, 3>(a, s);
+      case 256: return launch_mfma_t<64, 8, 3, 1>(a, s);
     }
   } else if (a.D == 16) {
-    // padding masks at head dim 16 (the pipelined encoder takes the rest): 2 KB tiles, 4-stage rings
+    // padding masks at head dim 16 (the pipelined encoder takes the rest)
     switch (a.M) {
       case 32: return launch_mfma_t<16, 1, 4, 1>(a, s);
       case 64: return launch_mfma_t<16, 2, 4, 1>(a, s);
@@ -984,9 +905,7 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
       case 32: return launch_mfma_t<128, 1, 3, 1>(a, s);
       case 64: return launch_mfma_t<128, 2, 3, 1>(a, s);
       case 128: return launch_mfma_t<128, 4, 4, 1>(a, s);
-      case 256:
-        return getenv("FLARE_ENCODE_VSUM") ? launch_mfma_t<128, 8, 4, 1, 0, false>(a, s)
-                                           : launch_mfma_t<128, 8, 4, 1>(a, s);
+      case 256: return launch_mfma_t<128, 8, 4, 1>(a, s);
     }
   }
   return hipErrorInvalidValue;

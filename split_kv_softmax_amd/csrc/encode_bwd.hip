@@ -35,6 +35,11 @@ template <typename TIn>
 __device__ __forceinline__ void stg_(TIn* p, float v) {
   if constexpr (sizeof(TIn) == 2) *p = to_bf16(v); else *p = v;
 }
+// v as stored in TIn, widened back (the identity for float)
+template <typename TIn>
+__device__ __forceinline__ float rnd_(float v) {
+  if constexpr (sizeof(TIn) == 2) return bf16_to_f32(to_bf16(v)); else return v;
+}
 
 // ---------------------------------------------------------------------------
 // General vector kernels (float32 inputs, or shapes without a matrix-core
@@ -92,16 +97,17 @@ __global__ __launch_bounds__(256) void bwd_kv_generic_kernel(const BwdArgs a) {
       }
     }
   }
-  // an accumulating call adds exactly the gradient a writing call stores (the
-  // product is rounded before the add, never contracted into it)
+  // an accumulating call adds exactly the gradient a writing call stores: the
+  // product is rounded to float (never contracted into the add) and then to the
+  // output type before the add
 #pragma unroll
   for (int j = 0; j < MAXDL; ++j) {
     const int d = lane + 64 * j;
     if (d < D) {
 #pragma clang fp contract(off)
       const float gk = a.scale * ak[j];
-      stg_(dv + d, a.accumulate_dv ? av[j] + ldg_(dv + d) : av[j]);
-      stg_(dk + d, a.accumulate_dk ? gk + ldg_(dk + d) : gk);
+      stg_(dv + d, a.accumulate_dv ? rnd_<TIn>(av[j]) + ldg_(dv + d) : av[j]);
+      stg_(dk + d, a.accumulate_dk ? rnd_<TIn>(gk) + ldg_(dk + d) : gk);
     }
   }
 }
@@ -845,42 +851,37 @@ static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool DQ>
-static hipError_t launch_kv_dq(const BwdArgs& a, hipStream_t s) {
-  if (a.D == 16) {
-    switch (a.M) {
-      case 32: return launch_kv_t<16, 32, 4, 3, DQ>(a, s);
-      case 64: return launch_kv_t<16, 64, 4, 3, DQ>(a, s);
-      case 128: return launch_kv_t<16, 128, 4, 3, DQ>(a, s);
-    }
-  } else if (a.D == 64) {
-    switch (a.M) {
-      case 32: return launch_kv_t<64, 32, 4, 3, DQ>(a, s);
-      case 64: return launch_kv_t<64, 64, 4, 3, DQ>(a, s);
-      case 128: return launch_kv_t<64, 128, 4, 3, DQ>(a, s);
-      case 256: return launch_kv_t<64, 256, 8, 3, DQ>(a, s);
-    }
-  } else if (a.D == 128) {
-    switch (a.M) {
-      case 32: return launch_kv_t<128, 32, 4, 3, DQ>(a, s);
-      case 64: return launch_kv_t<128, 64, 4, 3, DQ>(a, s);
-      case 128: return launch_kv_t<128, 128, 4, 3, DQ>(a, s);
-      case 256:   // no fused query gradient here (bwd_kv_fuses_dq): it would not fit the registers
-        if constexpr (!DQ) return launch_kv_t<128, 256, 8, 2, false>(a, s);
-        break;
-    }
-  }
-  return hipErrorInvalidValue;
-}
-
 bool bwd_kv_fuses_dq(int M, int D) { return !(M == 256 && D == 128); }
 
 // D=64 with M<=128: 4 waves of <=248 VGPRs and <=80 KB of LDS, so two per CU;
 // the other shapes need more than half the LDS or all 256 VGPRs per lane
 int bwd_kv_blocks_per_cu(int M, int D) { return (D == 64 || D == 16) && M <= 128 ? 2 : 1; }
 
-hipError_t launch_bwd_kv_mfma(const BwdArgs& a, bool with_dq, hipStream_t s) {
-  return with_dq ? launch_kv_dq<true>(a, s) : launch_kv_dq<false>(a, s);
+// Every shape fuses the query gradient into the key/value kernel except
+// M=256, D=128, which would not fit the registers (bwd_kv_fuses_dq).
+hipError_t launch_bwd_kv_mfma(const BwdArgs& a, hipStream_t s) {
+  if (a.D == 16) {
+    switch (a.M) {
+      case 32: return launch_kv_t<16, 32, 4, 3, true>(a, s);
+      case 64: return launch_kv_t<16, 64, 4, 3, true>(a, s);
+      case 128: return launch_kv_t<16, 128, 4, 3, true>(a, s);
+    }
+  } else if (a.D == 64) {
+    switch (a.M) {
+      case 32: return launch_kv_t<64, 32, 4, 3, true>(a, s);
+      case 64: return launch_kv_t<64, 64, 4, 3, true>(a, s);
+      case 128: return launch_kv_t<64, 128, 4, 3, true>(a, s);
+      case 256: return launch_kv_t<64, 256, 8, 3, true>(a, s);
+    }
+  } else if (a.D == 128) {
+    switch (a.M) {
+      case 32: return launch_kv_t<128, 32, 4, 3, true>(a, s);
+      case 64: return launch_kv_t<128, 64, 4, 3, true>(a, s);
+      case 128: return launch_kv_t<128, 128, 4, 3, true>(a, s);
+      case 256: return launch_kv_t<128, 256, 8, 2, false>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, bool accumulate,

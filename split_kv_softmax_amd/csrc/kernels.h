@@ -168,13 +168,14 @@ hipError_t launch_bwd_rowdot(const void* dZ, bool bf16, const float* Z, int64_t 
 hipError_t launch_bwd_generic(const BwdArgs& a, bool bf16, hipStream_t s);
 bool bwd_mfma_supported(int M, int D);
 hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s);
-// key/value gradients on matrix cores; with_dq also writes the query-gradient
-// chunk partials (only where bwd_kv_fuses_dq says the registers allow it)
+// whether the key/value gradient kernel of this shape also writes the
+// query-gradient chunk partials (where the registers allow it); where it does
+// not, launch_bwd_dq_mfma runs first
 bool bwd_kv_fuses_dq(int M, int D);
 // workgroups of the key/value gradient kernel one CU holds at once (its
 // registers and LDS), which sizes the token chunks of the backward
 int bwd_kv_blocks_per_cu(int M, int D);
-hipError_t launch_bwd_kv_mfma(const BwdArgs& a, bool with_dq, hipStream_t s);
+hipError_t launch_bwd_kv_mfma(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_reduce(const float* ws, int nslots, int64_t elems, float scale, float* dQ, bool accumulate,
                                 void* dQ_cast, hipStream_t s);
 hipError_t launch_bwd_kv_generic(const BwdArgs& a, bool bf16, hipStream_t s);

@@ -41,9 +41,9 @@ def _check_decode(Xq, Kl, Z, dY, tm, scale, fp32=False, with_cast=False):
     torch.cuda.synchronize()
     g = ref.decode_bwd_ref(Xq, Kl, Z, scale, dY, token_mask=tm)
     if fp32:
-        compare(dX, g["dXq"], "dXq", 2e-5)
-        compare(dK, g["dKlat"], "dKlat", 2e-5)
-        compare(dZ, g["dZ"], "dZ", 2e-5)
+        compare(dX, g["dXq"], "dXq", 1e-5)
+        compare(dK, g["dKlat"], "dKlat", 1e-5)
+        compare(dZ, g["dZ"], "dZ", 1e-5)
     else:
         compare_bf16(dX, g["dXq"], "dXq")
         compare_bf16(dK, g["dKlat"], "dKlat")
@@ -121,19 +121,30 @@ def test_flarepp_backward_chain_small():
     compare_bf16(g["dQX"], r["dQX"], "dQX")
     for k in ("dQt", "dKt", "dVt", "dK", "dV"):
         compare_bf16(g[k], r[k], k)
+    # the plain chain (Q(X) kept in float64) at the same bf16 bounds
+    p = ref.flarepp_bwd_ref(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale, dY)
+    for k in ("dQX", "dQt", "dKt", "dVt", "dK", "dV"):
+        compare_bf16(g[k], p[k], k + " plain")
 
 
-@pytest.mark.parametrize("M,D,masked", [(128, 64, False), (64, 64, True), (256, 128, True), (16, 32, False)])
-def test_encoder_backward_accumulate_dv(M, D, masked):
-    """ACCUMULATE_DK | ACCUMULATE_DV add the gradient to what dK and dV hold (bf16 sums of
-    the same bf16 gradient, so bit for bit); rows of masked tokens keep their old values."""
+_BWD_SHAPES = [(32, 64, True), (64, 64, True), (128, 64, False), (256, 64, True), (32, 128, False),
+               (64, 128, True), (128, 128, True), (256, 128, True), (32, 16, False), (64, 16, True),
+               (128, 16, True), (16, 32, False), (16, 64, True)]
+
+
+@pytest.mark.parametrize("M,D,masked", _BWD_SHAPES)
+def test_encoder_backward_accumulate_flags_every_shape(M, D, masked):
+    """ACCUMULATE_DK, ACCUMULATE_DV and both add the gradient to what dK and dV hold
+    (bf16 sums of the same bf16 gradient, so bit for bit), on every matrix-core shape of
+    the key/value kernel and on the vector path; rows of masked tokens keep their old
+    values, and the gradient not accumulated is written as without flags."""
     B, H, N = 2, 2, 2600
     offsets = [0, 900, 900, 2000, 2600]
-    dt = torch.bfloat16 if D >= 64 else torch.float32
-    Q = W.normal((H, M, D), 1410 + M, W.T_Q, D ** -0.5, dt, DEV)
-    K = W.normal((B, H, N, D), 1410 + M, W.T_K, 1.0, dt, DEV)
-    V = W.normal((B, H, N, D), 1410 + M, W.T_V, 1.0, dt, DEV)
-    dZ = W.normal((B, H, M, D), 1410 + M, W.T_DZ, 1.0, dt, DEV)
+    dt = torch.bfloat16 if D != 32 else torch.float32
+    Q = W.normal((H, M, D), 1410 + M + D, W.T_Q, D ** -0.5, dt, DEV)
+    K = W.normal((B, H, N, D), 1410 + M + D, W.T_K, 1.0, dt, DEV)
+    V = W.normal((B, H, N, D), 1410 + M + D, W.T_V, 1.0, dt, DEV)
+    dZ = W.normal((B, H, M, D), 1410 + M + D, W.T_DZ, 1.0, dt, DEV)
     mask = None
     if masked:
         g = np.random.default_rng(M + D)
@@ -143,22 +154,32 @@ def test_encoder_backward_accumulate_dv(M, D, masked):
     scale = fl.scale_for(D)
     O, Lp = fl.encode(Q, K, V, offsets, mask, scale)
     Z, L, _ = fl.lse_merge(O, Lp)
-    _, dK0, dV0 = fl.encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ)
+    dQ0, dK0, dV0 = fl.encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ)
+    torch.cuda.synchronize()
+    e = ref.encode_ref(Q, K, V, offsets, mask, scale)
+    gr = ref.encode_bwd_ref(Q, K, V, mask, scale, e["Z"], e["L"], dZ)
+    if dt == torch.float32:
+        for k, t in (("dQ", dQ0), ("dK", dK0), ("dV", dV0)):
+            compare(t, gr[k], k, 1e-5)
+    else:
+        for k, t in (("dQ", dQ0), ("dK", dK0), ("dV", dV0)):
+            compare_bf16(t, gr[k], k)
     prevK = torch.randn_like(dK0.float()).to(dt)
     prevV = torch.randn_like(dV0.float()).to(dt)
-    dK, dV = prevK.clone(), prevV.clone()
-    fl.encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dK=dK, dV=dV, flags=fl.ACCUMULATE_DK | fl.ACCUMULATE_DV)
-    torch.cuda.synchronize()
-    assert torch.equal(dK, (prevK.float() + dK0.float()).to(dt))
-    assert torch.equal(dV, (prevV.float() + dV0.float()).to(dt))
-    if masked:
-        inv = (mask == 0)[:, None, :, None].expand_as(dK)
-        assert torch.equal(dK[inv], prevK[inv]) and torch.equal(dV[inv], prevV[inv])
-    # dV alone
-    dV2 = prevV.clone()
-    _, dK2, _ = fl.encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dV=dV2, flags=fl.ACCUMULATE_DV)
-    torch.cuda.synchronize()
-    assert torch.equal(dV2, dV) and torch.equal(dK2, dK0)
+    inv = None if mask is None else (mask == 0)[:, None, :, None].expand_as(dK0)
+    for flags in (fl.ACCUMULATE_DK, fl.ACCUMULATE_DV, fl.ACCUMULATE_DK | fl.ACCUMULATE_DV):
+        dK, dV = prevK.clone(), prevV.clone()
+        fl.encode_bwd(Q, K, V, offsets, mask, scale, Z, L, dZ, dK=dK, dV=dV, flags=flags)
+        torch.cuda.synchronize()
+        wantK = (prevK.float() + dK0.float()).to(dt) if flags & fl.ACCUMULATE_DK else dK0
+        wantV = (prevV.float() + dV0.float()).to(dt) if flags & fl.ACCUMULATE_DV else dV0
+        assert torch.equal(dK, wantK), flags
+        assert torch.equal(dV, wantV), flags
+        if inv is not None:
+            if flags & fl.ACCUMULATE_DK:
+                assert torch.equal(dK[inv], prevK[inv])
+            if flags & fl.ACCUMULATE_DV:
+                assert torch.equal(dV[inv], prevV[inv])
 
 
 def test_flarepp_shared_projection_chain_small():
@@ -178,6 +199,9 @@ def test_flarepp_shared_projection_chain_small():
     compare_bf16(g["dQX"], r["dQX"], "dQX")
     for k in ("dQt", "dK", "dV"):
         compare_bf16(g[k], r[k], k)
+    p = ref.flarepp_shared_bwd_ref(x["Qt"], K, V, w.offsets, w.scale, dY)
+    for k in ("dQX", "dQt", "dK", "dV"):
+        compare_bf16(g[k], p[k], k + " plain")
     assert g["dKt"] is g["dK"] and g["dVt"] is g["dV"]
 
 
@@ -191,14 +215,15 @@ def test_flarepp_backward_chain_head_dim_16(shared):
     fwd = fl.flarepp_forward(x["Qt"], Kt, Vt, x["K"], x["V"], w.offsets, w.scale)
     g = fl.flarepp_backward(fwd, x["Qt"], Kt, Vt, x["K"], x["V"], w.offsets, dY, w.scale)
     torch.cuda.synchronize()
-    if shared:
-        r = ref.flarepp_shared_bwd_ref(x["Qt"], x["K"], x["V"], w.offsets, w.scale, dY, round_qx_bf16=True)
-        names = ("dQt", "dK", "dV")
-    else:
-        r = ref.flarepp_bwd_ref(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale, dY,
-                                round_qx_bf16=True)
-        names = ("dQt", "dKt", "dVt", "dK", "dV")
-    compare_bf16(g["dQX"], r["dQX"], "dQX")
-    for k in names:
-        compare_bf16(g[k], r[k], k)
+    for rnd in (True, False):     # as executed, then the plain chain, at the same bf16 bounds
+        if shared:
+            r = ref.flarepp_shared_bwd_ref(x["Qt"], x["K"], x["V"], w.offsets, w.scale, dY, round_qx_bf16=rnd)
+            names = ("dQt", "dK", "dV")
+        else:
+            r = ref.flarepp_bwd_ref(x["Qt"], x["Kt"], x["Vt"], x["K"], x["V"], w.offsets, w.scale, dY,
+                                    round_qx_bf16=rnd)
+            names = ("dQt", "dKt", "dVt", "dK", "dV")
+        compare_bf16(g["dQX"], r["dQX"], f"dQX round={rnd}")
+        for k in names:
+            compare_bf16(g[k], r[k], f"{k} round={rnd}")
 
