@@ -65,8 +65,8 @@ def test_fp32_small_encoder_workload():
     _check_encode(w, x, fp32=True)
 
 
-@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64), (64, 128), (128, 128), (256, 128),
-                                 (32, 16), (64, 16), (128, 16), (256, 16)])
+@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64), (32, 128), (64, 128), (128, 128),
+                                 (256, 128), (32, 16), (64, 16), (128, 16), (256, 16)])
 @pytest.mark.parametrize("masked", [False, True])
 def test_bf16_encoder_matrix_core(M, D, masked):
     # head dim 16 at 64 or 128 latent rows without a mask takes the pipelined encoder
@@ -133,7 +133,7 @@ def test_decode_nan_token_stays_in_its_row():
     compare_bf16(Y, ref_y, "Y")
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128])
 def test_single_query_split_kv(D):
     w, x = _enc_case(1, D, N=5000, R=7, B=2, H=3, q_per_batch=True)
     _check_encode(w, x)
@@ -145,14 +145,40 @@ def test_generic_vector_path_bf16():
     _check_encode(w, x)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,D", [(5, 128), (5, 256), (7, 64), (3, 32)])
+@pytest.mark.parametrize("masked", [False, True])
+def test_vector_path_wide_heads_and_partial_row_groups(M, D, dtype, masked):
+    """The vector encoder at head dims above 64 (32- and 16-token tiles, several lanes per
+    head dim) and M not a multiple of 4 (inactive waves), ragged partitions with an empty
+    one, masked and not; float32 to max-abs 1e-5, bfloat16 to the bf16 bounds."""
+    w, x = _enc_case(M, D, N=1100, R=4, dtype=dtype, masked=masked, wid=700)
+    _check_encode(w, x, fp32=dtype == "f32")
+
+
+def test_nan_padding_never_leaks_vector_path():
+    """NaN keys and Inf values in padded slots, float32 through the vector encoder: the states
+    are bitwise those of clean padding (padded rows are zero rows in the staged tile)."""
+    w, x = _enc_case(16, 32, N=1500, R=4, dtype="f32", masked=True, wid=710)
+    inv = (x["mask"] == 0)[:, None, :, None].expand_as(x["K"])
+    K2 = x["K"].masked_fill(inv, float("nan"))
+    V2 = x["V"].masked_fill(inv, float("inf"))
+    a = fl.encode(x["Q"], x["K"], x["V"], w.offsets, x["mask"], w.scale)
+    b = fl.encode(x["Q"], K2, V2, w.offsets, x["mask"], w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert not torch.isnan(b[0]).any()
+    _check_encode(w, x, fp32=True)
+
+
 def test_fp32_generic_larger():
     w, x = _enc_case(24, 32, N=1500, R=4, dtype="f32", masked=True)
     _check_encode(w, x, fp32=True)
 
 
 # ------------------------------------------------------------------- decode
-@pytest.mark.parametrize("M,D", [(64, 64), (128, 64), (64, 128), (256, 128), (32, 16), (64, 16), (128, 16),
-                                 (256, 16)])
+@pytest.mark.parametrize("M,D", [(32, 64), (64, 64), (128, 64), (256, 64), (32, 128), (64, 128), (128, 128),
+                                 (256, 128), (32, 16), (64, 16), (128, 16), (256, 16)])
 def test_decode_matrix_core(M, D):
     B, H, N = 2, 2, 1000
     Xq = W.normal((B, H, N, D), 600 + M, W.T_K, 1.0, torch.bfloat16, DEV)
@@ -278,7 +304,7 @@ def test_runs_are_bitwise_deterministic():
 
 
 # ------------------------------------------------------------ spike tests
-def _spike_inputs(B, H, N, M, D, spikes, device=DEV):
+def _spike_inputs(B, H, N, M, D, spikes, device=DEV, dtype=torch.bfloat16):
     """Q[m] = a e_{m mod D}; K[n*] = a e_j for each (n*, j) spike, 0 elsewhere;
     V rows carry (n mod 256, n // 256 mod 256, h, b) as bf16-exact integers."""
     a = 32.0 if D <= 64 else 64.0
@@ -294,7 +320,7 @@ def _spike_inputs(B, H, N, M, D, spikes, device=DEV):
     V[..., 1] = ((n_idx // 256) % 256)[None, None]
     V[..., 2] = torch.arange(H, dtype=torch.float32)[None, :, None]
     V[..., 3] = torch.arange(B, dtype=torch.float32)[:, None, None]
-    return (Q.to(torch.bfloat16).to(device), K.to(torch.bfloat16).to(device), V.to(torch.bfloat16).to(device))
+    return (Q.to(dtype).to(device), K.to(dtype).to(device), V.to(dtype).to(device))
 
 
 @pytest.mark.parametrize("M,D", [(64, 64), (128, 64), (256, 128), (1, 128), (64, 16), (128, 16)])
@@ -335,6 +361,38 @@ def test_spike_index_handling_is_bit_exact(M, D):
             if j >= min(M, D):
                 continue
             assert torch.equal(Yc[:, :, n_star], Zc[:, :, j]), (j, n_star)
+
+
+@pytest.mark.parametrize("M", [16, 5])
+def test_spike_index_handling_fp32_vector_path(M):
+    """The float32 small-encoder shape (partitions 300/200/424/100, vector kernel with its
+    64-token tiles and 128-token chunks): spikes at partition edges and tile tails give
+    O_r[m] = V[n*] and Z[m] = V[n*] bit for bit, L_r = s a^2 to 2 ulp, and the spike of a
+    masked slot is ignored.  M = 5 leaves inactive waves in the last group of four rows."""
+    B, H, N, D = 1, 1, 1024, 32
+    offs = [0, 300, 500, 924, 1024]
+    positions = [0, 63, 64, 127, 128, 299, 300, 499, 500, 923, 924, 1023]
+    spikes = list(zip(positions, range(len(positions))))
+    Q, K, V = _spike_inputs(B, H, N, M, D, spikes + [(700, 0)], dtype=torch.float32)
+    Q = Q.unsqueeze(0).contiguous()          # the small encoder's Q is per batch
+    mask = torch.ones(B, N, dtype=torch.uint8, device=DEV)
+    mask[:, 700] = 0                          # a padded decoy in direction 0
+    s = float(np.float32(D ** -0.5))
+    O_part, L_part = fl.encode(Q, K, V, offs, mask, s)
+    Z, L, _ = fl.lse_merge(O_part, L_part)
+    torch.cuda.synchronize()
+    Vc = V.cpu()
+    want_L = float(np.float32(s) * np.float32(32.0 * 32.0))
+    for m in range(min(M, len(positions))):
+        n_star = positions[m]
+        r_star = max(r for r in range(len(offs) - 1) if offs[r] <= n_star < offs[r + 1])
+        assert torch.equal(O_part[r_star, :, :, m].cpu(), Vc[:, :, n_star]), (m, n_star)
+        assert torch.equal(Z[:, :, m].cpu(), Vc[:, :, n_star]), (m, n_star)
+        assert abs(float(L_part[r_star, 0, 0, m]) - want_L) <= 2 * np.spacing(np.float32(want_L)), m
+        for r in range(len(offs) - 1):
+            if r != r_star:
+                # no spike of its direction here: every score is 0, O is the partition's mean of V
+                assert float(L_part[r, 0, 0, m]) < 10.0
 
 
 def test_uniform_scores_give_mean_of_v_on_gpu():

@@ -209,6 +209,13 @@ def test_full_flarepp_backward_chain():
         compare_bf16(g["dQX"][:, h:h + 1], r["dQX"], f"dQX[h={h}]")
         for k in ("dQt", "dKt", "dVt", "dK", "dV"):
             compare_bf16(g[k][:, h:h + 1], r[k], f"{k}[h={h}]")
+    # the plain chain (Q(X) kept in float64) on one head, at the same bf16 bounds
+    h = 3
+    xs = {k: v[:, h:h + 1].cpu() if v.dim() == 4 else v[h:h + 1].cpu() for k, v in x.items()}
+    p = ref.flarepp_bwd_ref(xs["Qt"], xs["Kt"], xs["Vt"], xs["K"], xs["V"], w.offsets, w.scale,
+                            dY[:, h:h + 1].cpu())
+    for k in ("dQX", "dQt", "dKt", "dVt", "dK", "dV"):
+        compare_bf16(g[k][:, h:h + 1], p[k], f"{k}[h={h}] plain")
 
 
 def test_full_flarepp_backward_chain_head_dim_16():
@@ -230,4 +237,8 @@ def test_full_flarepp_backward_chain_head_dim_16():
     compare_bf16(g["dQX"][:, h:h + 1], r["dQX"], f"dQX[h={h}]")
     for k in ("dQt", "dKt", "dVt", "dK", "dV"):
         compare_bf16(g[k][:, h:h + 1], r[k], f"{k}[h={h}]")
+    p = ref.flarepp_bwd_ref(xs["Qt"], xs["Kt"], xs["Vt"], xs["K"], xs["V"], w.offsets, w.scale,
+                            dY[:, h:h + 1].cpu())
+    for k in ("dQX", "dQt", "dKt", "dVt", "dK", "dV"):
+        compare_bf16(g[k][:, h:h + 1], p[k], f"{k}[h={h}] plain")
 
