@@ -1,15 +1,17 @@
 """Throughput of the split-KV / FLARE softmax hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--cpu-seconds S]
-                    [--backward] [--shared] [--fused] [--graph]
+                    [--backward] [--shared] [--fused] [--graph] [--flush-mall]
 
 A step is one pass of the whole path over one batch of synthetic input that
 already sits in HBM.  For the default workload (FLARE++, B=1, H=16, N=262144,
 M=128, D=64, R=16, bf16) that is: encoder 1 over (Q~, K~, V~) -> merge ->
 encoder 2 over (Q(X), K, V) -> merge -> decode of every token.  The line
-printed is one JSON object: tokens/s (B*N*H per step), the roofline of the
-dominant kernel (the encoder: achieved algorithmic HBM bytes per launch over
-its event-timed duration) and the CPU oracle timed on a bounded sample.
+printed is one JSON object: tokens/s (B*N*H per step; mean, median and
+minimum step times), the roofline of the binding kernel (of the encoder and
+the decode, the one furthest below the HBM roofline: achieved algorithmic HBM
+bytes per launch over its event-timed duration), the step-level fraction of
+the roofline, and the CPU oracle timed on a bounded sample.
 
 Only one GPU is used; --gpus above 1 is refused.
 """
@@ -18,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -33,7 +36,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
 COUNTERS = os.path.join(HERE, "profiles", "encode_flarepp_N262144_hbm_counters.md")
 ENCODER_SOURCES = [os.path.join(HERE, "split_kv_softmax_amd", "csrc", f)
-                   for f in ("encode.hip", "common.h", "kernels.h")]
+                   for f in ("encode.hip", "decode.hip", "common.h", "kernels.h")]
 
 
 def encoder_source_hash() -> str:
@@ -44,9 +47,9 @@ def encoder_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per encoder launch from the committed counter summary, or None
-    when the encoder sources changed since the counters were taken."""
+def measured_traffic(kernel="encoder"):
+    """HBM bytes per launch of the FLARE++ encoder or decode from the committed counter
+    summary, or None when the encoder/decode sources changed since the counters were taken."""
     try:
         txt = open(COUNTERS).read()
         blk = txt.split("```json", 1)[1].split("```", 1)[0]
@@ -55,7 +58,7 @@ def measured_traffic():
         return None
     if d.get("source_hash") != encoder_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("hbm_bytes_per_launch" if kernel == "encoder" else "decode_hbm_bytes_per_launch")
 
 
 def _ev():
@@ -226,42 +229,58 @@ def cpu_baseline(w: W.Workload, x, budget_s: float, shared: bool = False):
     what = {"flarepp": "FLARE++ chain (2 encoders + decode)", "flare": "FLARE block (encode + decode)",
             "encode_bwd": "masked encoder forward + backward", "splitkv": "split-KV encoder + merge",
             "encode": "encoder + merge"}[w.kind]
-    return {"value": w.N * done / spent, "unit": "tokens/s", "cores": int(_oracle_cores()), "kind": "oracle",
+    return {"value": w.N * done / spent, "unit": "tokens/s", "cores": int(_oracle_cores()), "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": f"{what} on {done} of {w.B * w.H} (batch, head) slices, full N={w.N} each; "
                       f"{spent:.2f} s wall"}
 
 
-def roofline_of(w: W.Workload, x, step, ph):
-    """Dominant kernel's algorithmic bytes per launch over its event-timed duration."""
+def roofline_candidates(w: W.Workload, x, step, ph):
+    """(kernel name, ms per launch, algorithmic bytes per launch, measured HBM bytes or None) of
+    each kernel that can bind the step; the caller reports the one furthest below the roofline."""
     kvb = 2 if w.dtype == "bf16" else 4
     row = w.D * kvb                               # bytes of one K, V, Y, dK or dV row
     rows = w.B * w.H * w.N
+    main = w.name == W.FLAREPP.name
     if w.kind == "flarepp" and "encode2_bwd" in ph:
         # physical-value encoder backward: K, V read, dV written, dK read and written (it adds into the
         # decoder's key gradient); query-synthesis encoder backward: Kt, Vt read, dKt, dVt written, or
         # with shared projections K, V read and dK, dV read and written (it adds into both)
         ms = 0.5 * (ph["encode2_bwd"] + ph["encode1_bwd"])
         enc1_rows = 6 if getattr(step, "shared", False) else 4
-        return ms, (5 + enc1_rows) * rows * row // 2, ("flare_encode_bwd call (row term, key/value-gradient kernel "
-                                                       "with fused query gradient, reduce); both encoder backwards "
-                                                       "averaged")
-    if w.kind == "flarepp" and "encode_merge1" in ph:
-        ms = 0.5 * (ph["encode_merge1"] + ph["encode_merge2"])
-        return ms, 2 * rows * row, ("encode_ilv_kernel with the merge inside (flare_encode_merge, one launch; "
-                                    "both encoders averaged)")
+        return [("flare_encode_bwd call (row term, key/value-gradient kernel with fused query gradient, reduce); "
+                 "both encoder backwards averaged", ms, (5 + enc1_rows) * rows * row // 2, None)]
     if w.kind == "flarepp":
-        ms = 0.5 * (ph["encode1"] + ph["encode2"])
-        return ms, 2 * rows * row, "encode_ilv_kernel (flare_encode, one launch; both encoders averaged)"
+        if "encode_merge1" in ph:
+            enc = ("encode_ilv_kernel with the merge inside (flare_encode_merge, one launch; both encoders "
+                   "averaged)", 0.5 * (ph["encode_merge1"] + ph["encode_merge2"]), 2 * rows * row, None)
+        else:
+            enc = ("encode_ilv_kernel (flare_encode, one launch; both encoders averaged)",
+                   0.5 * (ph["encode1"] + ph["encode2"]), 2 * rows * row,
+                   measured_traffic("encoder") if main else None)
+        dec = ("decode_mfma_kernel (flare_decode, one launch)", ph["decode"], 2 * rows * row,
+               measured_traffic("decode") if main else None)
+        return [enc, dec]
     if w.kind == "flare":
         enc = ph.get("encode", ph.get("encode_merge"))
-        if ph["decode"] > enc:
-            return ph["decode"], 2 * rows * row, "decode_mfma_kernel (flare_decode, one launch)"
-        return enc, 2 * rows * row, "encode_mfma_kernel (flare_encode, one launch)"
+        return [("encode_mfma_kernel (flare_encode, one launch)", enc, 2 * rows * row, None),
+                ("decode_mfma_kernel (flare_decode, one launch)", ph["decode"], 2 * rows * row, None)]
     if w.kind == "encode_bwd":
         valid = int(x["mask"].sum().item()) * w.H if "mask" in x else rows
-        return (ph["backward"], 2 * valid * row + 2 * rows * row,
-                "flare_encode_bwd call (row term, query-gradient, key/value-gradient and reduce kernels)")
-    return ph.get("encode", ph.get("encode_merge")), 2 * rows * row, "flare_encode call (one encoder launch)"
+        return [("flare_encode_bwd call (row term, query-gradient, key/value-gradient and reduce kernels)",
+                 ph["backward"], 2 * valid * row + 2 * rows * row, None)]
+    return [("flare_encode call (one encoder launch)", ph.get("encode", ph.get("encode_merge")), 2 * rows * row,
+             None)]
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_reference(nbytes=1 << 30, reps=5):
@@ -342,6 +361,9 @@ def main():
     ap.add_argument("--shared", action="store_true",
                     help="FLARE++ only: the shared-projection variant (the query-synthesis encoder reads K and V; "
                          "with --backward its key and value gradients add into dK and dV)")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="in the per-phase pass (after the timed region), write a 512 MiB scratch buffer "
+                         "before every step so that no input is served from the 256 MB last-level cache")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device 3 times "
                          "(the plain copy that scales the HBM byte counters)")
@@ -384,26 +406,40 @@ def main():
         run()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronised on both sides
+    # timed region: exactly K steps, synchronised on both sides; an event after
+    # every step gives the per-step durations (median, minimum) without a sync
     t_start, t_end = _ev(), _ev()
+    step_ev = [_ev() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start.record()
     wall0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         run()
+        step_ev[i].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
+    per_step = [t_start.elapsed_time(step_ev[0])] + [step_ev[i - 1].elapsed_time(step_ev[i])
+                                                    for i in range(1, args.steps)]
 
     # per-kernel durations from events on the launch stream: a separate pass of
-    # the same back-to-back steps, synchronised only at its end
+    # the same back-to-back steps, synchronised only at its end (with
+    # --flush-mall a 512 MiB scratch write precedes every step, outside its events)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush_mall else None
     for _ in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(1)
         step(timed_phases=True)
+    torch.cuda.synchronize()
+    pass_steps = [ev[0].elapsed_time(ev[-1]) for ev in step.pending] if scratch is not None else None
     step.collect()
+    del scratch
     ph = {n: p / step.count for n, p in zip(step.names, step.phase_ms)}
-    kern_ms, kern_bytes, kern_name = roofline_of(w, x, step, ph)
+    cands = roofline_candidates(w, x, step, ph)
+    # the binding kernel: the one furthest below the HBM roofline
+    kern_name, kern_ms, kern_bytes, kern_traffic = min(cands, key=lambda c: c[2] / c[1])
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     tokens = w.B * w.N * w.H
     kvb = 2 if w.dtype == "bf16" else 4
@@ -430,17 +466,26 @@ def main():
                    **({"projections": "shared"} if args.shared else {}),
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if is_main else None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": kern_traffic,
                      "kernel": kern_name, "kernel_ms": kern_ms, "algorithmic_bytes": kern_bytes},
+        "step_ms": {"mean": ms_per_step, "median": statistics.median(per_step), "min": min(per_step)},
         "phases_ms": ph,
         "wall_s_timed": wall,
     }
+    if len(cands) > 1:
+        line["kernels"] = [{"kernel": n, "ms": ms, "algorithmic_bytes": b, "traffic": t,
+                            "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS} for n, ms, b, t in cands]
+    if pass_steps:
+        line["step_ms_mall_flushed"] = {"mean": sum(pass_steps) / len(pass_steps),
+                                        "median": statistics.median(pass_steps), "min": min(pass_steps)}
     if is_main:
         step_bytes = 6 * tokens * w.D * kvb        # 2 encoders (K,V) + decode (read K, write Y)
         line["roofline"]["source_hash"] = encoder_source_hash()
         line["step_roofline"] = {"algorithmic_bytes": step_bytes,
                                  "achieved_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
-                                 "frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                                 "frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "frac_median_step": step_bytes / (line["step_ms"]["median"] * 1e-3) / 1e9
+                                 / HBM_PEAK_GBS}
     if "mask" in x:
         line["config"]["valid_fraction"] = float(x["mask"].float().mean().item())
     line["copy_reference"] = copy_reference()
