@@ -98,6 +98,29 @@ flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D,
                           void* workspace, size_t workspace_bytes, flare_stream_t stream);
 
 /*
+ * flare_encode_noalloc -- flare_encode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, outputs, validation and results (the
+ * same kernels, bit for bit) as flare_encode without the workspace arguments:
+ * the workspace comes from a fixed array in device memory that the library
+ * holds on every device it runs on until the process ends.
+ *  - The call allocates and frees nothing and issues no memset.
+ *  - Arguments whose workspace (flare_encode_workspace_size) exceeds
+ *    FLARE_NOALLOC_SCRATCH_BYTES are rejected with FLARE_EWORKSPACE before
+ *    anything is launched.
+ *  - All calls on one device share that device's array; it carries nothing
+ *    from one call to the next that a call reads.  Two calls whose work may
+ *    overlap in time on one device (other streams, graphs replayed alongside)
+ *    race on it and must not be made.
+ *  - The first call on a device looks up the array's address (thread-safe).
+ */
+#define FLARE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+flare_status flare_encode_noalloc(flare_dtype dtype, int B, int H, int N, int M, int D,
+                                  const void* Q, int64_t q_batch_stride, const void* K, const void* V,
+                                  int R, const int64_t* offsets, const uint8_t* mask, float scale,
+                                  float* O_part, float* L_part, flare_stream_t stream);
+
+/*
  * lse_merge -- the exact cross-partition merge of [FLARE++] (eqs. 21-23 and
  * the max-stabilised merge paragraph), evaluated as the balanced binary tree
  * of [RING]: leaves are (m, l, acc) = (L_r, 1, O_r) (or (-inf, 0, 0) for an

@@ -8,6 +8,7 @@ library is missing or no GPU is present, the calls raise.
 
 Shapes (see the header for the contract):
   encode:     Q [H,M,D] or [B,H,M,D]; K, V [B,H,N,D]  ->  O_part [R,B,H,M,D], L_part [R,B,H,M]
+  encode_noalloc: encode with the library's fixed scratch instead of a workspace
   lse_merge:  O_part, L_part                          ->  Z [.., M, D], L [.., M] (+ bf16 Z)
   encode_merge: encode then lse_merge in one call     ->  O_part, L_part, Z, L (+ bf16 Z)
   decode:     Xq [B,H,N,D], Klat [H,M,D] or [B,H,M,D], Z [B,H,M,D] -> Y [B,H,N,D]
@@ -21,7 +22,7 @@ from typing import Dict, Optional, Sequence, Tuple
 
 import torch  # noqa: F401  (loaded first so the library binds to torch's HIP runtime)
 
-__all__ = ["FlareError", "encode", "lse_merge", "encode_merge", "decode", "encode_bwd", "decode_bwd", "flare_forward",
+__all__ = ["FlareError", "encode", "encode_noalloc", "lse_merge", "encode_merge", "decode", "encode_bwd", "decode_bwd", "flare_forward",
            "flarepp_forward", "flarepp_backward", "encode_workspace_size", "encode_bwd_workspace_size",
            "decode_bwd_workspace_size", "library_path", "scale_for", "ACCUMULATE_DQ", "ACCUMULATE_DK",
            "ACCUMULATE_DV", "encode_merge", "merge_counters"]
@@ -63,6 +64,9 @@ def _load():
     lib.flare_encode.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp,
                                  vp, sz, vp]
     lib.flare_encode.restype = i32
+    lib.flare_encode_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp,
+                                         vp]
+    lib.flare_encode_noalloc.restype = i32
     lib.flare_encode_merge.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp,
                                        vp, vp, vp, vp, vp, vp, sz, vp]
     lib.flare_encode_merge.restype = i32
@@ -214,6 +218,41 @@ def encode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, offsets: Sequence[
     with torch.cuda.device(dev):
         _check(lib.flare_encode(code, B, H, N, M, D, _ptr(Q), qbs, _ptr(K), _ptr(V), R, offs, _ptr(mask),
                                 float(scale), _ptr(O_part), _ptr(L_part), _ptr(ws), nbytes, _stream()))
+    return O_part, L_part
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20    # FLARE_NOALLOC_SCRATCH_BYTES
+
+
+def encode_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, offsets: Sequence[int],
+                   mask: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                   O_part: Optional[torch.Tensor] = None, L_part: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """encode through flare_encode_noalloc: the library's fixed per-device scratch in place of a
+    workspace (for callers that cannot allocate; pass O_part and L_part to allocate nothing here)."""
+    lib = _load()
+    _kv_check(K, V, Q)
+    B, H, N, D = K.shape
+    M, qbs = _q_layout(Q, B, H, D)
+    R = len(offsets) - 1
+    mask = _mask_check(mask, B, N, K.device)
+    if scale is None:
+        scale = scale_for(D)
+    dev = K.device
+    if O_part is None:
+        O_part = torch.empty((R, B, H, M, D), dtype=torch.float32, device=dev)
+    if L_part is None:
+        L_part = torch.empty((R, B, H, M), dtype=torch.float32, device=dev)
+    if tuple(O_part.shape) != (R, B, H, M, D) or tuple(L_part.shape) != (R, B, H, M):
+        raise ValueError("O_part / L_part have the wrong shape")
+    if O_part.dtype != torch.float32 or L_part.dtype != torch.float32:
+        raise TypeError("O_part / L_part must be float32")
+    _dev(O_part, "O_part")
+    _dev(L_part, "L_part")
+    with torch.cuda.device(dev):
+        _check(lib.flare_encode_noalloc(_dtype_code(K), B, H, N, M, D, _ptr(Q), qbs, _ptr(K), _ptr(V), R,
+                                        _offsets(offsets), _ptr(mask), float(scale), _ptr(O_part), _ptr(L_part),
+                                        _stream()))
     return O_part, L_part
 
 

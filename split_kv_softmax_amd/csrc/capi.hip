@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -362,9 +363,64 @@ flare_status encode_impl(flare_dtype dtype, int B, int H, int N, int M, int D, c
   return FLARE_OK;
 }
 
+// ------------------------------------------------- fixed scratch (no allocation)
+// flare_encode_noalloc takes its workspace from this array instead of a caller
+// buffer.  Each device holds its own copy for the life of the process.  Host
+// code never passes the array's name to a kernel (on the host it only stands in
+// for the symbol): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+constexpr size_t kScratchBytes = FLARE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first
+// call on that device).
+flare_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FLARE_EUNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned16(p)) return fail(FLARE_EHIP, "scratch address %p unusable", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLARE_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+flare_status flare_encode_noalloc(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
+                                  int64_t q_batch_stride, const void* K, const void* V, int R,
+                                  const int64_t* offsets, const uint8_t* mask, float scale, float* O_part,
+                                  float* L_part, flare_stream_t stream) {
+  // arguments flare_encode would reject are reported by it, unchanged
+  size_t need = 0;
+  if (check_common(dtype, B, H, N, M, D) == FLARE_OK && check_offsets(N, R, offsets) == FLARE_OK) {
+    need = plan_encode(dtype, B, H, N, M, D, R, offsets, mask != nullptr).ws_bytes;
+    if (need > kScratchBytes)
+      return fail(FLARE_EWORKSPACE,
+                  "flare_encode_noalloc: these arguments need %zu bytes of scratch, above its fixed %zu bytes "
+                  "(call flare_encode with a workspace instead)",
+                  need, kScratchBytes);
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const flare_status st = scratch_of_current_device(&ws);
+    if (st != FLARE_OK) return st;
+  }
+  return encode_impl(dtype, B, H, N, M, D, Q, q_batch_stride, K, V, R, offsets, mask, scale, O_part, L_part, ws,
+                     need > 0 ? kScratchBytes : 0, stream, nullptr);
+}
 
 flare_status flare_encode(flare_dtype dtype, int B, int H, int N, int M, int D, const void* Q,
                           int64_t q_batch_stride, const void* K, const void* V, int R,

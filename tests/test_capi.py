@@ -32,6 +32,7 @@ def lib():
     p64 = ctypes.POINTER(ctypes.c_int64)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     L.flare_encode.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp, sz, vp]
+    L.flare_encode_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, vp, vp, i32, p64, vp, f32, vp, vp, vp]
     L.flare_encode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, p64, i32]
     L.flare_encode_workspace_size.restype = sz
     L.lse_merge.argtypes = [i32, i64, i32, vp, vp, vp, vp, vp, vp]
@@ -154,3 +155,20 @@ def test_encode_merge_validates(lib):
     o = offs(0, 40000, 80000)
     n = lib.flare_encode_workspace_size(1, 1, 1, 80000, 64, 64, 2, o, 0)
     assert n > 0 and _encm(lib, o, N=80000, ws=FAKE, nbytes=n - 1) == EWS               # same workspace as encode
+
+
+def test_noalloc_encoder_rejects_workspace_beyond_its_scratch(lib):
+    """flare_encode_noalloc refuses (before any launch or HIP call) arguments whose workspace
+    exceeds its fixed scratch: one (batch, head) slice of 2^20 tokens, 256 latent rows at head
+    dim 128, split into 256 chunks whose partial states need 32 MiB; invalid arguments get
+    flare_encode's own status."""
+    N = 1 << 20
+    o = offs(0, N)
+    need = lib.flare_encode_workspace_size(1, 1, 1, N, 256, 128, 1, o, 0)
+    assert need > 16 << 20
+    st = lib.flare_encode_noalloc(1, 1, 1, N, 256, 128, FAKE, 0, FAKE, FAKE, 1, o, None, 0.088, FAKE, FAKE, None)
+    assert st == EWS
+    assert b"flare_encode_noalloc" in lib.flare_last_error() and b"scratch" in lib.flare_last_error()
+    st = lib.flare_encode_noalloc(1, 1, 1, 1024, 64, 64, FAKE, 0, FAKE, FAKE, 2, offs(0, 600, 500), None, 0.125,
+                                  FAKE, FAKE, None)
+    assert st == EINVAL and b"offsets" in lib.flare_last_error()
