@@ -64,7 +64,12 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
   constexpr int NI = BB / 1024;              // direct loads per block
   constexpr int ST = NI;                     // 1 KB row stores per block (as many as its loads)
   constexpr int MAXT = 8192;                 // tokens per workgroup (host keeps tokens_per_block <= MAXT)
+  // FOLD (head dim 16, where the score products are cheap): the latent keys
+  // are staged as the bf16 pair hi + lo of s log2(e) Klat (16 significant
+  // bits), so a weight against the zero reference is one exp2 of the product
+  constexpr bool FOLD = D == 16;
   __shared__ __attribute__((aligned(16))) uint16_t Kl[M * KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Klo[FOLD ? M * KLD : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Zt[D * ZLD];
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * S * BB];
   __shared__ uint8_t tmask[MAXT];
@@ -105,7 +110,22 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int f = tid + T * i;
-      if (f < M * D / 8) st16(&Kl[(f / (D / 8)) * KLD + 8 * (f % (D / 8))], kv[i]);
+      if (f < M * D / 8) {
+        const int off = (f / (D / 8)) * KLD + 8 * (f % (D / 8));
+        if constexpr (FOLD) {
+          u32x4_t hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float f0 = bf16lo(kv[i][e]) * a.scale_log2, f1 = bf16hi(kv[i][e]) * a.scale_log2;
+            hi[e] = pack_bf16x2(f0, f1);
+            lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
+          }
+          st16(&Kl[off], hi);
+          st16(&Klo[off], lo);
+        } else {
+          st16(&Kl[off], kv[i]);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < ZI; ++i) {
@@ -194,19 +214,27 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     // the same softmax up to the bf16 rounding of p.
     auto scores_of = [&](int mb) -> f32x16_t {
       f32x16_t t = f32x16_t{};
-      const uint16_t* krow = &Kl[(32 * mb + swap23(l32)) * KLD + 8 * hh];
+      const int ro = (32 * mb + swap23(l32)) * KLD + 8 * hh;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        t = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + 16 * ks)), xop[ks],
+      for (int ks = 0; ks < KS; ++ks) {
+        t = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&Kl[ro + 16 * ks])), xop[ks],
                          t);
+        if constexpr (FOLD)
+          t = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&Klo[ro + 16 * ks])),
+                           xop[ks], t);
+      }
       return t;
     };
-    auto weigh = [&](const f32x16_t& t, float nm, bf16x8_t* pk2) {
+    // weights exp2(s log2(e) T + nm); FOLD: the scores are already s log2(e) T
+    auto weigh = [&](const f32x16_t& t, float nm, bf16x8_t* pk2, bool shifted) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         float p[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) p[jj] = fast_exp2(__builtin_fmaf(t[8 * g + jj], c2, nm));
+        for (int jj = 0; jj < 8; ++jj) {
+          const float x = t[8 * g + jj];
+          p[jj] = fast_exp2(FOLD ? (shifted ? x + nm : x) : __builtin_fmaf(x, c2, nm));
+        }
         const u32x4_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                            pack_bf16x2(p[6], p[7])};
         pk2[g] = __builtin_bit_cast(bf16x8_t, w);
@@ -234,7 +262,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       bf16x8_t pk2[2];
-      weigh(scores_of(mb), 0.f, pk2);
+      weigh(scores_of(mb), 0.f, pk2, false);
       accumulate(2 * mb, pk2[0]);
       accumulate(2 * mb + 1, pk2[1]);
     }
@@ -256,7 +284,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmax2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-      const float nmc = -mx * c2;
+      const float nmc = FOLD ? -mx : -mx * c2;
       clear();
       f32x16_t lacc = f32x16_t{};
       const bf16x8_t ones =
@@ -264,7 +292,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         bf16x8_t pk2[2];
-        weigh(t[mb], nmc, pk2);
+        weigh(t[mb], nmc, pk2, true);
         accumulate(2 * mb, pk2[0]);
         accumulate(2 * mb + 1, pk2[1]);
         lacc = mfma32x32x16(ones, pk2[0], lacc);

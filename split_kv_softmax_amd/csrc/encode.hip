@@ -551,13 +551,37 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + (int64_t)b * a.q_bstride +
                        (int64_t)h * a.M * D;
 
-  bf16x8_t qop[KS];
+  // FOLD (head dim 16, where the score products are cheap): s log2(e) and the
+  // row's reference are folded into the score products, so a weight is one
+  // exp2 of the product's result.  Q enters as the bf16 pair hi + lo of
+  // s log2(e) Q (16 significant bits: the scores carry a relative error below
+  // 2^-16), and the accumulator starts at -R, R the row's reference in
+  // log2 units.
+  constexpr bool FOLD = D == 16;
+  const float c2 = a.scale_log2;
+  bf16x8_t qop[KS], qlo[KS];
   {
     const uint16_t* qrow = Qg + (int64_t)(32 * wave + l32) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qop[ks] = __builtin_bit_cast(bf16x8_t, ld16(qrow + 16 * ks));
   }
   wait_vm<0>();   // afterwards only the ring's loads are in flight
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t w = __builtin_bit_cast(u32x4_t, qop[ks]);
+      u32x4_t hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f0 = bf16lo(w[e]) * c2, f1 = bf16hi(w[e]) * c2;
+        const uint32_t h2 = pack_bf16x2(f0, f1);
+        hi[e] = h2;
+        lo[e] = pack_bf16x2(f0 - bf16lo(h2), f1 - bf16hi(h2));
+      }
+      qop[ks] = __builtin_bit_cast(bf16x8_t, hi);
+      qlo[ks] = __builtin_bit_cast(bf16x8_t, lo);
+    }
+  }
 
   // Local tiles 0 .. ntg-1 of this group are chunk tiles grp, grp+G, ...; only
   // the chunk's last tile can be partial.
@@ -617,7 +641,6 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   }
   typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4;
 
-  const float c2 = a.scale_log2;
   // Row sums on a 16x16x32 product: fed the weight operand of the 32x32x16
   // product as its B, lane l contributes row l%32, tokens 8*(l/32)+0..7 as
   // column l%16, contraction block l/16.  Selector rows 0 and 8 pick blocks 0
@@ -635,6 +658,8 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
 
   // scores of the tile in K slot `slot`: register r of lane half hh in block b2
   // holds token 32*b2 + 16*(r/8) + 8*hh + r%8 of latent row l32
+  // FOLD: -R of row l32 in every accumulator register (R = 0 until a rebase)
+  f32x16_t cinit = f32x16_t{};
   auto scores = [&](int slot, f32x16_t* sc) {
     u32x4_t kop[KS][NB];
 #pragma unroll
@@ -642,11 +667,14 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
 #pragma unroll
       for (int b2 = 0; b2 < NB; ++b2) kop[k][b2] = *(lds_u32x4*)(uintptr_t)(kaddr[k] + slot * TB + 32 * b2 * ROWB);
 #pragma unroll
-    for (int b2 = 0; b2 < NB; ++b2) sc[b2] = f32x16_t{};
+    for (int b2 = 0; b2 < NB; ++b2) sc[b2] = FOLD ? cinit : f32x16_t{};
 #pragma unroll
     for (int k = 0; k < KS; ++k)
 #pragma unroll
-      for (int b2 = 0; b2 < NB; ++b2) sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, kop[k][b2]), qop[k], sc[b2]);
+      for (int b2 = 0; b2 < NB; ++b2) {
+        sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, kop[k][b2]), qop[k], sc[b2]);
+        if constexpr (FOLD) sc[b2] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, kop[k][b2]), qlo[k], sc[b2]);
+      }
   };
   f32x16_t o[DB];
 #pragma unroll
@@ -698,7 +726,10 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
       for (int g = 0; g < 2; ++g) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sc[b2][8 * g + j], c2, nm));
+        for (int j = 0; j < 8; ++j) {
+          const float x = sc[b2][8 * g + j];
+          p[j] = fast_exp2(FOLD ? (own_rows_only ? x + nm : x) : __builtin_fmaf(x, c2, nm));
+        }
         const u32x4_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                            pack_bf16x2(p[6], p[7])};
         pk[2 * b2 + g] = __builtin_bit_cast(bf16x8_t, w);
@@ -720,12 +751,25 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
     return ts[0];
   };
   constexpr float kSumMax = 4096.f;
+  // FOLD keeps R at 0 from the start, so a row whose scores sit far below 0
+  // sums to almost nothing: a row sum (with this tile) below 2^-64 also
+  // sends it through the rebase.
+  constexpr float kSumMin = 0x1p-64f;
+  float rref = 0.f;          // FOLD: the reference R of row l32 (log2 units)
+  auto bad_sum = [&](float ts) -> bool {
+    if constexpr (FOLD) return !(ts <= kSumMax) || (lsum + ts < kSumMin);
+    return !(ts <= kSumMax);
+  };
   // Rare path: rows whose tile sum failed the check move their reference to
   // the tile's maximum (the online-softmax rescale of the value accumulators
   // and the row sum by exp2(s log2(e) (m_old - m_new)), 0 from an empty
   // state), then the tile's weights and sums are recomputed, the sums with
-  // each row's own weights only.
-  auto rebase = [&](const f32x16_t* sc, bf16x8_t* pk, float& ts) {
+  // each row's own weights only.  FOLD: the scores are relative to R, so the
+  // shift delta (the tile maximum, or log2 of the mass so far if that is
+  // larger) moves R, the accumulator start and the scores already formed for
+  // the next tile (sc_next); delta may be negative only while it stays at or
+  // above the mass so far.
+  auto rebase = [&](f32x16_t* sc, bf16x8_t* pk, float& ts, f32x16_t* sc_next) {
     float mc[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int k = 0; k < 2 * NB; ++k) {
@@ -741,6 +785,24 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmax2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
+    if constexpr (FOLD) {
+      const bool bad = bad_sum(ts);
+      const float d = lsum > 0.f ? fmax2(mx, __log2f(lsum)) : mx;
+      const float delta = (bad && d != kNegInf) ? d : 0.f;
+      const float alpha = delta == 0.f ? 1.f : (lsum > 0.f ? fast_exp2(-delta) : 0.f);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) o[i] *= alpha;
+      rref += delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cinit[r] -= delta;
+#pragma unroll
+      for (int b2 = 0; b2 < NB; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc_next[b2][r] -= delta;
+      ts = weights(sc, pk, -delta, true);
+      return;
+    }
     const bool bad = !(ts <= kSumMax);
     const float m_new = (bad && mx != kNegInf) ? fmax2(mx, m_run) : m_run;
     const float alpha = (m_new == m_run) ? 1.f : fast_exp2((m_run - m_new) * c2);   // 0 when m_run = -inf
@@ -751,11 +813,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
     nmc = m_run == kNegInf ? __builtin_huge_valf() : -m_run * c2;
     ts = weights(sc, pk, m_run == kNegInf ? 0.f : nmc, true);
   };
-  auto softmax_tile = [&](const f32x16_t* sc, bf16x8_t* pk) {
-    float ts = weights(sc, pk, nmc);
-    if (__ballot(!(ts <= kSumMax))) rebase(sc, pk, ts);
-    lsum += ts;
-  };
+
 
   // ---- V slots start as zeros: a round past the group's end multiplies
   // weights that are exactly 0 with whatever its slot holds, which must not
@@ -781,11 +839,12 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   // tile u+1 and the scores of tile u+2
   f32x16_t scb[2][NB];
   bf16x8_t pkb[2][NK];
+  float ts_pend;   // row sums of the weights made last round, checked at the start of the next
   {
     scores(0, scb[0]);
     scores(1, scb[1]);
     if (nval(0) < TILE) mask_tail(scb[0], nval(0));
-    softmax_tile(scb[0], pkb[0]);
+    ts_pend = weights(scb[0], pkb[0], nmc);
   }
   barrier_lds();             // every wave is done with K slots 0 and 1
   if (S < ntg) issue(S, 0, false);
@@ -805,12 +864,14 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
         if (u + S + 1 < ntg) issue(u + S + 1, (st + 1) % S, false);
         if (u + S - 1 < ntg) issue(u + S - 1, (st + S - 1) % S, true);
         const int e = sr % 2, f = 1 - e;     // tile u: buffer e; tile u+1: buffer f; tile u+2: buffer e
+        if (__ballot(bad_sum(ts_pend))) rebase(scb[e], pkb[e], ts_pend, scb[f]);
+        lsum += ts_pend;
         const int n1 = nval(u + 1);
         if (n1 < TILE) mask_tail(scb[f], n1);
         // one straight-line block: the value products of tile u, the weights
         // of tile u+1 and their row sums, the score products of tile u+2
         values(st, pkb[e]);
-        float ts = weights(scb[f], pkb[f], nmc);
+        ts_pend = weights(scb[f], pkb[f], nmc);
         scores((st + 2) % S, scb[e]);
         // order: all operand reads (V, then K), a few exponentials while they
         // arrive, then each product with exponentials and conversions between
@@ -818,16 +879,17 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * NK * DB + NB * KS, 0);
         __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
 #pragma unroll
-        for (int i = 0; i < NK * DB + NB * KS; ++i) {
+        for (int i = 0; i < NK * DB + (FOLD ? 2 : 1) * NB * KS; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
         }
-        if (__ballot(!(ts <= kSumMax))) rebase(scb[f], pkb[f], ts);
-        lsum += ts;
       }
     }
   }
 
+  // (the sums left pending belong to the tile after the group's last, which
+  // holds no token)
+  if constexpr (FOLD) m_run = lsum > 0.f ? rref / c2 : kNegInf;   // the reference in raw units
   finish_chunk<D, NW, G>(smem, a, grp, wave, lane, o, m_run, lsum, b, h, c);
   merge_tail(a, b, h, c, reinterpret_cast<int*>(smem));
 }

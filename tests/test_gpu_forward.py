@@ -74,6 +74,35 @@ def test_bf16_encoder_matrix_core(M, D, masked):
     _check_encode(w, x)
 
 
+@pytest.mark.parametrize("M,D", [(128, 16), (64, 16), (128, 64)])
+def test_far_negative_and_large_scores(M, D):
+    """Rows whose every score sits near -300 (so a weight against a zero reference underflows and
+    the row must re-base downwards), rows with score spread ~30 (re-base upwards), and ordinary
+    rows, through the unmasked pipelined encoder (head dim 16 folds the scale and the reference
+    into the score products): parity with the oracle, L within the bf16 bound."""
+    w, x = _enc_case(M, D, N=3000, R=4, wid=720)
+    Q = x["Q"].float().clone()
+    K = x["K"].float().clone()
+    c = 12.0 if D == 16 else 16.0
+    K[..., 0] = c                                   # every key has a large first coordinate
+    Q[:, : M // 4, :] = 0.0
+    Q[:, : M // 4, 0] = -c                          # rows 0..M/4-1: every score = -s c^2 (about -36..-32 s^-1)
+    Q[:, M // 4: M // 2] *= 8.0 * D ** 0.5          # rows M/4..M/2-1: wide spread
+    x["Q"] = Q.to(torch.bfloat16)
+    x["K"] = K.to(torch.bfloat16)
+    # the scale puts the first quarter's scores at about -300 (natural units)
+    sc = float(np.float32(300.0 / (c * c)))
+    O_part, L_part = fl.encode(x["Q"], x["K"], x["V"], w.offsets, None, sc)
+    Z, L, _ = fl.lse_merge(O_part, L_part)
+    torch.cuda.synchronize()
+    out = ref.encode_ref(x["Q"], x["K"], x["V"], w.offsets, None, sc)
+    compare_bf16(O_part, out["O_part"], "O_part")
+    compare_L(L_part, out["L_part"], "L_part")
+    compare_bf16(Z, out["Z"], "Z")
+    compare_L(L, out["L"], "L")
+    assert float(L[0, 0, 0]) < -250.0
+
+
 def test_bf16_encoder_stress_scores():
     """Q scaled so score spread is ~4: exercises the running-max rescale."""
     w, x = _enc_case(128, 64, N=3000, R=4, stress=4 * 8.0)
