@@ -682,9 +682,9 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   }
   e = launch_bwd_kv_mfma(a, s);
   if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
-  // the fused kernel's partials already carry s (it contracts s dS); the query-gradient kernel's do not
-  e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, fuse ? 1.f : scale, dQ, a.accumulate_dq != 0,
-                           dQ_cast, s);
+  // partials that already carry s (the fused kernel contracting s dS) are summed as they are
+  e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, bwd_kv_partials_scaled(M, D) ? 1.f : scale, dQ,
+                           a.accumulate_dq != 0, dQ_cast, s);
   if (e != hipSuccess) return hip_fail(e, "query-gradient reduce launch");
   return FLARE_OK;
 }

@@ -265,21 +265,25 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       weigh(scores_of(mb), 0.f, pk2, false);
       accumulate(2 * mb, pk2[0]);
       accumulate(2 * mb + 1, pk2[1]);
+      // 256 latents: keep the scheduler from forming every block's scores
+      // ahead of the first weights (their registers would spill)
+      if constexpr (MB >= 8) __builtin_amdgcn_sched_barrier(0);
     }
     float lsum = ls4[0];
     if (__ballot(!(lsum >= 0x1p-64f && lsum <= 0x1p64f))) {
       // exact form: the token's maximum over its M scores first.  Its row sums
       // come from ones x P on the 32x32x16 product, which only adds a token's
       // own weights (the selector form multiplies the neighbouring token's
-      // weights by 0, and 0 x NaN from a padded row would leak across).
-      f32x16_t t[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) t[mb] = scores_of(mb);
+      // weights by 0, and 0 x NaN from a padded row would leak across).  The
+      // scores are formed twice (for the maximum, then for the weights), so no
+      // block's scores are held across the other blocks' products.
       float mx = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        const f32x16_t t = scores_of(mb);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmax2(mx, t[mb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmax2(mx, t[r]);
+      }
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmax2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         bf16x8_t pk2[2];
-        weigh(t[mb], nmc, pk2, true);
+        weigh(scores_of(mb), nmc, pk2, true);
         accumulate(2 * mb, pk2[0]);
         accumulate(2 * mb + 1, pk2[1]);
         lacc = mfma32x32x16(ones, pk2[0], lacc);

@@ -235,8 +235,14 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
   constexpr int ST = NI + 2;                 // stores per block: dXq rows, log2-normaliser, delta
   // latent rows unpadded, 16-byte chunk c of row m at c ^ kv_swz(m): conflict-free
   // for the row reads of the score products and the transposing reads of dXq
+  // FOLD (head dim 16, where the score products are cheap): the scores use the
+  // bf16 pair hi + lo of s log2(e) Klat (16 significant bits), so a weight is
+  // one exp2 of the product; dXq still uses Klat itself
+  constexpr bool FOLD = D == 16;
   __shared__ __attribute__((aligned(1024))) uint8_t Kl[M * ROWB];
   __shared__ __attribute__((aligned(1024))) uint8_t Zr[M * ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t Khi[FOLD ? M * ROWB : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t Klo[FOLD ? M * ROWB : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * S * 2 * BB];
   auto lat = [](int m, int c) { return m * ROWB + ((c ^ kv_swz<D>(m)) * 16); };   // byte of chunk c, row m
 
@@ -259,7 +265,19 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
     const float* zg = a.Z + bh * (int64_t)M * D;
     for (int f = tid; f < M * D / 8; f += T) {
       const int m = f / (D / 8), c = f % (D / 8);
-      st16(Kl + lat(m, c), ld16(kg + 8 * (int64_t)f));
+      const u32x4_t kv = ld16(kg + 8 * (int64_t)f);
+      st16(Kl + lat(m, c), kv);
+      if constexpr (FOLD) {
+        u32x4_t hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f0 = bf16lo(kv[e]) * a.scale_log2, f1 = bf16hi(kv[e]) * a.scale_log2;
+          hi[e] = pack_bf16x2(f0, f1);
+          lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
+        }
+        st16(Khi + lat(m, c), hi);
+        st16(Klo + lat(m, c), lo);
+      }
       const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(zg + 8 * (int64_t)f);
       const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(zg + 8 * (int64_t)f + 4);
       st16(Zr + lat(m, c), u32x4_t{pack_bf16x2(z0[0], z0[1]), pack_bf16x2(z0[2], z0[3]), pack_bf16x2(z1[0], z1[1]),
@@ -349,8 +367,14 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
       for (int mb = 0; mb < MB; ++mb) {
         t[mb] = f32x16_t{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Kl + 32 * mb * ROWB + koff[ks])), xop[ks], t[mb]);
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (FOLD) {
+            t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Khi + 32 * mb * ROWB + koff[ks])), xop[ks], t[mb]);
+            t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Klo + 32 * mb * ROWB + koff[ks])), xop[ks], t[mb]);
+          } else {
+            t[mb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, ld16(Kl + 32 * mb * ROWB + koff[ks])), xop[ks], t[mb]);
+          }
+        }
       }
     };
     scores();
@@ -372,7 +396,7 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        t[mb][r] = fast_exp2(t[mb][r] * c2);
+        t[mb][r] = fast_exp2(FOLD ? t[mb][r] : t[mb][r] * c2);
         lsum += t[mb][r];
       }
     lsum += __shfl_xor(lsum, 32, 64);
@@ -387,13 +411,13 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmax2(mx, t[mb][r]);
       mx = fmax2(mx, __shfl_xor(mx, 32, 64));
-      ref2 = mx * c2;
+      ref2 = FOLD ? mx : mx * c2;
       lsum = 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          t[mb][r] = fast_exp2(__builtin_fmaf(t[mb][r], c2, -ref2));
+          t[mb][r] = fast_exp2(FOLD ? t[mb][r] - ref2 : __builtin_fmaf(t[mb][r], c2, -ref2));
           lsum += t[mb][r];
         }
       lsum += __shfl_xor(lsum, 32, 64);
@@ -464,9 +488,10 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xs + byte);
       __builtin_amdgcn_raw_buffer_store_b128(v, yr, r * ROWB + ((pc ^ tok_swz(D, r)) * 16), 0, kCachePolicyNT);
     }
-    // per-token statistics; lanes of the upper half and rows past the run fall outside the range
-    const float lse2 = keep ? (ref2 + __log2f(lsum)) : __builtin_huge_valf();
-    const float dl = keep ? delta : 0.f;
+    // per-token statistics, negated (the latent side starts its accumulators
+    // from them); lanes of the upper half and rows past the run fall outside the range
+    const float lse2 = keep ? -(ref2 + __log2f(lsum)) : kNegInf;
+    const float dl = keep ? -delta : 0.f;
     const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(lseg + n0, 0, valid_rows * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(delg + n0, 0, valid_rows * 4, 0x00020000);
     const int soff = hh ? (1 << 20) : l32 * 4;
@@ -481,7 +506,8 @@ __global__ __launch_bounds__(64 * NWV) void dbwd_tok_mfma_kernel(const DecBwdArg
 // [32w, 32w+32) (lane = latent), 64-token tiles of Xq, dY and the tokens'
 // statistics arrive through a direct-load ring:
 //   S^T = Xq Klat^T, dA^T = dY Z^T          (A = token rows, B = latents in registers)
-//   A = exp2(s log2e S - lse2[n]),  dT = A (dA - delta[n])
+//   A = exp2(s log2e S - lse2[n]),  dT = A (dA - delta[n])   (-lse2 and -delta
+//   arrive from the token side and start the accumulators of S and dA)
 //   dZ^T += dY^T A^T,  dKlat^T += Xq^T dT^T  (A = transposing reads of the tiles)
 // The chunk's sums go to its workspace slot (dKlat without the scale s).
 // ---------------------------------------------------------------------------
@@ -542,6 +568,25 @@ __global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs
   }
   wait_vm<0>();   // only the ring's loads are in flight from here on
   const float c2 = a.scale_log2;
+  // FOLD (head dim 16): the latent keys enter the score product as the bf16
+  // pair hi + lo of s log2(e) Klat, so A = exp2 of the product
+  constexpr bool FOLD = D == 16;
+  bf16x8_t klo[KS];
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t w = __builtin_bit_cast(u32x4_t, kop[ks]);
+      u32x4_t hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f0 = bf16lo(w[e]) * c2, f1 = bf16hi(w[e]) * c2;
+        hi[e] = pack_bf16x2(f0, f1);
+        lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
+      }
+      kop[ks] = __builtin_bit_cast(bf16x8_t, hi);
+      klo[ks] = __builtin_bit_cast(bf16x8_t, lo);
+    }
+  }
 
   const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
   auto tile_bits = [&](int u) -> uint64_t {
@@ -626,18 +671,9 @@ __global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs
       bf16x8_t pa[4], pd[4];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
-        f32x16_t sc = f32x16_t{}, da = f32x16_t{};
-        const uint8_t* xrow = xst + (32 * b2 + swap23(l32)) * ROWB;
-        const uint8_t* grow = gst + (32 * b2 + swap23(l32)) * ROWB;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch = (2 * ks + hh) ^ swk;
-          sc = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xrow + ch * 16)),
-                            kop[ks], sc);
-          da = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(grow + ch * 16)),
-                            zop[ks], da);
-        }
-        // register r of lane half hh holds token 32*b2 + 16*(r/8) + 8*hh + r%8
+        // register r of lane half hh holds token 32*b2 + 16*(r/8) + 8*hh + r%8: the
+        // tokens' -lse2 and -delta in the same order start the accumulators
+        f32x16_t nl, nd;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const int t0 = 32 * b2 + 16 * g + 8 * hh;
@@ -645,14 +681,34 @@ __global__ __launch_bounds__(64 * NW) void dbwd_lat_mfma_kernel(const DecBwdArgs
           const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(stt + t0 + 4);
           const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(stt + 64 + t0);
           const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(stt + 64 + t0 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            nl[8 * g + e] = l0[e];
+            nl[8 * g + 4 + e] = l1[e];
+            nd[8 * g + e] = d0[e];
+            nd[8 * g + 4 + e] = d1[e];
+          }
+        }
+        f32x16_t sc = FOLD ? nl : f32x16_t{}, da = nd;
+        const uint8_t* xrow = xst + (32 * b2 + swap23(l32)) * ROWB;
+        const uint8_t* grow = gst + (32 * b2 + swap23(l32)) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = (2 * ks + hh) ^ swk;
+          const bf16x8_t xo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xrow + ch * 16));
+          sc = mfma32x32x16(xo, kop[ks], sc);
+          if constexpr (FOLD) sc = mfma32x32x16(xo, klo[ks], sc);
+          da = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(grow + ch * 16)),
+                            zop[ks], da);
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
           float pv[8], dv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * g + e;
-            const float l2 = e < 4 ? l0[e] : l1[e - 4];
-            const float dl = e < 4 ? d0[e] : d1[e - 4];
-            pv[e] = fast_exp2(__builtin_fmaf(sc[r], c2, -l2));
-            dv[e] = pv[e] * (da[r] - dl);
+            pv[e] = fast_exp2(FOLD ? sc[r] : __builtin_fmaf(sc[r], c2, nl[r]));
+            dv[e] = pv[e] * da[r];
           }
           if (!full) {
 #pragma unroll

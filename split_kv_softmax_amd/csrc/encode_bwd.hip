@@ -489,12 +489,40 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       }
   }
   const float Lm = a.L[bh * M + m];
-  const float cms = a.scale * a.c[bh * M + m];
+  // FOLD (head dim 16, where the score products are cheap): Q enters the score
+  // product as the bf16 pair hi + lo of s log2(e) Q with the accumulator
+  // starting at -L log2(e), so P = exp2 of the product; dP's accumulator starts
+  // at -c, so dS = P dP is one product per weight, unscaled (s is applied to
+  // the key-gradient rows at staging and to the query gradient by the reduce)
+  constexpr bool FOLD = D == 16;
+  const float cms = FOLD ? a.c[bh * M + m] : a.scale * a.c[bh * M + m];
   wait_vm<0>();
   barrier_lds();   // the stationary copy is dead from here on: the ring reuses it
   const float c2 = a.scale_log2;
   const float sc1 = a.scale;
   const float nl2 = (Lm == kNegInf) ? __builtin_huge_valf() : Lm * kLog2e;
+  bf16x8_t qlo[KS];
+  f32x16_t sinit = f32x16_t{}, dpinit = f32x16_t{};
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t w = __builtin_bit_cast(u32x4_t, qop[ks]);
+      u32x4_t hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f0 = bf16lo(w[e]) * c2, f1 = bf16hi(w[e]) * c2;
+        hi[e] = pack_bf16x2(f0, f1);
+        lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
+      }
+      qop[ks] = __builtin_bit_cast(bf16x8_t, hi);
+      qlo[ks] = __builtin_bit_cast(bf16x8_t, lo);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sinit[r] = -nl2;   // -inf for a row without any valid key: P = 0
+      dpinit[r] = -cms;
+    }
+  }
 
   const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
   auto tile_bits = [&](int u) -> uint64_t {
@@ -606,14 +634,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
         const bool full = bits == ~0ull;   // uniform: no per-element masking for whole tiles
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2) {
-          f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+          f32x16_t sc = sinit, dp = dpinit;
           const uint8_t* krow = kst + (32 * b2 + swap23(l32)) * ROWB;
           const uint8_t* vrow = vst + (32 * b2 + swap23(l32)) * ROWB;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const int ch = (2 * ks + hh) ^ swk;
-            sc = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16)),
-                              qop[ks], sc);
+            const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16));
+            sc = mfma32x32x16(kop, qop[ks], sc);
+            if constexpr (FOLD) sc = mfma32x32x16(kop, qlo[ks], sc);
             dp = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vrow + ch * 16)),
                               gop[ks], dp);
           }
@@ -625,8 +654,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int r = 8 * g + j;
-              pv[j] = fast_exp2(__builtin_fmaf(sc[r], c2, -nl2));
-              ds[j] = pv[j] * __builtin_fmaf(dp[r], sc1, -cms);   // s dS: dK and dQ take it unscaled
+              if constexpr (FOLD) {
+                pv[j] = fast_exp2(sc[r]);
+                ds[j] = pv[j] * dp[r];                           // dS, unscaled
+              } else {
+                pv[j] = fast_exp2(__builtin_fmaf(sc[r], c2, -nl2));
+                ds[j] = pv[j] * __builtin_fmaf(dp[r], sc1, -cms);   // s dS: dK and dQ take it unscaled
+              }
             }
             if (!full) {
               // padding and rows past the chunk: exact zeros (their K/V rows may hold anything)
@@ -710,6 +744,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
           return __builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]});
         };
         // register r of lane half hh: d = 32*db + 16*(r/8) + 8*hh + r%8, token 32*nb + l32
+        // FOLD: the key-gradient rows take s here (dS is unscaled)
+        const float os = (FOLD && tsel == 1) ? sc1 : 1.f;
         auto stage_out = [&](int nb, const f32x16_t* acc) {
           const int n = 32 * nb + l32;
 #pragma unroll
@@ -717,8 +753,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
               const f32x16_t& v = acc[j];
-              const u32x4_t w = {pack_bf16x2(v[8 * g + 0], v[8 * g + 1]), pack_bf16x2(v[8 * g + 2], v[8 * g + 3]),
-                                 pack_bf16x2(v[8 * g + 4], v[8 * g + 5]), pack_bf16x2(v[8 * g + 6], v[8 * g + 7])};
+              const u32x4_t w = {pack_bf16x2(v[8 * g + 0] * os, v[8 * g + 1] * os),
+                                 pack_bf16x2(v[8 * g + 2] * os, v[8 * g + 3] * os),
+                                 pack_bf16x2(v[8 * g + 4] * os, v[8 * g + 5] * os),
+                                 pack_bf16x2(v[8 * g + 6] * os, v[8 * g + 7] * os)};
               const int ch = 4 * (db0 + j) + 2 * g + hh;
               st16(stg + n * ROWB + (ch ^ out_swz(n)) * 16, w);
             }
@@ -852,6 +890,10 @@ static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t s) {
 }
 
 bool bwd_kv_fuses_dq(int M, int D) { return !(M == 256 && D == 128); }
+
+// whether the fused kernel's query-gradient partials already carry the scale s
+// (head dim 16 forms dS unscaled)
+bool bwd_kv_partials_scaled(int M, int D) { return bwd_kv_fuses_dq(M, D) && D != 16; }
 
 // D=64 with M<=128: 4 waves of <=248 VGPRs and <=80 KB of LDS, so two per CU;
 // the other shapes need more than half the LDS or all 256 VGPRs per lane

@@ -172,6 +172,9 @@ hipError_t launch_bwd_dq_mfma(const BwdArgs& a, hipStream_t s);
 // query-gradient chunk partials (where the registers allow it); where it does
 // not, launch_bwd_dq_mfma runs first
 bool bwd_kv_fuses_dq(int M, int D);
+// whether the query-gradient chunk partials already carry the scale s (else
+// the reduce applies it)
+bool bwd_kv_partials_scaled(int M, int D);
 // workgroups of the key/value gradient kernel one CU holds at once (its
 // registers and LDS), which sizes the token chunks of the backward
 int bwd_kv_blocks_per_cu(int M, int D);
