@@ -34,31 +34,43 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
-COUNTERS = os.path.join(HERE, "profiles", "encode_flarepp_N262144_hbm_counters.md")
-ENCODER_SOURCES = [os.path.join(HERE, "split_kv_softmax_amd", "csrc", f)
-                   for f in ("encode.hip", "decode.hip", "common.h", "kernels.h")]
+# committed rocprofv3 counter summaries (profiles/<name>_counters.md) per workload
+COUNTER_FILES = {
+    W.FLAREPP.name: "flarepp_fwd_N262144_counters.md",
+    W.FLARE_BLOCK.name: "flare_block_N65536_counters.md",
+    W.SPLITKV_Q1.name: "splitkv_q1_N131072_counters.md",
+    W.MASKED_FWD_BWD.name: "masked_fwd_bwd_N262144_counters.md",
+    W.FLAREPP_D16.name: "flarepp_fwd_D16_N1048576_counters.md",
+    W.FLARE_ENCODE_F32_SMALL.name: "encode_fp32_small_N1024_counters.md",
+}
+# the sources each kernel family is built from (the summaries record their hash)
+KERNEL_SOURCES = {"encode_ilv": ["encode.hip"], "encode_mfma": ["encode.hip"], "encode_q1": ["encode.hip"],
+                  "encode_generic": ["encode.hip"], "decode_mfma": ["decode.hip"], "bwd_kv_mfma": ["encode_bwd.hip"],
+                  "bwd_dq_mfma": ["encode_bwd.hip"]}
 
 
-def encoder_source_hash() -> str:
+def source_hash(kernel: str) -> str:
     import hashlib
+    key = next(k for k in KERNEL_SOURCES if k in kernel)
     h = hashlib.sha256()
-    for f in ENCODER_SOURCES:
-        h.update(open(f, "rb").read())
+    for f in KERNEL_SOURCES[key] + ["common.h", "kernels.h"]:
+        h.update(open(os.path.join(HERE, "split_kv_softmax_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel="encoder"):
-    """HBM bytes per launch of the FLARE++ encoder or decode from the committed counter
-    summary, or None when the encoder/decode sources changed since the counters were taken."""
+def counter_summary(workload: str, kernel: str):
+    """HBM bytes and matrix-core use per launch of `kernel` from the committed counter summary of
+    `workload`, or None when there is none or its sources changed since the counters were taken."""
     try:
-        txt = open(COUNTERS).read()
-        blk = txt.split("```json", 1)[1].split("```", 1)[0]
-        d = json.loads(blk)
-    except Exception:
+        txt = open(os.path.join(HERE, "profiles", COUNTER_FILES[workload])).read()
+        d = json.loads(txt.split("```json", 1)[1].split("```", 1)[0])
+        key = next(k for k in d["kernels"] if kernel in k)
+        e = d["kernels"][key]
+        if e["source_hash"] != source_hash(kernel):
+            return None
+        return e
+    except (KeyError, OSError, StopIteration, ValueError, IndexError):
         return None
-    if d.get("source_hash") != encoder_source_hash():
-        return None
-    return d.get("hbm_bytes_per_launch" if kernel == "encoder" else "decode_hbm_bytes_per_launch")
 
 
 def _ev():
@@ -236,12 +248,12 @@ def cpu_baseline(w: W.Workload, x, budget_s: float, shared: bool = False):
 
 
 def roofline_candidates(w: W.Workload, x, step, ph):
-    """(kernel name, ms per launch, algorithmic bytes per launch, measured HBM bytes or None) of
-    each kernel that can bind the step; the caller reports the one furthest below the roofline."""
+    """(kernel name, ms per launch, algorithmic bytes per launch, kernel key of the committed counter
+    summary or None) of each kernel that can bind the step; the caller reports the one furthest below
+    the roofline."""
     kvb = 2 if w.dtype == "bf16" else 4
     row = w.D * kvb                               # bytes of one K, V, Y, dK or dV row
     rows = w.B * w.H * w.N
-    main = w.name == W.FLAREPP.name
     if w.kind == "flarepp" and "encode2_bwd" in ph:
         # physical-value encoder backward: K, V read, dV written, dK read and written (it adds into the
         # decoder's key gradient); query-synthesis encoder backward: Kt, Vt read, dKt, dVt written, or
@@ -251,26 +263,28 @@ def roofline_candidates(w: W.Workload, x, step, ph):
         return [("flare_encode_bwd call (row term, key/value-gradient kernel with fused query gradient, reduce); "
                  "both encoder backwards averaged", ms, (5 + enc1_rows) * rows * row // 2, None)]
     if w.kind == "flarepp":
+        plain = not getattr(step, "shared", False)
         if "encode_merge1" in ph:
             enc = ("encode_ilv_kernel with the merge inside (flare_encode_merge, one launch; both encoders "
                    "averaged)", 0.5 * (ph["encode_merge1"] + ph["encode_merge2"]), 2 * rows * row, None)
         else:
             enc = ("encode_ilv_kernel (flare_encode, one launch; both encoders averaged)",
-                   0.5 * (ph["encode1"] + ph["encode2"]), 2 * rows * row,
-                   measured_traffic("encoder") if main else None)
+                   0.5 * (ph["encode1"] + ph["encode2"]), 2 * rows * row, "encode_ilv_kernel" if plain else None)
         dec = ("decode_mfma_kernel (flare_decode, one launch)", ph["decode"], 2 * rows * row,
-               measured_traffic("decode") if main else None)
+               "decode_mfma_kernel" if plain else None)
         return [enc, dec]
     if w.kind == "flare":
         enc = ph.get("encode", ph.get("encode_merge"))
-        return [("encode_mfma_kernel (flare_encode, one launch)", enc, 2 * rows * row, None),
-                ("decode_mfma_kernel (flare_decode, one launch)", ph["decode"], 2 * rows * row, None)]
+        return [("encode_ilv_kernel (flare_encode, one launch)", enc, 2 * rows * row,
+                 "encode_ilv_kernel" if "encode" in ph else None),
+                ("decode_mfma_kernel (flare_decode, one launch)", ph["decode"], 2 * rows * row, "decode_mfma_kernel")]
     if w.kind == "encode_bwd":
         valid = int(x["mask"].sum().item()) * w.H if "mask" in x else rows
         return [("flare_encode_bwd call (row term, query-gradient, key/value-gradient and reduce kernels)",
                  ph["backward"], 2 * valid * row + 2 * rows * row, None)]
+    key = {"splitkv": "encode_q1_kernel", "encode": "encode_generic_kernel"}.get(w.kind)
     return [("flare_encode call (one encoder launch)", ph.get("encode", ph.get("encode_merge")), 2 * rows * row,
-             None)]
+             key if "encode" in ph else None)]
 
 
 def cpu_model() -> str:
@@ -439,8 +453,9 @@ def main():
     ph = {n: p / step.count for n, p in zip(step.names, step.phase_ms)}
     cands = roofline_candidates(w, x, step, ph)
     # the binding kernel: the one furthest below the HBM roofline
-    kern_name, kern_ms, kern_bytes, kern_traffic = min(cands, key=lambda c: c[2] / c[1])
+    kern_name, kern_ms, kern_bytes, kern_key = min(cands, key=lambda c: c[2] / c[1])
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
+    summ = counter_summary(w.name, kern_key) if kern_key else None
     tokens = w.B * w.N * w.H
     kvb = 2 if w.dtype == "bf16" else 4
     is_main = w.name == W.FLAREPP.name and not args.backward and not args.shared
@@ -466,21 +481,29 @@ def main():
                    **({"projections": "shared"} if args.shared else {}),
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": kern_traffic,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": summ["hbm_bytes_per_launch"] if summ else None,
+                     "mfma_util": summ["mfma_util"] if summ else None,
                      "kernel": kern_name, "kernel_ms": kern_ms, "algorithmic_bytes": kern_bytes},
         "step_ms": {"mean": ms_per_step, "median": statistics.median(per_step), "min": min(per_step)},
         "phases_ms": ph,
         "wall_s_timed": wall,
     }
     if len(cands) > 1:
-        line["kernels"] = [{"kernel": n, "ms": ms, "algorithmic_bytes": b, "traffic": t,
-                            "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS} for n, ms, b, t in cands]
+        line["kernels"] = []
+        for n, ms, b, key in cands:
+            cs = counter_summary(w.name, key) if key else None
+            line["kernels"].append({"kernel": n, "ms": ms, "algorithmic_bytes": b,
+                                    "traffic": cs["hbm_bytes_per_launch"] if cs else None,
+                                    "mfma_util": cs["mfma_util"] if cs else None,
+                                    "frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
     if pass_steps:
         line["step_ms_mall_flushed"] = {"mean": sum(pass_steps) / len(pass_steps),
                                         "median": statistics.median(pass_steps), "min": min(pass_steps)}
     if is_main:
         step_bytes = 6 * tokens * w.D * kvb        # 2 encoders (K,V) + decode (read K, write Y)
-        line["roofline"]["source_hash"] = encoder_source_hash()
+        if kern_key:
+            line["roofline"]["source_hash"] = source_hash(kern_key)
         line["step_roofline"] = {"algorithmic_bytes": step_bytes,
                                  "achieved_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
                                  "frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
