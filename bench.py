@@ -394,7 +394,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "the path is per-GPU and this build has no multi-GPU leg.", file=sys.stderr)
+              "the path is per-GPU and there is no multi-GPU leg.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
