@@ -456,7 +456,9 @@ def main():
     # a bounded wait kernel (a few ms to tenths of a second, by the counter its clock reads)
     # holds the GPU while the host queues every step of the pass, so the steps run back to
     # back and no host-side launch gap lands inside a phase
-    torch.cuda._sleep(50_000_000)
+    hold = getattr(torch.cuda, "_sleep", None)   # torch's own spin kernel (a private helper)
+    if hold is not None:
+        hold(50_000_000)
     for _ in range(args.steps):
         if scratch is not None:
             scratch.fill_(1)
