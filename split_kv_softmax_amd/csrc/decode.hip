@@ -3,6 +3,7 @@
 // every token attends over the M replicated latents, Y[n] = softmax_m(s Xq[n].Klat[m]) Z,
 // with no cross-partition work.  The softmax over m is exact (all M scores of a
 // token are formed before any exponential).
+#include <type_traits>
 #include "common.h"
 #include "kernels.h"
 
@@ -150,14 +151,14 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
   const int nb = span > 0 ? (span + BLK * NWV - 1) / (BLK * NWV) : 0;
   // this lane's 16-byte piece of each load: byte offset within a full block,
   // and within row 0 (rows past the run re-read row 0; results not stored)
-  uint32_t voff[NI], voff0[NI];
+  // (the row-0 offset is the low bits of the row's offset: ch * 16 < ROWB)
+  uint32_t voff[NI];
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
     const int byte = ii * 1024 + lane * 16;
     const int r = byte / ROWB, pc = (byte % ROWB) / 16;
     const int ch = pc ^ row_swz(D, r);
     voff[ii] = r * ROWB + ch * 16;
-    voff0[ii] = ch * 16;
   }
   auto issue = [&](int j, int stage) {
     const int n0 = n_lo + BLK * (wave + NWV * j);
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
       const int r = (ii * 1024) / ROWB + lane / (ROWB / 16);
-      dma16_off(xb, n0 + r < n_hi ? voff[ii] : voff0[ii], st + ii * 1024);
+      dma16_off(xb, n0 + r < n_hi ? voff[ii] : (voff[ii] & (ROWB - 1)), st + ii * 1024);
     }
   };
 #pragma unroll
@@ -174,6 +175,30 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     if (j < nb) issue(j, j);
 
   const int swx = row_swz(D, l32);
+  // Latent operands in registers for the whole run (head dims 64 and 16 up to
+  // 128 latents): the latent keys' score-product rows and Z^T's value-product
+  // rows of this lane, read from LDS once instead of once per token block
+  // (128 VGPRs at head dim 64; the exact form below keeps its row sums on the
+  // vector ALUs so that the two waves of a SIMD still fit 256 registers).
+  constexpr bool REGOP = (D == 64 || D == 16) && MB <= 4;
+  u32x4_t kreg[REGOP ? MB * KS : 1], klreg[REGOP && FOLD ? MB * KS : 1], zreg[REGOP ? DB * MS : 1];
+  if constexpr (REGOP) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ro = (32 * mb + swap23(l32)) * KLD + 8 * hh + 16 * ks;
+        kreg[mb * KS + ks] = *reinterpret_cast<const u32x4_t*>(&Kl[ro]);
+        if constexpr (FOLD) klreg[mb * KS + ks] = *reinterpret_cast<const u32x4_t*>(&Klo[ro]);
+      }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < MS; ++ks) {
+        const uint16_t* zrow = &Zt[(32 * db + (D >= 32 ? swap23(l32) : swap23(l32) & 15)) * ZLD + 8 * hh];
+        zreg[db * MS + ks] = *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks);
+      }
+  }
   // Row sums on a 16x16x32 product: fed the weight operand of the 32x32x16
   // product as its B, lane l contributes token l%32, latents 8*(l/32)+0..7 of
   // the k-step as column l%16, contraction block l/16.  Selector rows 0 and 8
@@ -217,11 +242,16 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       const int ro = (32 * mb + swap23(l32)) * KLD + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        t = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&Kl[ro + 16 * ks])), xop[ks],
-                         t);
-        if constexpr (FOLD)
-          t = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(&Klo[ro + 16 * ks])),
-                           xop[ks], t);
+        u32x4_t khi, klo;
+        if constexpr (REGOP) {
+          khi = kreg[mb * KS + ks];
+          klo = klreg[FOLD ? mb * KS + ks : 0];
+        } else {
+          khi = *reinterpret_cast<const u32x4_t*>(&Kl[ro + 16 * ks]);
+          if constexpr (FOLD) klo = *reinterpret_cast<const u32x4_t*>(&Klo[ro + 16 * ks]);
+        }
+        t = mfma32x32x16(__builtin_bit_cast(bf16x8_t, khi), xop[ks], t);
+        if constexpr (FOLD) t = mfma32x32x16(__builtin_bit_cast(bf16x8_t, klo), xop[ks], t);
       }
       return t;
     };
@@ -248,9 +278,14 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       for (int db = 0; db < DB; ++db) {
         // Z^T rows permuted so that register group g of lane half hh holds the 8
         // consecutive head dims 32*db + 16*g + 8*hh .. +7
-        const uint16_t* zrow = &Zt[(32 * db + (D >= 32 ? swap23(l32) : swap23(l32) & 15)) * ZLD + 8 * hh];
-        y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks)), pk,
-                             y[db]);
+        u32x4_t zop;
+        if constexpr (REGOP) {
+          zop = zreg[db * MS + ks];
+        } else {
+          const uint16_t* zrow = &Zt[(32 * db + (D >= 32 ? swap23(l32) : swap23(l32) & 15)) * ZLD + 8 * hh];
+          zop = *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks);
+        }
+        y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, zop), pk, y[db]);
       }
     };
     auto clear = [&]() {
@@ -272,11 +307,12 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     float lsum = ls4[0];
     if (__ballot(!(lsum >= 0x1p-64f && lsum <= 0x1p64f))) {
       // exact form: the token's maximum over its M scores first.  Its row sums
-      // come from ones x P on the 32x32x16 product, which only adds a token's
-      // own weights (the selector form multiplies the neighbouring token's
-      // weights by 0, and 0 x NaN from a padded row would leak across).  The
-      // scores are formed twice (for the maximum, then for the weights), so no
-      // block's scores are held across the other blocks' products.
+      // are added up on the vector ALUs from the lane's own rounded weights
+      // (the selector form multiplies the neighbouring token's weights by 0,
+      // and 0 x NaN from a padded row would leak across); lanes l and l+32
+      // hold the two latent halves of token l%32.  The scores are formed twice
+      // (for the maximum, then for the weights), so no block's scores are held
+      // across the other blocks' products.
       float mx = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -290,40 +326,53 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       }
       const float nmc = FOLD ? -mx : -mx * c2;
       clear();
-      f32x16_t lacc = f32x16_t{};
-      const bf16x8_t ones =
-          __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+      float half_sum = 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         bf16x8_t pk2[2];
         weigh(scores_of(mb), nmc, pk2, true);
         accumulate(2 * mb, pk2[0]);
         accumulate(2 * mb + 1, pk2[1]);
-        lacc = mfma32x32x16(ones, pk2[0], lacc);
-        lacc = mfma32x32x16(ones, pk2[1], lacc);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const u32x4_t w = __builtin_bit_cast(u32x4_t, pk2[g]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) half_sum += bf16lo(w[e]) + bf16hi(w[e]);
+        }
       }
-      lsum = lacc[0];
+      {
+        const auto sw =
+            __builtin_amdgcn_permlane32_swap(__float_as_uint(half_sum), __float_as_uint(half_sum), false, false);
+        lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
     }
     // Y block out through its own (consumed) ring stage: each lane writes its
     // token's head dims as 16-byte pieces, then whole rows leave with 16-byte
     // stores.  Buffer stores drop the rows past the run, so every block issues
-    // the same ST stores (the ring's wait counts rely on that).
-    const bool keep = inb && tmask[inb ? n - n_lo : 0] != 0;
-    const float inv = 1.f / lsum;
+    // the same ST stores (the ring's wait counts rely on that).  Masked tokens
+    // are written as zeros; only a wave that holds one selects.
+    const bool keep = !inb || tmask[inb ? n - n_lo : 0] != 0;
+    const float inv = __builtin_amdgcn_rcpf(lsum);
     uint8_t* stg = myring + st * BB;
+    auto stage_y = [&](auto masked) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        u32x4_t w;
+        for (int g = 0; g < NG; ++g) {
+          u32x4_t w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t v = pack_bf16x2(y[db][8 * g + 2 * e] * inv, y[db][8 * g + 2 * e + 1] * inv);
-          w[e] = keep ? v : 0u;
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t v = pack_bf16x2(y[db][8 * g + 2 * e] * inv, y[db][8 * g + 2 * e + 1] * inv);
+            w[e] = (decltype(masked)::value && !keep) ? 0u : v;
+          }
+          const int pc = (4 * db + 2 * g + hh) ^ swx;
+          st16(stg + l32 * ROWB + pc * 16, w);
         }
-        const int pc = (4 * db + 2 * g + hh) ^ swx;
-        st16(stg + l32 * ROWB + pc * 16, w);
-      }
+    };
+    if (__ballot(!keep))
+      stage_y(std::true_type{});
+    else
+      stage_y(std::false_type{});
     const int valid_rows = min(BLK, n_hi - n0);
     const __amdgpu_buffer_rsrc_t yr =
         __builtin_amdgcn_make_buffer_rsrc(Yg + (int64_t)n0 * D, 0, valid_rows * ROWB, 0x00020000);
