@@ -160,14 +160,15 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     const int ch = pc ^ row_swz(D, r);
     voff[ii] = r * ROWB + ch * 16;
   }
-  auto issue = [&](int j, int stage) {
+  // (full: the block is known to lie inside the run)
+  auto issue = [&](int j, int stage, bool full = false) {
     const int n0 = n_lo + BLK * (wave + NWV * j);
     const uint32_t st = myring_lds + stage * BB;
     const uint16_t* xb = Xg + (int64_t)n0 * D;
 #pragma unroll
     for (int ii = 0; ii < NI; ++ii) {
       const int r = (ii * 1024) / ROWB + lane / (ROWB / 16);
-      dma16_off(xb, n0 + r < n_hi ? voff[ii] : (voff[ii] & (ROWB - 1)), st + ii * 1024);
+      dma16_off(xb, (full || n0 + r < n_hi) ? voff[ii] : (voff[ii] & (ROWB - 1)), st + ii * 1024);
     }
   };
 #pragma unroll
@@ -212,19 +213,24 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     const uint32_t w = on ? 0x3f803f80u : 0u;
     sel = __builtin_bit_cast(bf16x8_t, u32x4_t{w, w, w, w});
   }
-  // S blocks per trip, so that each block's ring stage is a compile-time constant
-  for (int j0 = 0; j0 < nb; j0 += S)
-#pragma unroll
-  for (int st = 0; st < S; ++st) {
-    const int j = j0 + st;
-    if (j >= nb) break;
-    const int lb = min(S - 2, nb - 1 - j);          // blocks loaded after block j
-    const int ls = min(j, S - 1);                   // blocks stored after block j was loaded
-    wait_block<NI, ST, S>(lb > 0 ? lb : 0, ls);
-    if (j + S - 1 < nb) issue(j + S - 1, (st + S - 1) % S);
+  const bool has_mask = a.token_mask != nullptr;
+  // Block j of this wave in ring stage st.  STEADY: j >= S-1 and block j+S-1
+  // lies inside the run, so block j is full, its load is followed by S-2 full
+  // loads and S-1 stores, and the block S-1 ahead is issued without a row check.
+  auto block = [&](const int j, const int st, auto steady_t) {
+    constexpr bool STEADY = decltype(steady_t)::value;
+    if constexpr (STEADY) {
+      wait_vm<NI * (S - 2) + ST * (S - 1)>();
+      issue(j + S - 1, (st + S - 1) % S, true);
+    } else {
+      const int lb = min(S - 2, nb - 1 - j);          // blocks loaded after block j
+      const int ls = min(j, S - 1);                   // blocks stored after block j was loaded
+      wait_block<NI, ST, S>(lb > 0 ? lb : 0, ls);
+      if (j + S - 1 < nb) issue(j + S - 1, (st + S - 1) % S);
+    }
     const int n0 = n_lo + BLK * (wave + NWV * j);
     const int n = n0 + l32;
-    const bool inb = n < n_hi;
+    const bool inb = STEADY || n < n_hi;
     const uint8_t* xs = myring + st * BB + l32 * ROWB;
     bf16x8_t xop[KS];
 #pragma unroll
@@ -351,7 +357,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     // stores.  Buffer stores drop the rows past the run, so every block issues
     // the same ST stores (the ring's wait counts rely on that).  Masked tokens
     // are written as zeros; only a wave that holds one selects.
-    const bool keep = !inb || tmask[inb ? n - n_lo : 0] != 0;
+    const bool keep = !has_mask || !inb || tmask[inb ? n - n_lo : 0] != 0;
     const float inv = __builtin_amdgcn_rcpf(lsum);
     uint8_t* stg = myring + st * BB;
     auto stage_y = [&](auto masked) {
@@ -373,7 +379,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       stage_y(std::true_type{});
     else
       stage_y(std::false_type{});
-    const int valid_rows = min(BLK, n_hi - n0);
+    const int valid_rows = STEADY ? BLK : min(BLK, n_hi - n0);
     const __amdgpu_buffer_rsrc_t yr =
         __builtin_amdgcn_make_buffer_rsrc(Yg + (int64_t)n0 * D, 0, valid_rows * ROWB, 0x00020000);
 #pragma unroll
@@ -384,6 +390,22 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       // non-temporal: the output rows are not read again by this path
       __builtin_amdgcn_raw_buffer_store_b128(v, yr, r * ROWB + ((pc ^ row_swz(D, r)) * 16), 0, kCachePolicyNT);
     }
+  };
+  // S blocks per trip, so that each block's ring stage is a compile-time
+  // constant: the first trip (the ring fills), steady trips, then the rest
+  const int nbf = span >= BLK ? (span - BLK) / (BLK * NWV) + 1 : 0;   // full blocks of this wave
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    if (st < nb) block(st, st, std::false_type{});
+  int j0 = S;
+  for (; j0 + 2 * S - 1 <= nbf; j0 += S) {
+#pragma unroll
+    for (int st = 0; st < S; ++st) block(j0 + st, st, std::true_type{});
+  }
+  for (; j0 < nb; j0 += S) {
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+      if (j0 + st < nb) block(j0 + st, st, std::false_type{});
   }
 }
 

@@ -13,6 +13,7 @@
 // returned log-normaliser is natural: L = s m + ln l.
 #include <stdlib.h>
 
+#include <type_traits>
 #include "common.h"
 #include "kernels.h"
 
@@ -608,15 +609,17 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
     voff[j] = r * ROWB + ch * 16;
     voff0[j] = ch * 16;
   }
-  // K (is_v false) or V rows of local tile u into ring slot `slot`
-  auto issue = [&](int u, int slot, bool is_v) {
+  // K (is_v false) or V rows of local tile u into ring slot `slot` (full:
+  // the tile is known to hold TILE rows)
+  auto issue = [&](int u, int slot, bool is_v, bool full = false) {
     if (NI < NW && wave >= NI) return;   // (wave-uniform)
     const int t0 = t_begin + (grp + G * u) * TILE;
     const int nrows = t_end - t0;
     const uint16_t* base = (is_v ? Vg : Kg) + (int64_t)t0 * D;
     const uint32_t dst = ring_lds + (is_v ? S + slot : slot) * TB;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) dma16_off(base, vrow[j] < nrows ? voff[j] : voff0[j], dst + (wave + NW * j) * 1024);
+    for (int j = 0; j < NJ; ++j)
+      dma16_off(base, (full || vrow[j] < nrows) ? voff[j] : voff0[j], dst + (wave + NW * j) * 1024);
   };
 
   // Per-lane LDS addresses in slot 0; slots and k-steps are immediate offsets
@@ -851,40 +854,57 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   if (S - 2 < ntg) issue(S - 2, S - 2, true);
 
   // ---- rounds, 2S per trip so that ring slots and buffer parities are
-  // compile-time constants
-  for (int u0 = 0; u0 < nrounds; u0 += 2 * S) {
-#pragma unroll
-    for (int sr = 0; sr < 2 * S; ++sr) {
-      const int u = u0 + sr, st = sr % S;
-      if (u < nrounds) {
-        // batch u = {K(u+2), V(u)} complete for this wave; batches u+1 .. u+S-2 may be in flight
-        wait_units<NJ, 2 * (S - 2)>(clampS2(ntg - u - 3) + clampS2(ntg - u - 1));
-        barrier_lds();
-        // every wave is past round u-1: K slot (u+1)%S and V slot (u-1)%S are free
-        if (u + S + 1 < ntg) issue(u + S + 1, (st + 1) % S, false);
-        if (u + S - 1 < ntg) issue(u + S - 1, (st + S - 1) % S, true);
-        const int e = sr % 2, f = 1 - e;     // tile u: buffer e; tile u+1: buffer f; tile u+2: buffer e
-        if (__ballot(bad_sum(ts_pend))) rebase(scb[e], pkb[e], ts_pend, scb[f]);
-        lsum += ts_pend;
-        const int n1 = nval(u + 1);
-        if (n1 < TILE) mask_tail(scb[f], n1);
-        // one straight-line block: the value products of tile u, the weights
-        // of tile u+1 and their row sums, the score products of tile u+2
-        values(st, pkb[e]);
-        ts_pend = weights(scb[f], pkb[f], nmc);
-        scores((st + 2) % S, scb[e]);
-        // order: all operand reads (V, then K), a few exponentials while they
-        // arrive, then each product with exponentials and conversions between
-        // (vector groups take vector and transcendental instructions)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NK * DB + NB * KS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
-#pragma unroll
-        for (int i = 0; i < NK * DB + (FOLD ? 2 : 1) * NB * KS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
-        }
-      }
+  // compile-time constants.  Round u (slot st = u % S, parity sr % 2):
+  auto round = [&](const int u, const int sr, auto steady_t) {
+    // STEADY: u + S + 2 < ntg, so both of the round's loads are issued, every
+    // tile they and the round touch is full, and S-2 full batches are in
+    // flight behind batch u
+    constexpr bool STEADY = decltype(steady_t)::value;
+    const int st = sr % S;
+    // batch u = {K(u+2), V(u)} complete for this wave; batches u+1 .. u+S-2 may be in flight
+    if constexpr (STEADY)
+      wait_vm<2 * (S - 2) * NJ>();
+    else
+      wait_units<NJ, 2 * (S - 2)>(clampS2(ntg - u - 3) + clampS2(ntg - u - 1));
+    barrier_lds();
+    // every wave is past round u-1: K slot (u+1)%S and V slot (u-1)%S are free
+    if (STEADY || u + S + 1 < ntg) issue(u + S + 1, (st + 1) % S, false, STEADY);
+    if (STEADY || u + S - 1 < ntg) issue(u + S - 1, (st + S - 1) % S, true, STEADY);
+    const int e = sr % 2, f = 1 - e;     // tile u: buffer e; tile u+1: buffer f; tile u+2: buffer e
+    if (__ballot(bad_sum(ts_pend))) rebase(scb[e], pkb[e], ts_pend, scb[f]);
+    lsum += ts_pend;
+    if constexpr (!STEADY) {
+      const int n1 = nval(u + 1);
+      if (n1 < TILE) mask_tail(scb[f], n1);
     }
+    // one straight-line block: the value products of tile u, the weights
+    // of tile u+1 and their row sums, the score products of tile u+2
+    values(st, pkb[e]);
+    ts_pend = weights(scb[f], pkb[f], nmc);
+    scores((st + 2) % S, scb[e]);
+    // order: all operand reads (V, then K), a few exponentials while they
+    // arrive, then each product with exponentials and conversions between
+    // (vector groups take vector and transcendental instructions)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NK * DB + NB * KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);
+#pragma unroll
+    for (int i = 0; i < NK * DB + (FOLD ? 2 : 1) * NB * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+  };
+  // steady trips first (no tile tail, fixed waits, unconditional loads), then
+  // the remaining rounds with every check
+  const int nsteady = ntg - S - 2;
+  int u0 = 0;
+  for (; u0 + 2 * S <= nsteady; u0 += 2 * S) {
+#pragma unroll
+    for (int sr = 0; sr < 2 * S; ++sr) round(u0 + sr, sr, std::true_type{});
+  }
+  for (; u0 < nrounds; u0 += 2 * S) {
+#pragma unroll
+    for (int sr = 0; sr < 2 * S; ++sr)
+      if (u0 + sr < nrounds) round(u0 + sr, sr, std::false_type{});
   }
 
   // (the sums left pending belong to the tile after the group's last, which
