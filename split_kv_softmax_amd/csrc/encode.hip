@@ -879,9 +879,9 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
     }
     // one straight-line block: the value products of tile u, the weights
     // of tile u+1 and their row sums, the score products of tile u+2
+    scores((st + 2) % S, scb[e]);
     values(st, pkb[e]);
     ts_pend = weights(scb[f], pkb[f], nmc);
-    scores((st + 2) % S, scb[e]);
     // order: all operand reads (V, then K), a few exponentials while they
     // arrive, then each product with exponentials and conversions between
     // (vector groups take vector and transcendental instructions)
