@@ -514,7 +514,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   constexpr int NB = TILE / 32;            // 32-token blocks of the score product
   constexpr int NK = TILE / 16;            // 16-token k-steps of the value product
   static_assert(TILE == 32 || TILE == 64, "tile of 32 or 64 tokens");
-  static_assert(D == 16 || D == 64, "head dim 16 or 64");
+  static_assert(D == 16 || D == 64 || D == 128, "head dim 16, 64 or 128");
   constexpr int ROWB = 2 * D;              // bytes per row
   constexpr int TB = TILE * ROWB;          // bytes of a K (or V) tile
   constexpr int RING = 2 * S * TB;         // S K slots, then S V slots
@@ -540,17 +540,51 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int lg = lane >> 4, li = lane & 15;
   const int nch = a.tab.nchunks;
-  int bid = blockIdx.x;
+  int bid = ordered_block(a.order);
   const int c = bid % nch;
   bid /= nch;
   const int h = bid % a.H;
   const int b = bid / a.H;
-  const int t_begin = a.tab.bnd[c], t_end = a.tab.bnd[c + 1];
+  const int t_begin = a.tab.bnd[c];
+  int t_end = a.tab.bnd[c + 1];
   const int64_t bh = (int64_t)b * a.H + h;
   const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + bh * (int64_t)a.N * D;
   const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + bh * (int64_t)a.N * D;
   const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + (int64_t)b * a.q_bstride +
                        (int64_t)h * a.M * D;
+
+  // Padding mask (one token group only: its per-tile barriers must be uniform
+  // over the workgroup).  The chunk ends at its last valid token; a chunk whose
+  // valid tokens then form its whole range (a valid prefix) runs as unmasked.
+  const_u64* mw = (G == 1 && a.mask_words) ? (const_u64*)(a.mask_words + (int64_t)b * a.mask_words_stride) : nullptr;
+  if (mw) {
+    int* red = reinterpret_cast<int*>(smem);   // (the ring is not in use yet)
+    if (tid == 0) {
+      red[0] = t_begin - 1;
+      red[1] = 0;
+    }
+    __syncthreads();
+    int last = t_begin - 1, cnt = 0;
+    for (int w = (t_begin >> 6) + tid; w <= ((t_end - 1) >> 6); w += 64 * NW * G) {
+      uint64_t x = reinterpret_cast<const uint64_t*>(a.mask_words + (int64_t)b * a.mask_words_stride)[w];
+      const int lo = 64 * w;
+      if (lo < t_begin) x &= ~0ull << (t_begin - lo);
+      if (t_end - lo < 64) x &= (1ull << (t_end - lo)) - 1ull;
+      if (x) {
+        last = lo + 63 - __builtin_clzll(x);
+        cnt += __builtin_popcountll(x);
+      }
+    }
+    if (cnt) {
+      atomicMax(&red[0], last);
+      atomicAdd(&red[1], cnt);
+    }
+    __syncthreads();
+    const int lastv = red[0], nvalid = red[1];
+    __syncthreads();   // every thread has read the result before the ring reuses it
+    t_end = lastv + 1;
+    if (nvalid == t_end - t_begin) mw = nullptr;
+  }
 
   // FOLD (head dim 16, where the score products are cheap): s log2(e) and the
   // row's reference are folded into the score products, so a weight is one
@@ -594,6 +628,14 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   auto nval = [&](int u) -> int {
     if (u >= ntg) return 0;
     return (u == ntg - 1 && owns_last) ? tail : TILE;
+  };
+  // validity bits of local tile u (masked chunks): tokens in the chunk and valid
+  constexpr uint64_t FULLB = TILE == 64 ? ~0ull : ((1ull << TILE) - 1ull);
+  auto tbits = [&](int u) -> uint64_t {
+    const int n = nval(u);
+    if (n == 0) return 0ull;
+    const uint64_t in = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    return in & mask_tile_bits(mw, t_begin + (grp + G * u) * TILE);
   };
 
   uint8_t* ring = smem + grp * RING;
@@ -712,6 +754,16 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
       for (int r = 0; r < 16; ++r) {
         const int tk = 32 * b2 + 16 * (r >> 3) + 8 * hh + (r & 7);
         if (tk >= n) sc[b2][r] = kNegInf;
+      }
+  };
+  // scores of the tile's invalid tokens become -inf
+  auto mask_bits = [&](f32x16_t* sc, uint64_t bits) {
+#pragma unroll
+    for (int b2 = 0; b2 < NB; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tk = 32 * b2 + 16 * (r >> 3) + 8 * hh + (r & 7);
+        if (!((bits >> tk) & 1ull)) sc[b2][r] = kNegInf;
       }
   };
   // Weights of a (masked) score tile against the reference maximum m_run:
@@ -846,7 +898,12 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   {
     scores(0, scb[0]);
     scores(1, scb[1]);
-    if (nval(0) < TILE) mask_tail(scb[0], nval(0));
+    if (mw) {
+      const uint64_t b0 = tbits(0);
+      if (b0 != FULLB) mask_bits(scb[0], b0);
+    } else if (nval(0) < TILE) {
+      mask_tail(scb[0], nval(0));
+    }
     ts_pend = weights(scb[0], pkb[0], nmc);
   }
   barrier_lds();             // every wave is done with K slots 0 and 1
@@ -871,11 +928,29 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
     if (STEADY || u + S + 1 < ntg) issue(u + S + 1, (st + 1) % S, false, STEADY);
     if (STEADY || u + S - 1 < ntg) issue(u + S - 1, (st + S - 1) % S, true, STEADY);
     const int e = sr % 2, f = 1 - e;     // tile u: buffer e; tile u+1: buffer f; tile u+2: buffer e
+    if (!STEADY && mw) {
+      // invalid rows of V(u) become zero (a padded row may hold NaN, and its
+      // weight 0 must not meet it); uniform over the workgroup (one group)
+      const uint64_t bu = tbits(u);
+      if (bu != FULLB) {
+        uint8_t* vs = ring + (S + st) * TB;
+        for (int i = tid; i < TILE * (ROWB / 16); i += 64 * NW) {
+          const int r = i / (ROWB / 16);
+          if (!((bu >> r) & 1ull)) st16(vs + 16 * i, u32x4_t{0, 0, 0, 0});
+        }
+        barrier_lds();
+      }
+    }
     if (__ballot(bad_sum(ts_pend))) rebase(scb[e], pkb[e], ts_pend, scb[f]);
     lsum += ts_pend;
     if constexpr (!STEADY) {
-      const int n1 = nval(u + 1);
-      if (n1 < TILE) mask_tail(scb[f], n1);
+      if (mw) {
+        const uint64_t b1 = tbits(u + 1);
+        if (b1 != FULLB) mask_bits(scb[f], b1);
+      } else {
+        const int n1 = nval(u + 1);
+        if (n1 < TILE) mask_tail(scb[f], n1);
+      }
     }
     // one straight-line block: the value products of tile u, the weights
     // of tile u+1 and their row sums, the score products of tile u+2
@@ -895,7 +970,7 @@ __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArg
   };
   // steady trips first (no tile tail, fixed waits, unconditional loads), then
   // the remaining rounds with every check
-  const int nsteady = ntg - S - 2;
+  const int nsteady = mw ? 0 : ntg - S - 2;   // (masked chunks: every round checks its tiles)
   int u0 = 0;
   for (; u0 + 2 * S <= nsteady; u0 += 2 * S) {
 #pragma unroll
@@ -945,7 +1020,7 @@ int encode_mfma_per_cu(int M, int D, bool masked) {
 // tiles, 64 rows as four 2-wave groups (32-token tiles at head dim 64) --
 // 8 waves and four-stage rings either way, one workgroup per CU.
 bool encode_ilv_used(int M, int D, bool masked) {
-  return (D == 64 || D == 16) && (M == 128 || M == 64) && !masked;
+  return ((D == 64 || D == 16) && (M == 128 || M == 64) && !masked) || (D == 128 && M == 256);
 }
 
 static bool encode_ilv_selected(const EncodeArgs& a) { return encode_ilv_used(a.M, a.D, a.mask_words != nullptr); }
@@ -960,6 +1035,10 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((encode_ilv_kernel<16, 4, 4, 2, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
       else
         hipLaunchKernelGGL((encode_ilv_kernel<16, 2, 4, 4, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    } else if (a.D == 128) {
+      // 256 latent rows: one group of eight waves, 32-token tiles, padding masks
+      // handled per tile
+      hipLaunchKernelGGL((encode_ilv_kernel<128, 8, 6, 1, 32>), dim3((unsigned)grid), dim3(512), 0, s, a);
     } else if (a.M == 128) {
       hipLaunchKernelGGL((encode_ilv_kernel<64, 4, 4, 2, 64>), dim3((unsigned)grid), dim3(512), 0, s, a);
     } else {
