@@ -71,7 +71,12 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
   constexpr bool FOLD = D == 16;
   __shared__ __attribute__((aligned(16))) uint16_t Kl[M * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Klo[FOLD ? M * KLD : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Zt[D * ZLD];
+  // ONES (head dim 16): the value product's A operand has 32 rows, 16 of them
+  // head dims; rows 16..31 hold ones, so that result rows 16..31 are the
+  // tokens' row sums and no separate row-sum products run
+  constexpr bool ONES = D == 16;
+  constexpr int ZROWS = ONES ? 32 : D;
+  __shared__ __attribute__((aligned(16))) uint16_t Zt[ZROWS * ZLD];
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * S * BB];
   __shared__ uint8_t tmask[MAXT];
 
@@ -137,6 +142,9 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
         for (int e = 0; e < 4; ++e) Zt[(d + e) * ZLD + m] = to_bf16(zv[i][e]);
       }
     }
+    if constexpr (ONES) {
+      for (int i = tid; i < 16 * M; i += T) Zt[(16 + i / M) * ZLD + i % M] = 0x3f80;   // bf16 1.0
+    }
   }
   __syncthreads();   // also completes the staging loads before the ring starts
 
@@ -196,7 +204,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int ks = 0; ks < MS; ++ks) {
-        const uint16_t* zrow = &Zt[(32 * db + (D >= 32 ? swap23(l32) : swap23(l32) & 15)) * ZLD + 8 * hh];
+        const uint16_t* zrow = &Zt[(32 * db + swap23(l32)) * ZLD + 8 * hh];
         zreg[db * MS + ks] = *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks);
       }
   }
@@ -279,7 +287,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
     f32x16_t y[DB];
     f32x4_t ls4;
     auto accumulate = [&](int ks, const bf16x8_t& pk) {
-      ls4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk, ls4, 0, 0, 0);
+      if constexpr (!ONES) ls4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pk, ls4, 0, 0, 0);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         // Z^T rows permuted so that register group g of lane half hh holds the 8
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
         if constexpr (REGOP) {
           zop = zreg[db * MS + ks];
         } else {
-          const uint16_t* zrow = &Zt[(32 * db + (D >= 32 ? swap23(l32) : swap23(l32) & 15)) * ZLD + 8 * hh];
+          const uint16_t* zrow = &Zt[(32 * db + swap23(l32)) * ZLD + 8 * hh];
           zop = *reinterpret_cast<const u32x4_t*>(zrow + 16 * ks);
         }
         y[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, zop), pk, y[db]);
@@ -310,7 +318,8 @@ __global__ __launch_bounds__(64 * NWV) void decode_mfma_kernel(const DecodeArgs 
       // ahead of the first weights (their registers would spill)
       if constexpr (MB >= 8) __builtin_amdgcn_sched_barrier(0);
     }
-    float lsum = ls4[0];
+    // (ONES: result register 8 holds row 16 + 4 hh, a ones row)
+    float lsum = ONES ? y[0][8] : ls4[0];
     if (__ballot(!(lsum >= 0x1p-64f && lsum <= 0x1p64f))) {
       // exact form: the token's maximum over its M scores first.  Its row sums
       // are added up on the vector ALUs from the lane's own rounded weights
