@@ -127,3 +127,64 @@ def test_decode_steady_blocks_masks_nan_rows_and_exact_form():
     Yr = ref.decode_ref(Xq.nan_to_num(0.0), Kl, Z, s, token_mask=tm)
     compare_bf16(Y, Yr, "Y")
     assert torch.equal(Y[0, :, nan_at], torch.zeros_like(Y[0, :, nan_at]))
+
+
+# ---- the pipelined encoder at head dim 128, 256 latent rows, padding masks
+def _masked128_case(N, offs, mask, wid, B=2, H=2):
+    M, D = 256, 128
+    w = W.Workload(name=f"masked128_{wid}", wid=wid, kind="encode", dtype="bf16", B=B, H=H, N=N, M=M, D=D,
+                   offsets=offs, q_std=D ** -0.5, q_per_batch=False)
+    x = w.make(DEV)
+    x["mask"] = torch.from_numpy(mask).to(DEV)
+    return w, x
+
+
+def _check_masked(w, x):
+    O_part, L_part = fl.encode(x["Q"], x["K"], x["V"], w.offsets, x["mask"], w.scale)
+    Z, L, _ = fl.lse_merge(O_part, L_part)
+    torch.cuda.synchronize()
+    out = ref.encode_ref(x["Q"], x["K"], x["V"], w.offsets, x["mask"], w.scale)
+    compare_bf16(O_part, out["O_part"], "O_part")
+    compare_L(L_part, out["L_part"], "L_part")
+    compare_bf16(Z, out["Z"], "Z")
+    compare_L(L, out["L"], "L")
+
+
+def test_masked_head_dim_128_prefix_edges():
+    """Valid prefixes (each chunk then runs as unmasked over its prefix) with the
+    edge cases of the chunk-end scan: empty prefixes, one valid token, fully
+    valid partitions, partitions and prefix ends at various offsets within and
+    across 64-token mask words; plus NaN in the padded K and V rows."""
+    offs = [0, 1000, 2531, 4000, 4100, 6000, 7777, 9000]
+    lens = [[0, 1, 64 * 5, 65, 100, 1900, 1, 1223], [999, 1531, 1469, 100, 1, 0, 1777, 17]]
+    N = offs[-1]
+    mask = np.zeros((2, N), dtype=np.uint8)
+    for b in range(2):
+        for r in range(len(offs) - 1):
+            mask[b, offs[r]: offs[r] + min(lens[b][r], offs[r + 1] - offs[r])] = 1
+    w, x = _masked128_case(N, offs, mask, 1201)
+    pad = torch.from_numpy(mask == 0).to(DEV)
+    for t in ("K", "V"):
+        v = x[t].float()
+        v[:, :, :, 0][pad.view(2, 1, N).expand(2, 2, N)] = float("nan")
+        x[t] = v.to(torch.bfloat16)
+    _check_masked(w, x)
+
+
+def test_masked_head_dim_128_holes_and_split_chunks():
+    """Masks with holes inside the valid range (the chunk runs masked: every tile
+    masks its scores and zeroes its invalid V rows), NaN padding, and partitions
+    long enough to be split into chunks of 8192 tokens (one (batch, head) slice
+    and three partitions)."""
+    offs = [0, 20000, 20001, 45000]
+    N = offs[-1]
+    g = np.random.default_rng(1202)
+    mask = (g.random((1, N)) > 0.3).astype(np.uint8)
+    mask[0, 30000:30100] = 0
+    mask[0, 44000:] = 0
+    w, x = _masked128_case(N, offs, mask, 1202, B=1, H=1)
+    pad = torch.from_numpy(mask == 0).to(DEV)
+    v = x["V"].float()
+    v[:, :, :, 3][pad.view(1, 1, N)] = float("nan")
+    x["V"] = v.to(torch.bfloat16)
+    _check_masked(w, x)
