@@ -508,6 +508,11 @@ __global__ __launch_bounds__(64 * NW * G) void encode_mfma_kernel(const EncodeAr
 // the round's barrier shows every wave past round u-1 (the last reader of both
 // slots).  Rows past the chunk re-read row 0 of the tile (finite values whose
 // weights are exactly 0), so a partial tile only masks its scores.
+//
+// Padding masks (one token group): the chunk is cut at its last valid token;
+// if every token before it is valid the chunk runs as unmasked, otherwise each
+// round masks the scores of its tile's invalid tokens and zeroes their V rows
+// in LDS (a padded row may hold NaN, which a weight of 0 must not meet).
 // ---------------------------------------------------------------------------
 template <int D, int NW, int S, int G, int TILE>
 __global__ __launch_bounds__(64 * NW * G) void encode_ilv_kernel(const EncodeArgs a) {
@@ -1018,7 +1023,9 @@ int encode_mfma_per_cu(int M, int D, bool masked) {
 // The two-tile pipelined encoder serves bf16 inputs without a padding mask at
 // head dims 64 and 16: 128 latent rows as two 4-wave groups with 64-token
 // tiles, 64 rows as four 2-wave groups (32-token tiles at head dim 64) --
-// 8 waves and four-stage rings either way, one workgroup per CU.
+// 8 waves and four-stage rings either way, one workgroup per CU.  At head dim
+// 128 it serves 256 latent rows, masked or not, as one group of 8 waves with
+// 32-token tiles and a six-stage ring.
 bool encode_ilv_used(int M, int D, bool masked) {
   return ((D == 64 || D == 16) && (M == 128 || M == 64) && !masked) || (D == 128 && M == 256);
 }
@@ -1062,11 +1069,11 @@ hipError_t launch_encode_mfma(const EncodeArgs& a, hipStream_t s) {
       case 256: return launch_mfma_t<16, 8, 4, 1>(a, s);
     }
   } else if (a.D == 128) {
+    // (256 latent rows take the pipelined encoder)
     switch (a.M) {
       case 32: return launch_mfma_t<128, 1, 3, 1>(a, s);
       case 64: return launch_mfma_t<128, 2, 3, 1>(a, s);
       case 128: return launch_mfma_t<128, 4, 4, 1>(a, s);
-      case 256: return launch_mfma_t<128, 8, 4, 1>(a, s);
     }
   }
   return hipErrorInvalidValue;
