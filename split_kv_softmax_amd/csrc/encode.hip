@@ -1210,8 +1210,8 @@ __global__ __launch_bounds__(256) void encode_q1_kernel(const EncodeArgs a) {
       ok[u] = t < t_end;
       if (ok[u] && mk) ok[u] = mk[t] != 0;
       if (ok[u]) {
-        kw[u] = ld16(Kg + (int64_t)t * D);
-        vw[u] = ld16(Vg + (int64_t)t * D);
+        kw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Kg + (int64_t)t * D));
+        vw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(Vg + (int64_t)t * D));
       } else {
         kw[u] = u32x4_t{0, 0, 0, 0};
         vw[u] = u32x4_t{0, 0, 0, 0};

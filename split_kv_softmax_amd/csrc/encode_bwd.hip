@@ -718,13 +718,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       for (int k = 0; k < NPK; ++k) {   // rows past the chunk read row 0 (in range, unused)
         if (CPT == 1 && ov) break;
         const int rk = r0 + RSTEP * k;
-        prev[k] = ld16(dKg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0);
+        prev[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(dKg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0));
       }
 #pragma unroll
       for (int k = 0; k < NPV; ++k) {
         if (CPT == 1 && !ov) break;
         const int rk = r0 + RSTEP * k;
-        prev[NPK + k] = ld16(dVg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0);
+        prev[NPK + k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(dVg + tb + (whole || rk < nrows ? rk : 0) * D + 8 * ch0));
       }
       // ---- phase B: this wave's output blocks, staged into the tile's K/V slot ----
       {
