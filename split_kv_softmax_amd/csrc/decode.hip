@@ -21,11 +21,14 @@ namespace flare {
 // other, and S-1 blocks of a wave are in flight while it computes one.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int row_swz(int D, int r) {
-  // 16-byte chunk swizzle of token row r: 128-byte rows (D=64) and 256-byte
-  // rows (D=128) permute their chunks; 32-byte rows (D=16) swap their two
-  // chunks on rows 8..15 of every 16, so 16 rows read by 16 lanes cover the 64
-  // banks once
-  return D == 64 ? ((r >> 1) & 7) : D == 16 ? ((r >> 3) & 1) : (r & 15);
+  // 16-byte chunk swizzle of token row r.  A 16-byte LDS read serves 16 lanes
+  // (256 bytes over the 64 banks) per cycle, a 16-byte write only 8 lanes (128
+  // bytes), and a lane here reads or writes one chunk of its own row, so the
+  // chunk index must differ over any 8 consecutive rows that share their bank
+  // window on a write and over any 16 on a read.  128-byte rows (D=64): chunk
+  // c ^ (r mod 8) ^ bit 3 of r; 32-byte rows (D=16): the two chunks swap where
+  // bits 2 and 3 of r differ; 256-byte rows (D=128): c ^ (r mod 16).
+  return D == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : D == 16 ? (((r >> 2) ^ (r >> 3)) & 1) : (r & 15);
 }
 
 template <int NI, int ST, int S>

@@ -196,9 +196,11 @@ hipError_t launch_decode_bwd_generic(const DecBwdArgs& a, bool bf16, hipStream_t
 // dXq rows leave through the consumed ring slot as whole rows; each token's
 // log2-normaliser and delta go to the workspace for the latent side.
 // ---------------------------------------------------------------------------
-// 16-byte chunk swizzle of token row r (32-byte rows at D=16 swap their chunks on rows 8..15 of every 16)
+// 16-byte chunk swizzle of token row r, free of bank conflicts both for 16-lane
+// reads (256 bytes per cycle) and for 8-lane writes (128 bytes per cycle) of one
+// chunk per lane and row (the forward decode's layout)
 __device__ __forceinline__ int tok_swz(int D, int r) {
-  return D == 64 ? ((r >> 1) & 7) : D == 16 ? ((r >> 3) & 1) : (r & 15);
+  return D == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : D == 16 ? (((r >> 2) ^ (r >> 3)) & 1) : (r & 15);
 }
 
 template <int NI, int ST, int S>

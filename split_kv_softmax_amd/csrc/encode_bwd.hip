@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
 // workgroup per (b, h, token chunk); 64-token tiles through a direct-load ring.
 // Phase A (one wave per 32 latent rows, lane = latent row):
 //   S^T = K Q^T, dP^T = V dZ^T, P = exp(s S - L), s dS = P (s dP - s c)
-//   P and s dS go to LDS as bf16 [m][token] (128-byte rows, K/V swizzle); with DQ the wave also adds
+//   P and s dS go to LDS as bf16 [m][token] (128-byte rows, pd_swz); with DQ the wave also adds
 //   K^T (s dS)^T into its query-gradient partial (so those partials already carry s).
 // Phase B (each wave one gradient tensor and a slice of output blocks,
 // lane = token):
@@ -385,6 +385,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_mfma_kernel(const BwdArgs a) {
 // no valid token are not loaded and only write zeros.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int swap_bits2(int x) { return ((x & 1) << 1) | (x >> 1); }
+
+// 16-byte chunk swizzle of the P / dS rows (128 bytes: 64 tokens of one latent).
+// Phase A writes one chunk per lane and row, lanes on consecutive rows, and a
+// 16-byte LDS write serves 8 lanes (128 bytes) per cycle, so the swizzle must be
+// a bijection on r mod 8.  Phase B reads them transposed, 8 bytes per lane and
+// 32 lanes (256 bytes) per cycle over four consecutive rows 4k..4k+3 and four
+// chunks, where bit 1 of the row on bit 2 of the chunk keeps rows r and r+2
+// (same bank half) apart.  The token-row swizzle of head dim 64 has the second
+// property but repeats on row pairs; flipping both low chunk bits on odd rows
+// gives the first as well.
+__device__ __forceinline__ int pd_swz(int r) { return kv_swz<64>(r) ^ ((r & 1) * 3); }
 
 template <int D, int M, int NW, int S, bool DQ, int ACC>
 __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
@@ -560,8 +571,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
       dma16(Vg + off, kst + TB + ii * 1024);
     }
   };
-  // staged gradient rows: 16-byte chunk ch of row n sits at ch ^ out_swz(n)
-  auto out_swz = [](int n) { return D == 64 ? kv_swz<64>(n) : D == 16 ? kv_swz<16>(n) : (n & 15); };
+  // staged gradient rows: 16-byte chunk ch of row n sits at ch ^ out_swz(n); each
+  // lane writes one chunk of its own row (8 lanes, consecutive rows, per write
+  // cycle), and the copy-out reads whole rows, so any swizzle that differs over 8
+  // consecutive rows within a 128-byte bank window is conflict-free both ways
+  auto out_swz = [](int n) { return D == 64 ? (n & 7) : D == 16 ? (((n >> 2) ^ (n >> 3)) & 1) : (n & 15); };
 
   f32x16_t dq[DQ ? DB : 1];
 #pragma unroll
@@ -677,7 +691,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
                                 pack_bf16x2(pv[6], pv[7])};
             const u32x4_t wd = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
                                 pack_bf16x2(ds[6], ds[7])};
-            const int pc = (4 * b2 + 2 * g + hh) ^ kv_swz<64>(m);
+            const int pc = (4 * b2 + 2 * g + hh) ^ pd_swz(m);
             st16(pbuf + m * (TILE * 2) + pc * 16, wp);
             st16(dsbuf + m * (TILE * 2) + pc * 16, wd);
             pk[g] = __builtin_bit_cast(bf16x8_t, wd);
@@ -737,7 +751,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
           for (int q = 0; q < 2; ++q) {
             const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
             const int col = 32 * nb + 16 * (lg & 1) + 4 * (li & 3);
-            const int pc = (col >> 3) ^ kv_swz<64>(row);
+            const int pc = (col >> 3) ^ pd_swz(row);
             part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                                                       (lds_bf16x4*)(bsrc + row * (TILE * 2) + pc * 16 + (col & 7) * 2)));
           }
