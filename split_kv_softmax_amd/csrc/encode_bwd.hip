@@ -575,6 +575,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   // lane writes one chunk of its own row (8 lanes, consecutive rows, per write
   // cycle), and the copy-out reads whole rows, so any swizzle that differs over 8
   // consecutive rows within a 128-byte bank window is conflict-free both ways
+  // DIRECT (head dim 16): a gradient row is 32 bytes, so the 16-byte piece each
+  // lane holds after phase B (token 32*nb + l32, chunk hh) already makes one
+  // store of the wave a contiguous 1 KB of whole rows; the pieces leave straight
+  // from registers, one store per lane and tile like the staged copy-out (the
+  // ring's wait counts rely on that), with no staging and no barrier before it.
+  // Not for the accumulating forms: their old rows, read by the lane itself,
+  // would be consumed right after phase B, and the compiler's (in-order) wait
+  // for them then also covers the ring loads issued at the top of the tile
+  // (measured 2% slower; the staged copy-out consumes them a barrier later).
+  constexpr bool DIRECT = D == 16 && ACC == 0;
+  static_assert(!DIRECT || (CPT == 1 && NDW == 1 && NNB == 1 && NG == 1), "one piece per lane and tile");
   auto out_swz = [](int n) { return D == 64 ? (n & 7) : D == 16 ? (((n >> 2) ^ (n >> 3)) & 1) : (n & 15); };
 
   f32x16_t dq[DQ ? DB : 1];
@@ -772,7 +783,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
                                  pack_bf16x2(v[8 * g + 4] * os, v[8 * g + 5] * os),
                                  pack_bf16x2(v[8 * g + 6] * os, v[8 * g + 7] * os)};
               const int ch = 4 * (db0 + j) + 2 * g + hh;
-              st16(stg + n * ROWB + (ch ^ out_swz(n)) * 16, w);
+              if constexpr (DIRECT) {
+                __builtin_amdgcn_raw_buffer_store_b128(w, tsel == 1 ? kout : vout, n * ROWB + ch * 16, 0,
+                                                       kCachePolicyNT);
+              } else {
+                st16(stg + n * ROWB + (ch ^ out_swz(n)) * 16, w);
+              }
             }
         };
         // all B operands of the wave in registers at once (M <= 128: 64 VGPRs at most)
@@ -813,10 +829,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
           }
         }
       }
-      barrier_lds();
       // ---- whole rows out: dK from the K slot, dV from the V slot; each thread
       // owns CPT fixed 16-byte chunks (the first half in dK) ----
-      {
+      if constexpr (!DIRECT) {
+        barrier_lds();
         // consume the old rows on every path here, so that the compiler's wait for
         // them sits in this block and no load is left pending into the next tile
 #pragma unroll
