@@ -77,54 +77,26 @@ def _ev():
     return torch.cuda.Event(enable_timing=True)
 
 
-def _prepare_events(step, nsteps):
-    """Create (by recording each once) the phase events of nsteps steps up front: an event
-    created between steps delays the next step's launches, and an event recorded on an
-    idle GPU then times that host-side delay as part of the step's first kernel."""
-    step.pool = [[_ev() for _ in range(len(step.names) + 1)] for _ in range(nsteps)]
-    for evs in step.pool:
-        for e in evs:
-            e.record()
-    torch.cuda.synchronize()
-
-
-def _new_events(step):
-    """The phase events of one step (from the pool); kept until collect() (no sync per
-    step, so the timed steps run back to back as in the timed region)."""
-    step.ev = step.pool.pop() if getattr(step, "pool", None) else [_ev() for _ in range(len(step.names) + 1)]
-    step.pending.append(step.ev)
-
-
-def _collect(step):
-    """Synchronise once and keep the phase durations of every recorded step."""
-    torch.cuda.synchronize()
-    for ev in step.pending:
-        for i in range(len(step.phase_ms)):
-            step.phase_ms[i].append(ev[i].elapsed_time(ev[i + 1]))
-    step.pending = []
-
-
 class Step:
-    """A step as named phases run back to back; with timed_phases an event is
-    recorded before the first phase and after each one."""
+    """A step as named phases run back to back."""
 
     def _phases(self, phases):
         self.phases = phases
         self.names = [n for n, _ in phases]
-        self.phase_ms = [[] for _ in phases]   # per-phase milliseconds of every collected step
-        self.pending = []
+        self.phase_ms = [[] for _ in phases]   # per-launch milliseconds of each phase
 
-    def __call__(self, timed_phases: bool):
-        if timed_phases:
-            _new_events(self)
-            self.ev[0].record()
-        for i, (_, fn) in enumerate(self.phases):
+    def __call__(self):
+        for _, fn in self.phases:
             fn()
-            if timed_phases:
-                self.ev[i + 1].record()
 
-    collect = _collect
-    prepare_events = _prepare_events
+    def run_marked(self, k, a, b):
+        """One step with events a and b recorded around its phase k."""
+        for i, (_, fn) in enumerate(self.phases):
+            if i == k:
+                a.record()
+            fn()
+            if i == k:
+                b.record()
 
 
 class FlareppStep(Step):
@@ -381,13 +353,14 @@ def main():
                          "encoder launch)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and replay it for the warm-up and timed steps "
-                         "(the per-phase pass stays eager)")
+                         "(the per-kernel times come from eager launches after the timed region)")
     ap.add_argument("--shared", action="store_true",
                     help="FLARE++ only: the shared-projection variant (the query-synthesis encoder reads K and V; "
                          "with --backward its key and value gradients add into dK and dV)")
     ap.add_argument("--flush-mall", action="store_true",
-                    help="in the per-phase pass (after the timed region), write a 512 MiB scratch buffer "
-                         "before every step so that no input is served from the 256 MB last-level cache")
+                    help="after the timed region, run the steps again with a 512 MiB scratch write before "
+                         "every step, so that no input is served from the 256 MB last-level cache, and report "
+                         "their step times")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device 3 times "
                          "(the plain copy that scales the HBM byte counters)")
@@ -412,7 +385,7 @@ def main():
         step = (FlareppTrainStep if args.backward else FlareppStep)(w, x, args.fused, args.shared)
     else:
         step = STEPS[w.kind](w, x, args.fused)
-    run = lambda: step(timed_phases=False)  # noqa: E731
+    run = step
     if args.graph:
         # one eager step on a side stream sizes the library's cached workspace
         # and counters outside the capture
@@ -430,15 +403,27 @@ def main():
         run()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronised on both sides; an event after
-    # every step gives the per-step durations (median, minimum) without a sync
+    # timed region: exactly K steps, synchronised on both sides.  An event after every step
+    # gives the per-step durations (median, minimum); eager step i also records an event pair
+    # around its phase i mod (number of phases), so every kernel's average launch duration comes
+    # from the timed launches themselves (two more events per step cost the step about 1 %;
+    # events between every kernel of a step slow the following steps by up to a quarter on this
+    # GPU).  A graph replay is one launch: with --graph, and for phases that K steps leave
+    # without a sample, the per-kernel durations come from the same scheme on eager steps run
+    # after the timed region.
+    nph = len(step.phases)
+    in_region = not args.graph
     t_start, t_end = _ev(), _ev()
     step_ev = [_ev() for _ in range(args.steps)]
+    marks = [(_ev(), _ev()) for _ in range(args.steps)] if in_region else []
     torch.cuda.synchronize()
     t_start.record()
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        run()
+        if in_region:
+            step.run_marked(i % nph, *marks[i])
+        else:
+            run()
         step_ev[i].record()
     t_end.record()
     torch.cuda.synchronize()
@@ -447,28 +432,34 @@ def main():
     ms_per_step = ms_total / args.steps
     per_step = [t_start.elapsed_time(step_ev[0])] + [step_ev[i - 1].elapsed_time(step_ev[i])
                                                     for i in range(1, args.steps)]
-
-    # per-kernel durations from events on the launch stream: a separate pass of
-    # the same back-to-back steps, synchronised only at its end (with
-    # --flush-mall a 512 MiB scratch write precedes every step, outside its events)
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush_mall else None
-    step.prepare_events(args.steps)
-    # a bounded wait kernel (a few ms to tenths of a second, by the counter its clock reads)
-    # holds the GPU while the host queues every step of the pass, so the steps run back to
-    # back and no host-side launch gap lands inside a phase
-    hold = getattr(torch.cuda, "_sleep", None)   # torch's own spin kernel (a private helper)
-    if hold is not None:
-        hold(50_000_000)
-    for _ in range(args.steps):
-        if scratch is not None:
+    for i, (a, b) in enumerate(marks):
+        step.phase_ms[i % nph].append(a.elapsed_time(b))
+    missing = [k for k in range(nph) if not step.phase_ms[k]]
+    if missing:
+        # three untimed steps first keep the GPU busy while the host queues the rest
+        extra = [(k, _ev(), _ev()) for _ in range(max(args.steps, 10)) for k in missing]
+        for _ in range(3):
+            step()
+        for k, a, b in extra:
+            step.run_marked(k, a, b)
+        torch.cuda.synchronize()
+        for k, a, b in extra:
+            step.phase_ms[k].append(a.elapsed_time(b))
+    pass_steps = None
+    if args.flush_mall:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ends = [(_ev(), _ev()) for _ in range(args.steps)]
+        for _ in range(3):
+            run()
+        for a, b in ends:
             scratch.fill_(1)
-        step(timed_phases=True)
-    torch.cuda.synchronize()
-    pass_steps = [ev[0].elapsed_time(ev[-1]) for ev in step.pending] if scratch is not None else None
-    step.collect()
-    del scratch
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        pass_steps = [a.elapsed_time(b) for a, b in ends]
+        del scratch
     ph = {n: sum(p) / len(p) for n, p in zip(step.names, step.phase_ms)}
-    ph_median = {n: statistics.median(p) for n, p in zip(step.names, step.phase_ms)}
     cands = roofline_candidates(w, x, step, ph)
     # the binding kernel: the one furthest below the HBM roofline
     kern_name, kern_ms, kern_bytes, kern_key = min(cands, key=lambda c: c[2] / c[1])
@@ -505,7 +496,7 @@ def main():
                      "kernel": kern_name, "kernel_ms": kern_ms, "algorithmic_bytes": kern_bytes},
         "step_ms": {"mean": ms_per_step, "median": statistics.median(per_step), "min": min(per_step)},
         "phases_ms": ph,
-        "phases_ms_median": ph_median,
+        "phases_timed_in_region": in_region,
         "wall_s_timed": wall,
     }
     if len(cands) > 1:

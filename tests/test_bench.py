@@ -22,7 +22,7 @@ def test_more_than_one_gpu_is_refused():
 @pytest.mark.gpu
 def test_bench_line_fields_small_workload():
     """A short run on the small fp32 workload prints exactly one JSON line carrying the metric,
-    the per-step statistics, the per-phase times and a roofline block for the binding kernel."""
+    the per-step statistics, the per-kernel times and a roofline block for the binding kernel."""
     r = subprocess.run([sys.executable, "-u", BENCH, "--workload", "flare_encode_fp32_B1_H1_N1024_M16_D32_R4",
                         "--steps", "5", "--warmup", "2", "--no-cpu-baseline"],
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
@@ -40,5 +40,4 @@ def test_bench_line_fields_small_workload():
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in ro, k
     assert ro["peak"] == 8000.0 and 0 < ro["frac"] < 1
-    assert set(d["phases_ms"]) == set(d["phases_ms_median"])
     assert all(v > 0 for v in d["phases_ms"].values())
