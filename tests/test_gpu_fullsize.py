@@ -91,7 +91,7 @@ def test_full_flarepp_chain_as_benchmarked():
     _say(f"case {w.name}")
     x = w.make(DEV)
     step = bench.FlareppStep(w, x)
-    step(timed_phases=False)
+    step()
     torch.cuda.synchronize()
     for name in ("O1", "L1", "QX", "QXL", "O2", "L2", "Z", "L", "Y"):
         _finite(getattr(step, name), name)
@@ -117,7 +117,7 @@ def test_full_flarepp_head_dim_16(fused, shared):
     _say(f"case {w.name} fused={fused} shared={shared}")
     x = w.make(DEV)
     step = bench.FlareppStep(w, x, fused, shared)
-    step(timed_phases=False)
+    step()
     torch.cuda.synchronize()
     for name in ("O1", "L1", "QX", "QXL", "O2", "L2", "Z", "L", "Y"):
         _finite(getattr(step, name), name)
