@@ -395,6 +395,39 @@ flare_status scratch_of_current_device(void** out) {
   return FLARE_OK;
 }
 
+// ------------------------------------------------- second stream (backward)
+// Where the key/value kernel cannot also hold the query-gradient accumulators
+// (256 latent rows at head dim 128), the two backward kernels read the same
+// inputs and write disjoint outputs, and the first is bound by HBM while the
+// second is bound by the matrix cores: the query-gradient kernel runs on a
+// second stream of the same device (default priority, not blocking on the null
+// stream), ordered after the caller's stream by one event and joined back to it
+// by another, so its workgroups fill the CUs that the memory-bound kernel
+// leaves.  One such stream per device, created on first use.
+std::mutex g_aux_mu;
+hipStream_t g_aux[kMaxDevices] = {};
+
+flare_status aux_stream_for(hipStream_t s, hipStream_t* out) {
+  int dev = -1;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FLARE_EUNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_aux_mu);
+  if (!g_aux[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    hipStream_t st = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return hip_fail(e, "second stream");
+    g_aux[dev] = st;
+  }
+  *out = g_aux[dev];
+  return FLARE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -676,12 +709,31 @@ flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int
   // one pass over K, V where the registers allow the fused kernel, else a
   // separate query-gradient pass; both leave per-chunk partials for the reduce
   const bool fuse = bwd_kv_fuses_dq(M, D);
-  if (!fuse) {
-    e = launch_bwd_dq_mfma(a, s);
-    if (e != hipSuccess) return hip_fail(e, "query-gradient launch");
+  if (fuse) {
+    e = launch_bwd_kv_mfma(a, s);
+    if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
+  } else {
+    // the query-gradient kernel on the second stream, alongside the key/value kernel
+    hipStream_t aux = nullptr;
+    st = aux_stream_for(s, &aux);
+    if (st != FLARE_OK) return st;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    auto done = [&](hipError_t err, const char* what) -> flare_status {
+      for (hipEvent_t x : ev)
+        if (x) (void)hipEventDestroy(x);
+      return err == hipSuccess ? FLARE_OK : hip_fail(err, what);
+    };
+    for (hipEvent_t& x : ev)
+      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return done(e, "event");
+    if ((e = hipEventRecord(ev[0], s)) != hipSuccess) return done(e, "event record");
+    if ((e = hipStreamWaitEvent(aux, ev[0], 0)) != hipSuccess) return done(e, "stream wait");
+    if ((e = launch_bwd_dq_mfma(a, aux)) != hipSuccess) return done(e, "query-gradient launch");
+    if ((e = hipEventRecord(ev[1], aux)) != hipSuccess) return done(e, "event record");
+    if ((e = launch_bwd_kv_mfma(a, s)) != hipSuccess) return done(e, "key/value-gradient launch");
+    if ((e = hipStreamWaitEvent(s, ev[1], 0)) != hipSuccess) return done(e, "stream wait");
+    st = done(hipSuccess, "");
+    if (st != FLARE_OK) return st;
   }
-  e = launch_bwd_kv_mfma(a, s);
-  if (e != hipSuccess) return hip_fail(e, "key/value-gradient launch");
   // partials that already carry s (the fused kernel contracting s dS) are summed as they are
   e = launch_bwd_dq_reduce(a.ws_dq, nc, (int64_t)B * H * M * D, bwd_kv_partials_scaled(M, D) ? 1.f : scale, dQ,
                            a.accumulate_dq != 0, dQ_cast, s);

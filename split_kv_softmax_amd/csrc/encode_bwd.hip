@@ -870,6 +870,376 @@ __global__ __launch_bounds__(64 * NW) void bwd_kv_mfma_kernel(const BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Key/value gradients at 256 latent rows and head dim 128, with wave roles
+// (FLARE++ appendix, backward pass: P with the global L, the row term c, the
+// local dK_r and dV_r).  In the kernel above every wave holds both the score-
+// side operands (the Q and dZ rows of its 32 latents) and the gradient-side
+// ones (a 32-dim slice of Q^T or dZ^T over all latents); at this shape that
+// fills 256 registers, two waves per SIMD, which then run phases A and B in
+// lock-step.  Here 16 waves split the roles and work on consecutive tiles:
+//   waves 0..7 (A, lane = latent row 32w + l32), round u, tile u:
+//     S^T = K Q^T, dP^T = V dZ^T, P = exp(s S - L), s dS = P (s dP - s c),
+//     P and s dS as bf16 [latent][token] into buffer u % 2
+//   waves 8..15 (B: tensor t = (w-8)/4, 0 = dV, 1 = dK; head-dim block (w-8)%4;
+//   lane = token), round u:
+//     rows 8*block .. 8*block+7 of tensor t of tile u-2, staged last round,
+//     leave as whole rows; then dV^T = dZ^T P or dK^T = Q^T (s dS) of tile u-1
+//     from buffer (u-1) % 2, staged in tile u-1's own K/V slot.
+// Each role runs at most 128 registers, so four waves share a SIMD and the
+// products of one role overlap the other's exponentials and LDS waits.
+// 32-token tiles through a 5-slot direct-load ring (tile u+2 is loaded in
+// round u); one barrier per round.  The tiles after a chunk's last valid
+// token only write zero rows (or, accumulating, leave the rows as they are):
+// up to two such tiles per round alongside the rounds (the rounds leave HBM
+// bandwidth to spare), the rest after them.
+// ---------------------------------------------------------------------------
+// 16-byte chunk swizzle of the P / dS rows here (64 bytes: 32 tokens of one
+// latent): phase A's 16-byte writes (8 lanes per cycle, rows r..r+7, one chunk)
+// and phase B's transposing reads (4 rows x 4 chunks per 32 lanes) both cover
+// all 16 bank groups once.
+__device__ __forceinline__ int pd32_swz(int r) { return (r >> 2) & 1; }
+
+template <int ACC, int S>
+__global__ __launch_bounds__(1024) void bwd_kv_ws_kernel(const BwdArgs a) {
+  constexpr int D = 128, M = 256, TILE = 32, NW = 16;
+  constexpr int ROWB = 2 * D;              // bytes of one K/V/gradient row
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int TB = TILE * ROWB;          // a K (or V) tile: 8 KB
+  constexpr int STAGE = 2 * TB;
+  // ring of S slots: tile u (A reads it), u-1 (B stages into it), u-2 (B copies it
+  // out) and the L = S-3 tiles in flight (tile u+L is loaded in round u)
+  constexpr int L = S - 3;
+  static_assert(L >= 1 && L <= 3, "ring depth");
+  constexpr int RING = S * STAGE;
+  constexpr int PDROW = 2 * TILE;          // one latent's bf16 weights of a tile
+  constexpr int PD = M * PDROW;            // P (or dS) of a tile: 16 KB
+  constexpr int LDS_MAIN = RING + 4 * PD;  // + two buffers of P and dS
+  constexpr int LDS_STAT = 2 * M * D * 2;  // Q and dZ rows while the operands load: 128 KB
+  constexpr int LDS = LDS_MAIN > LDS_STAT ? LDS_MAIN : LDS_STAT;
+  constexpr int KS = D / 16;               // contraction steps over the head dim
+  constexpr int KM = M / 16;               // contraction steps over the latents
+  static_assert(NW * 1024 == 2 * TB, "one 1 KB load per wave and tile");
+  static_assert(LDS_MAIN <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  uint8_t* pdb = smem + RING;              // buffer j: P at pdb + 2*j*PD, s dS at + PD
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lg = lane >> 4, li = lane & 15;
+  const int nch = a.tab.nchunks;
+  int bid = ordered_block(a.order);
+  const int c = bid % nch;
+  bid /= nch;
+  const int h = bid % a.H;
+  const int b = bid / a.H;
+  const int t_begin = a.tab.bnd[c], t_end = a.tab.bnd[c + 1];
+  const int64_t bh = (int64_t)b * a.H + h;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + bh * (int64_t)a.N * D;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + bh * (int64_t)a.N * D;
+  const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + (int64_t)b * a.q_bstride + (int64_t)h * M * D;
+  const uint16_t* Gg = static_cast<const uint16_t*>(a.dZ) + bh * (int64_t)M * D;
+  uint16_t* dKg = static_cast<uint16_t*>(a.dK) + bh * (int64_t)a.N * D;
+  uint16_t* dVg = static_cast<uint16_t*>(a.dV) + bh * (int64_t)a.N * D;
+  const_u64* mw = a.mask_words ? (const_u64*)(a.mask_words + (int64_t)b * a.mask_words_stride) : nullptr;
+
+  // ---- stationary operands: Q and dZ rows through LDS ([m][d], row-major) ----
+  for (int f = tid; f < M * CPR; f += 64 * NW) {
+    const int r = f / CPR, ch = f % CPR;
+    const u32x4_t q = ld16(Qg + (int64_t)r * D + 8 * ch);
+    const u32x4_t g = ld16(Gg + (int64_t)r * D + 8 * ch);
+    st16(smem + r * ROWB + ch * 16, q);
+    st16(smem + M * ROWB + r * ROWB + ch * 16, g);
+  }
+  __syncthreads();
+
+  const int ntiles = (t_end - t_begin + TILE - 1) / TILE;
+  // tiles up to the chunk's last valid token; the rest only get zero rows
+  int nv = ntiles;
+  if (mw) {
+    const int w0 = t_begin >> 6, nwd = t_end > t_begin ? ((t_end - 1) >> 6) - w0 + 1 : 0;
+    int last = -1;
+    for (int k = lane; k < nwd; k += 64) {
+      const int wi = w0 + k;
+      uint64_t x = a.mask_words[(int64_t)b * a.mask_words_stride + wi];
+      const int a0 = t_begin - 64 * wi, a1 = t_end - 64 * wi;   // keep bits [a0, a1)
+      if (a0 > 0) x &= ~0ull << a0;
+      if (a1 < 64) x &= (1ull << a1) - 1ull;
+      if (x) last = 64 * wi + 63 - __clzll(x);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    last = __builtin_amdgcn_readfirstlane(last);
+    nv = last < t_begin ? 0 : (last - t_begin) / TILE + 1;
+  }
+  // validity bits of tile t (0 for tiles outside [0, nv))
+  auto tile_bits = [&](int t) -> uint32_t {
+    if (t < 0 || t >= nv) return 0u;
+    const int t0 = t_begin + t * TILE;
+    const int n = t_end - t0;
+    uint32_t bits = n >= TILE ? 0xffffffffu : ((1u << n) - 1u);
+    if (mw) bits &= (uint32_t)mask_tile_bits(mw, t0);
+    return bits;
+  };
+  // this wave's 1 KB piece of tile t: waves 0..7 the K tile, 8..15 the V tile
+  auto issue = [&](int t) {
+    const int t0 = t_begin + t * TILE;
+    const int nrows = t_end - t0;
+    const uint32_t dst = lds_addr(smem) + (t % S) * STAGE + wave * 1024;   // (V pieces follow the K tile)
+    const int ii = wave & 7;
+    const int byte = ii * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    const int ch = pc ^ kv_swz<D>(r);
+    const int rr = r < nrows ? r : 0;
+    dma16((wave < 8 ? Kg : Vg) + (int64_t)(t0 + rr) * D + 8 * ch, dst);
+  };
+  const int nrounds = nv > 0 ? nv + 2 : 0;
+  // zero rows of the tiles after the last valid token, stored by the B waves (one
+  // 16-byte chunk of dK and one of dV per thread and tile; none for a tensor that
+  // accumulates): tiles nv+2r and nv+2r+1 in round r, the rest after the rounds
+  constexpr int ZPR = 2;
+  constexpr int NZT = ((ACC & 1) ? 0 : 1) + ((ACC & 2) ? 0 : 1);   // zero-row tensors
+  const int zoff = ((tid >> 4) & 31) * ROWB + (tid & 15) * 16;
+  auto zero_tile = [&](int t) {
+    const int t0 = t_begin + t * TILE;
+    const int len = min(TILE, t_end - t0) * ROWB;
+    if constexpr (!(ACC & 1))
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0, 0, 0, 0},
+                                             __builtin_amdgcn_make_buffer_rsrc(dKg + (int64_t)t0 * D, 0, len, 0x00020000),
+                                             zoff, 0, kCachePolicyNT);
+    if constexpr (!(ACC & 2))
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{0, 0, 0, 0},
+                                             __builtin_amdgcn_make_buffer_rsrc(dVg + (int64_t)t0 * D, 0, len, 0x00020000),
+                                             zoff, 0, kCachePolicyNT);
+  };
+  // zero tiles of round r, and the stores they take per B thread
+  auto ztiles = [&](int r) -> int {
+    if (r < 0 || r >= nrounds) return 0;
+    const int left = ntiles - (nv + ZPR * r);
+    return left <= 0 ? 0 : (left < ZPR ? left : ZPR);
+  };
+
+  if (wave < 8) {
+    // ================= role A: scores, weights and s dS of latent rows 32w .. 32w+31
+    const int m = 32 * wave + l32;
+    bf16x8_t qop[KS], gop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qop[ks] = __builtin_bit_cast(bf16x8_t, ld16(smem + m * ROWB + (16 * ks + 8 * hh) * 2));
+      gop[ks] = __builtin_bit_cast(bf16x8_t, ld16(smem + M * ROWB + m * ROWB + (16 * ks + 8 * hh) * 2));
+    }
+    const float Lm = a.L[bh * M + m];
+    const float cms = a.scale * a.c[bh * M + m];
+    const float c2 = a.scale_log2, sc1 = a.scale;
+    const float nl2 = (Lm == kNegInf) ? __builtin_huge_valf() : Lm * kLog2e;
+    const int swk = kv_swz<D>(swap23(l32));   // K/V row swap23(l32) of the tile
+    const int pm = m * PDROW;
+    const int psw = pd32_swz(m);
+    wait_vm<0>();
+    barrier_lds();   // every wave has its operands: the ring may reuse the staging rows
+    uint32_t rb[L + 3];  // rb[k]: bits of tile u-2+k
+    rb[0] = rb[1] = 0u;
+#pragma unroll
+    for (int k = 0; k <= L; ++k) rb[2 + k] = tile_bits(k);
+#pragma unroll
+    for (int k = 0; k < L; ++k)
+      if (rb[2 + k]) issue(k);
+    for (int u = 0; u < nrounds; ++u) {
+      // tile u's piece landed: later are the pieces of tiles u+1 .. u+L-1
+      int later = 0;
+#pragma unroll
+      for (int k = 1; k < L; ++k) later += rb[2 + k] ? 1 : 0;
+      wait_vm_le<L - 1>(later);
+      barrier_lds();
+      if (rb[2 + L]) issue(u + L);
+      const uint32_t bits = rb[2];
+      if (bits) {
+        const uint8_t* kst = smem + (u % S) * STAGE;
+        const uint8_t* krow = kst + swap23(l32) * ROWB;
+        const uint8_t* vrow = krow + TB;
+        f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch = (2 * ks + hh) ^ swk;
+          sc = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(krow + ch * 16)),
+                            qop[ks], sc);
+          dp = mfma32x32x16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vrow + ch * 16)),
+                            gop[ks], dp);
+        }
+        // register r of lane half hh holds token 16*(r/8) + 8*hh + r%8
+        const uint32_t lb = bits >> (8 * hh);
+        const bool full = bits == 0xffffffffu;
+        uint8_t* pbuf = pdb + 2 * (u & 1) * PD;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          float pv[8], ds[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * g + j;
+            pv[j] = fast_exp2(__builtin_fmaf(sc[r], c2, -nl2));
+            ds[j] = pv[j] * __builtin_fmaf(dp[r], sc1, -cms);   // s dS
+          }
+          if (!full) {
+            // padding and rows past the chunk: exact zeros (their K/V rows may hold anything)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              if (!((lb >> (16 * g + j)) & 1u)) {
+                pv[j] = 0.f;
+                ds[j] = 0.f;
+              }
+            }
+          }
+          const u32x4_t wp = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                              pack_bf16x2(pv[6], pv[7])};
+          const u32x4_t wd = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                              pack_bf16x2(ds[6], ds[7])};
+          const int pc = ((2 * g + hh) ^ psw) * 16;
+          st16(pbuf + pm + pc, wp);
+          st16(pbuf + PD + pm + pc, wd);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < L + 2; ++k) rb[k] = rb[k + 1];
+      rb[L + 2] = tile_bits(u + L + 1);
+    }
+  } else {
+    // ================= role B: gradient tensor tsel (0 = dV, 1 = dK), head dims 32*db .. 32*db+31
+    const int wb = wave - 8;
+    const int tsel = wb >> 2, db = wb & 3;
+    // A operand rows permuted so that each register group holds 8 consecutive d:
+    // lane i of a 16-lane group reads column swap_bits2(i%4) of the 4x16 block
+    bf16x8_t ast[KM];
+    {
+      const uint8_t* src = smem + (tsel == 0 ? M * ROWB : 0);
+#pragma unroll
+      for (int ks = 0; ks < KM; ++ks) {
+        u32x2_t part[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+          const int col = 32 * db + 16 * (lg & 1) + 4 * swap_bits2(li & 3);
+          part[q] = __builtin_bit_cast(
+              u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(src + row * ROWB + col * 2)));
+        }
+        ast[ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]});
+      }
+    }
+    wait_vm<0>();
+    barrier_lds();
+    uint16_t* const outg = tsel == 1 ? dKg : dVg;
+    constexpr int ACCT0 = ACC & 2, ACCT1 = ACC & 1;   // accumulate into dV / dK
+    const bool acc_t = tsel == 1 ? ACCT1 != 0 : ACCT0 != 0;
+    // copy-out rows of this wave: 8*db + 4*i + lane/16, 16-byte chunk lane%16
+    const int crow = 8 * db + (lane >> 4), cch = lane & 15;
+    uint32_t rb[L + 3];
+    rb[0] = rb[1] = 0u;
+#pragma unroll
+    for (int k = 0; k <= L; ++k) rb[2 + k] = tile_bits(k);
+#pragma unroll
+    for (int k = 0; k < L; ++k)
+      if (rb[2 + k]) issue(k);
+    for (int u = 0; u < nrounds; ++u) {
+      // this wave's piece of tile u (loaded in round u-L) landed: later are the
+      // pieces of tiles u+1 .. u+L-1 and the zero-row and copy-out stores of rounds
+      // u-L .. u-1 (two copy-out stores per round with a tile to copy)
+      int later = 0;
+#pragma unroll
+      for (int k = 1; k < L; ++k) later += rb[2 + k] ? 1 : 0;
+#pragma unroll
+      for (int r = u - L; r < u; ++r) later += NZT * ztiles(r) + (r >= 2 && r - 2 < nv ? 2 : 0);
+      wait_vm_le<(L - 1) + L * (2 * ZPR + 2)>(later);
+      barrier_lds();
+      // old rows of tile u-2 (accumulating forms), read before this round's load is issued
+      constexpr int NPREV = ACC ? 2 : 1;
+      u32x4_t prev[NPREV];
+      const int tc = u - 2;   // tile copied out this round
+      const bool copy = tc >= 0 && tc < nv;
+      const int tc0 = t_begin + tc * TILE;
+      const int ncr = copy ? min(TILE, t_end - tc0) : 0;
+      if constexpr (ACC != 0) {
+        if (copy && acc_t && rb[0]) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int r = crow + 4 * i;
+            prev[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(outg + (int64_t)(tc0 + (r < ncr ? r : 0)) * D + 8 * cch));
+          }
+        }
+      }
+      if (rb[2 + L]) issue(u + L);
+      {
+        const int k = ztiles(u);
+        for (int i = 0; i < k; ++i) zero_tile(nv + ZPR * u + i);
+      }
+      if (copy) {
+        // an empty tile leaves an accumulated gradient as it is (a zero-length range drops every store)
+        const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+            outg + (int64_t)tc0 * D, 0, (acc_t && !rb[0]) ? 0 : ncr * ROWB, 0x00020000);
+        const uint8_t* stg = smem + (tc % S) * STAGE + (tsel == 1 ? 0 : TB);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = crow + 4 * i;
+          u32x4_t v = ld16(stg + r * ROWB + ((cch ^ (r & 15)) * 16));
+          if constexpr (ACC != 0) {
+            if (acc_t && rb[0]) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                v[e] = pack_bf16x2(bf16lo(v[e]) + bf16lo(prev[i][e]), bf16hi(v[e]) + bf16hi(prev[i][e]));
+            }
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(v, out, r * ROWB + cch * 16, 0, kCachePolicyNT);
+        }
+      }
+      // gradient rows of tile u-1 into its own K (dK) or V (dV) slot
+      const int tg = u - 1;
+      if (tg >= 0 && tg < nv) {
+        uint8_t* stg = smem + (tg % S) * STAGE + (tsel == 1 ? 0 : TB);
+        const int n = l32;
+        if (rb[1]) {
+          const uint8_t* bsrc = pdb + 2 * (tg & 1) * PD + (tsel == 1 ? PD : 0);
+          f32x16_t acc = f32x16_t{};
+#pragma unroll
+          for (int ks = 0; ks < KM; ++ks) {
+            u32x2_t part[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const int row = 16 * ks + 8 * (lg >> 1) + 4 * q + (li >> 2);
+              const int col = 16 * (lg & 1) + 4 * (li & 3);
+              const int pc = (col >> 3) ^ pd32_swz(row);
+              part[q] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                                        (lds_bf16x4*)(bsrc + row * PDROW + pc * 16 + (col & 7) * 2)));
+            }
+            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, u32x4_t{part[0][0], part[0][1], part[1][0], part[1][1]});
+            acc = mfma32x32x16(ast[ks], bop, acc);
+          }
+          // register r of lane half hh: d = 32*db + 16*(r/8) + 8*hh + r%8, token l32
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const u32x4_t w = {pack_bf16x2(acc[8 * g + 0], acc[8 * g + 1]), pack_bf16x2(acc[8 * g + 2], acc[8 * g + 3]),
+                               pack_bf16x2(acc[8 * g + 4], acc[8 * g + 5]), pack_bf16x2(acc[8 * g + 6], acc[8 * g + 7])};
+            const int ch = 4 * db + 2 * g + hh;
+            st16(stg + n * ROWB + (ch ^ (n & 15)) * 16, w);
+          }
+        } else {
+          // no valid token: zero gradient rows
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int ch = 4 * db + 2 * g + hh;
+            st16(stg + n * ROWB + (ch ^ (n & 15)) * 16, u32x4_t{0, 0, 0, 0});
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < L + 2; ++k) rb[k] = rb[k + 1];
+      rb[L + 2] = tile_bits(u + L + 1);
+    }
+  }
+  // ---- zero tiles the rounds left (B waves)
+  if (wave >= 8)
+    for (int t = nv + ZPR * nrounds; t < ntiles; ++t) zero_tile(t);
+}
+
 // dQ = s * sum over chunk slots (fixed order) [+ dQ], one thread per 4
 // elements; optionally also written rounded to bf16.
 __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restrict__ ws, int nslots, int64_t n4,
@@ -919,6 +1289,19 @@ static hipError_t launch_kv_t(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 256 latent rows at head dim 128: the wave-role kernel (query gradient separate)
+constexpr int kWsSlots = 4;
+static hipError_t launch_kv_ws(const BwdArgs& a, hipStream_t s) {
+  const int64_t grid = (int64_t)a.tab.nchunks * a.H * a.B;
+  switch ((a.accumulate_dk ? 1 : 0) | (a.accumulate_dv ? 2 : 0)) {
+    case 0: hipLaunchKernelGGL((bwd_kv_ws_kernel<0, kWsSlots>), dim3((unsigned)grid), dim3(1024), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((bwd_kv_ws_kernel<1, kWsSlots>), dim3((unsigned)grid), dim3(1024), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((bwd_kv_ws_kernel<2, kWsSlots>), dim3((unsigned)grid), dim3(1024), 0, s, a); break;
+    default: hipLaunchKernelGGL((bwd_kv_ws_kernel<3, kWsSlots>), dim3((unsigned)grid), dim3(1024), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 bool bwd_kv_fuses_dq(int M, int D) { return !(M == 256 && D == 128); }
 
 // whether the fused kernel's query-gradient partials already carry the scale s
@@ -950,7 +1333,7 @@ hipError_t launch_bwd_kv_mfma(const BwdArgs& a, hipStream_t s) {
       case 32: return launch_kv_t<128, 32, 4, 3, true>(a, s);
       case 64: return launch_kv_t<128, 64, 4, 3, true>(a, s);
       case 128: return launch_kv_t<128, 128, 4, 3, true>(a, s);
-      case 256: return launch_kv_t<128, 256, 8, 2, false>(a, s);
+      case 256: return launch_kv_ws(a, s);
     }
   }
   return hipErrorInvalidValue;
