@@ -45,8 +45,10 @@ COUNTER_FILES = {
 }
 # the sources each kernel family is built from (the summaries record their hash)
 KERNEL_SOURCES = {"encode_ilv": ["encode.hip"], "encode_mfma": ["encode.hip"], "encode_q1": ["encode.hip"],
-                  "encode_generic": ["encode.hip"], "decode_mfma": ["decode.hip"], "bwd_kv_mfma": ["encode_bwd.hip"],
-                  "bwd_dq_mfma": ["encode_bwd.hip"]}
+                  "encode_generic": ["encode.hip"], "mask_words": ["encode.hip"], "heavy_first": ["encode.hip"],
+                  "decode_mfma": ["decode.hip"], "decode_generic": ["decode.hip"], "fold": ["merge.hip"],
+                  "bwd_kv_mfma": ["encode_bwd.hip"], "bwd_kv_ws": ["encode_bwd.hip"], "bwd_dq_mfma": ["encode_bwd.hip"],
+                  "bwd_dq_reduce": ["encode_bwd.hip"], "bwd_rowdot": ["encode_bwd.hip"], "dbwd_": ["decode_bwd.hip"]}
 
 
 def source_hash(kernel: str) -> str:
