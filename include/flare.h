@@ -214,6 +214,14 @@ size_t flare_encode_bwd_workspace_size(flare_dtype dtype, int B, int H, int N, i
  * matrix-core path runs; it needs
  * Q, K, V, dZ, dQ, dK, dV 16-byte aligned (else FLARE_EINVAL) and sums dQ over
  * token chunks in a fixed order, so results are bitwise reproducible.
+ * For bf16 with M = 256 and D = 128 the query gradient runs on a second
+ * non-blocking stream of the same device, which the library creates on first
+ * use and keeps until the process ends, forked from and joined back to
+ * `stream` with events: every result is ordered on `stream` as if all of the
+ * work ran there, and a graph captured on `stream` takes in both branches
+ * (make one eager call first, so that the stream is not created during the
+ * capture).  Calls on different streams of one device share that second
+ * stream, which orders their query-gradient kernels one after the other.
  */
 flare_status flare_encode_bwd(flare_dtype dtype, int B, int H, int N, int M, int D,
                               const void* Q, int64_t q_batch_stride, const void* K, const void* V,

@@ -197,3 +197,39 @@ def test_flarepp_training_step_graph_replays_match_eager(shared):
         torch.cuda.synchronize()
         for k in expect:
             assert torch.equal(out[k], expect[k]), f"replay {rep}: {k} differs from the eager step"
+
+
+def test_masked_backward_graph_replays_match_eager():
+    """256 latent rows at head dim 128: the backward forks its query-gradient kernel onto the
+    library's second stream and joins it with events; captured in one graph with the forward,
+    every replay equals the eager step, with eager calls between the replays."""
+    w = W.shrink(W.MASKED_FWD_BWD, 2048, R=4, B=2, H=2)
+    x = w.make(DEV)
+
+    def step():
+        O, Lp = fl.encode(x["Q"], x["K"], x["V"], w.offsets, x["mask"], w.scale)
+        Z, L, _ = fl.lse_merge(O, Lp)
+        return fl.encode_bwd(x["Q"], x["K"], x["V"], w.offsets, x["mask"], w.scale, Z, L, x["dZ"])
+
+    g0 = step()                          # creates the second stream outside the capture
+    torch.cuda.synchronize()
+    expect = [t.clone() for t in g0]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = step()
+    for rep in range(3):
+        for t in out:
+            t.fill_(float("nan"))        # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip(("dQ", "dK", "dV"), out, expect):
+            assert torch.equal(t, e), f"replay {rep}: {name} differs from the eager step"
+        other = step()                   # an eager call between replays
+        torch.cuda.synchronize()
+        assert all(torch.equal(t, e) for t, e in zip(other, expect))
